@@ -1,0 +1,19 @@
+"""fp64 CPU oracle (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The product path (the HIP library and its Python
+binding) never imports it and shares no code with it.
+"""
+
+from .attention import (  # noqa: F401
+    attention_probs,
+    attn_backward,
+    attn_backward_delta,
+    attn_forward,
+    band_mask,
+    kv_head,
+    qknorm,
+    rms_norm,
+    rms_norm_backward,
+    sssl_windows,
+)

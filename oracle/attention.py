@@ -1,0 +1,249 @@
+"""fp64 CPU oracle for QK-normed, grouped-query, sliding-window causal attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check of the entry module and
+the CPU-baseline leg of the benchmark use it. It shares no code with the HIP
+path (no kernels, headers, helpers or constants); the only common module is
+the seeded input generator ``synth``.
+
+What it computes is the plain definition, in float64, with no blocking, no
+fusion and no rounding:
+
+  1. weightless RMS norm of every q and k head row over head_dim
+     x_hat = x / sqrt(mean(x^2) + eps)
+  2. grouped-query head map: query head h reads KV head floor(h / (Hq/Hkv))
+  3. logits S_ij = scale * <q_hat_i, k_hat_j>
+  4. band: key j is visible to query i iff 0 <= i - j <= W, or j <= i when
+     W = -1 (full causal)
+  5. softmax over the band, O_i = sum_j P_ij v_j, LSE_i = log sum_j exp(S_ij)
+  6. backward of 1-5 with respect to the raw q, k, v
+
+Sources (cited by page title and section):
+  [post]   The social post that walks through autoresearch's train.py
+           (Spanish, French, German and Czech editions of discover post
+           71151920174080); its paragraph on the model: RMSNorm on queries
+           and keys just before the attention dot product (QK-norm), the
+           "SSSL" pattern of three sliding-window layers with a window of
+           half the sequence length followed by one full causal layer, the
+           8-layer map and the forced-global last layer.
+  [guide]  "autoresearch Administrator & Developer Guide": section 3.4
+           (WINDOW_PATTERN row: last layer always overridden to L),
+           section 6.3 (techniques table: sliding windows, GQA),
+           section 8.2.1 (model table: RMSNorm via F.rms_norm, GQA with
+           n_kv_head <= n_head, per-layer window from WINDOW_PATTERN).
+
+Readings where the pages are silent (each one is listed in the design notes):
+  - window boundary: key j with 0 <= i - j <= W is visible, i.e. W + 1 keys
+    counting the query's own position; W >= T - 1 is full causal;
+  - norm: weightless, over head_dim, eps = 1e-6 inside the square root;
+  - GQA map: contiguous groups, h -> floor(h / G);
+  - no attention-logit softcap, no dropout, no document mask;
+  - LSE in natural log; gradients are with respect to the raw (un-normed)
+    q and k.
+
+Every helper below is a module attribute so a test can replace one with a
+planted mistake and show that the pins catch it.
+
+Parity status: every public function here is pinned by the CPU tests
+(closed forms, library routines the pages name, finite differences,
+brute force); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+F64 = torch.float64
+
+
+# ---------------------------------------------------------------- schedule
+
+def sssl_windows(n_layer: int, seq_len: int, pattern: str = "SSSL") -> list:
+    """Per-layer window list for a pattern of 'S' (local) / 'L' (global) letters.
+
+    [post] model paragraph: the pattern repeats over the layers, 'S' layers
+    use a sliding window of half the sequence length, 'L' layers are full
+    causal, and the last layer is forced to be global whatever the pattern.
+    [guide] 3.4, WINDOW_PATTERN row. Returns -1 for full causal.
+    """
+    if not pattern or any(c not in "SL" for c in pattern.upper()):
+        raise ValueError(f"pattern must be a non-empty string of S/L, got {pattern!r}")
+    pattern = pattern.upper()
+    out = []
+    for layer in range(n_layer):
+        letter = pattern[layer % len(pattern)]
+        if layer == n_layer - 1:
+            letter = "L"
+        out.append(-1 if letter == "L" else seq_len // 2)
+    return out
+
+
+# ---------------------------------------------------------------- mask
+
+def band_mask(T: int, window: int) -> torch.Tensor:
+    """[T, T] bool, entry (i, j) true iff key j is visible to query i.
+
+    Causal (j <= i) and, for window >= 0, within the window (i - j <= window).
+    [post] model paragraph (banded attention matrix of the local layers);
+    [guide] 8.2.1 (sliding-window attention row).
+    """
+    i = torch.arange(T).view(T, 1)
+    j = torch.arange(T).view(1, T)
+    visible = j <= i
+    if window >= 0:
+        visible = visible & ((i - j) <= window)
+    return visible
+
+
+# ---------------------------------------------------------------- norm
+
+def rms_norm(x: torch.Tensor, eps: float):
+    """Weightless RMS norm over the last dim: returns (x_hat, r), r = (ms + eps)^-1/2.
+
+    [post] model paragraph (RMSNorm on queries and keys just before the
+    attention dot product); [guide] 8.2.1 (RMSNorm via F.rms_norm, no weight).
+    """
+    x = x.to(F64)
+    ms = (x * x).mean(dim=-1, keepdim=True)
+    r = 1.0 / torch.sqrt(ms + eps)
+    return x * r, r
+
+
+def rms_norm_backward(x_hat: torch.Tensor, r: torch.Tensor, dx_hat: torch.Tensor) -> torch.Tensor:
+    """Gradient through x_hat = r * x, r = (mean(x^2) + eps)^-1/2.
+
+    d x_hat_a / d x_b = r * delta_ab - r^3 * x_a * x_b / D, hence
+    dx = r * (dx_hat - x_hat * <dx_hat, x_hat> / D).
+    """
+    D = x_hat.shape[-1]
+    return r * (dx_hat - x_hat * (dx_hat * x_hat).sum(dim=-1, keepdim=True) / D)
+
+
+# ---------------------------------------------------------------- heads
+
+def kv_head(h: int, Hq: int, Hkv: int) -> int:
+    """Grouped-query map: query head h shares KV head floor(h / (Hq / Hkv)).
+
+    [guide] 6.3 and 8.2.1 (grouped-query attention, n_kv_head <= n_head).
+    """
+    return h // (Hq // Hkv)
+
+
+def _check_shapes(q, k, v):
+    B, T, Hq, D = q.shape
+    Bk, Tk, Hkv, Dk = k.shape
+    if (Bk, Tk, Dk) != (B, T, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q [B,T,Hq,D], k and v [B,T,Hkv,D] expected")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, T, Hq, Hkv, D
+
+
+def _normed(q, k, qk_norm, eps):
+    if qk_norm:
+        q_hat, r_q = rms_norm(q, eps)
+        k_hat, r_k = rms_norm(k, eps)
+    else:
+        q_hat, r_q = q.to(F64), None
+        k_hat, r_k = k.to(F64), None
+    return q_hat, r_q, k_hat, r_k
+
+
+def _probs_one_head(q_hat_bh, k_hat_bg, mask, scale):
+    """P [T, T] and LSE [T] for one (batch, head): masked softmax of the logits."""
+    S = scale * (q_hat_bh @ k_hat_bg.transpose(0, 1))
+    S = S.masked_fill(~mask, -math.inf)
+    m = S.max(dim=-1, keepdim=True).values
+    e = torch.exp(S - m)
+    denom = e.sum(dim=-1, keepdim=True)
+    P = e / denom
+    lse = (m + torch.log(denom)).squeeze(-1)
+    return P, lse
+
+
+# ---------------------------------------------------------------- forward
+
+def attention_probs(q, k, window, scale, qk_norm=True, eps=1e-6):
+    """Softmax probabilities P [B, Hq, T, T] (zero outside the band)."""
+    B, T, Hq, Hkv, D = _check_shapes(q, k, k)
+    q_hat, _, k_hat, _ = _normed(q, k, qk_norm, eps)
+    mask = band_mask(T, window)
+    P = torch.zeros(B, Hq, T, T, dtype=F64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            P[b, h], _ = _probs_one_head(q_hat[b, :, h], k_hat[b, :, g], mask, scale)
+    return P
+
+
+def attn_forward(q, k, v, window, scale, qk_norm=True, eps=1e-6):
+    """Forward of the layer: returns (o [B,T,Hq,D], lse [B,Hq,T]) in float64.
+
+    q [B,T,Hq,D], k and v [B,T,Hkv,D] (any float dtype; upcast exactly).
+    """
+    B, T, Hq, Hkv, D = _check_shapes(q, k, v)
+    q_hat, _, k_hat, _ = _normed(q, k, qk_norm, eps)
+    v = v.to(F64)
+    mask = band_mask(T, window)
+    o = torch.zeros(B, T, Hq, D, dtype=F64)
+    lse = torch.zeros(B, Hq, T, dtype=F64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            P, lse[b, h] = _probs_one_head(q_hat[b, :, h], k_hat[b, :, g], mask, scale)
+            o[b, :, h] = P @ v[b, :, g]
+    return o, lse
+
+
+# ---------------------------------------------------------------- backward
+
+def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6):
+    """Gradients (dq, dk, dv) of <O, dO> with respect to the raw q, k, v (float64).
+
+    Per (b, h) with g its KV head:
+      dV_g   += P^T dO
+      dP      = dO V_g^T
+      Delta_i = sum_j P_ij dP_ij
+      dS      = P * (dP - Delta)
+      dq_hat  = scale * dS K_hat_g
+      dk_hat_g += scale * dS^T Q_hat
+    then the RMS-norm backward maps dq_hat, dk_hat to dq, dk.
+    """
+    B, T, Hq, Hkv, D = _check_shapes(q, k, v)
+    q_hat, r_q, k_hat, r_k = _normed(q, k, qk_norm, eps)
+    v = v.to(F64)
+    do = do.to(F64)
+    mask = band_mask(T, window)
+    dq_hat = torch.zeros(B, T, Hq, D, dtype=F64)
+    dk_hat = torch.zeros(B, T, Hkv, D, dtype=F64)
+    dv = torch.zeros(B, T, Hkv, D, dtype=F64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head(h, Hq, Hkv)
+            P, _ = _probs_one_head(q_hat[b, :, h], k_hat[b, :, g], mask, scale)
+            dO = do[b, :, h]
+            dv[b, :, g] += P.transpose(0, 1) @ dO
+            dP = dO @ v[b, :, g].transpose(0, 1)
+            delta = (P * dP).sum(dim=-1, keepdim=True)
+            dS = P * (dP - delta)
+            dq_hat[b, :, h] = scale * (dS @ k_hat[b, :, g])
+            dk_hat[b, :, g] += scale * (dS.transpose(0, 1) @ q_hat[b, :, h])
+    if qk_norm:
+        dq = rms_norm_backward(q_hat, r_q, dq_hat)
+        dk = rms_norm_backward(k_hat, r_k, dk_hat)
+    else:
+        dq, dk = dq_hat, dk_hat
+    return dq, dk, dv
+
+
+def attn_backward_delta(o, do):
+    """Delta_i = <dO_i, O_i> per (b, h, i) as [B, Hq, T]; equal to sum_j P_ij dP_ij."""
+    return (o.to(F64) * do.to(F64)).sum(dim=-1).permute(0, 2, 1).contiguous()
+
+
+def qknorm(x, eps=1e-6):
+    """Standalone norm of [rows, D] rows: returns (y, rstd) with rstd [rows]."""
+    y, r = rms_norm(x, eps)
+    return y, r.squeeze(-1)
