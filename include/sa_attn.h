@@ -1,0 +1,129 @@
+/*
+ * sa_attn.h - C ABI of libsa_attn.so: QK-normed, grouped-query, sliding-window
+ * causal attention (forward and backward) for AMD Instinct MI355X (gfx950).
+ *
+ * The layer it implements is the attention of the small GPT trainer that the
+ * following pages describe:
+ *   [post]  the social post walking through autoresearch's train.py (Spanish,
+ *           French, German and Czech editions of discover post
+ *           71151920174080), paragraph on the model: RMSNorm on queries and
+ *           keys just before the attention dot product ("QK-norm"); the "SSSL"
+ *           pattern of three sliding-window layers (window = half the sequence
+ *           length) and one full causal layer, repeating, last layer global.
+ *   [guide] "autoresearch Administrator & Developer Guide", section 8.2.1
+ *           (model table: RMSNorm via F.rms_norm, grouped-query attention with
+ *           n_kv_head <= n_head, per-layer sliding window) and section 6.3.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (HIP device memory) unless a
+ *     parameter says otherwise. The caller allocates and owns every buffer,
+ *     including the backward workspace; the library never allocates, frees,
+ *     synchronises or prints.
+ *   - Tensors are contiguous, row-major, innermost dimension last:
+ *       q, o, dout, dq : bf16 [B, T, Hq,  D]
+ *       k, v, dk, dv   : bf16 [B, T, Hkv, D]
+ *       lse            : fp32 [B, Hq, T]   natural-log log-sum-exp of the
+ *                                          scaled logits over the band
+ *     bf16 is the IEEE-754 binary32 upper half (bfloat16), RNE rounding.
+ *   - D (head_dim) is 64 or 128. Hq must be a multiple of Hkv; query head h
+ *     reads KV head floor(h / (Hq / Hkv)) (contiguous groups).
+ *   - window: -1 = full causal. window >= 0: key j is visible to query i iff
+ *     0 <= i - j <= window (window + 1 keys counting the query itself). Any
+ *     window >= T - 1 is treated as full causal.
+ *   - qk_norm != 0 applies the weightless RMS norm
+ *       x_hat = x / sqrt(mean(x^2) + eps)
+ *     to every q and k head row (over D) before the logits
+ *     S_ij = softmax_scale * <q_hat_i, k_hat_j>; qk_norm = 0 uses q and k
+ *     as given. Gradients are always with respect to the raw q, k, v.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued on it; nothing blocks the host.
+ *   - Errors: every argument is validated before anything is launched, so an
+ *     error return means nothing was enqueued. Faults inside a kernel surface
+ *     at the caller's next synchronisation, as with any stream operation.
+ *   - Thread safety: no mutable global state; concurrent calls on different
+ *     streams are safe.
+ */
+#ifndef SA_ATTN_H
+#define SA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SA_ERR_SHAPE = 2,       /* a size <= 0, Hq % Hkv != 0, window < -1, or a size overflow */
+  SA_ERR_UNSUPPORTED = 3, /* head_dim not in {64, 128} */
+  SA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  SA_ERR_WORKSPACE = 5,   /* backward workspace NULL or smaller than sa_attn_bwd_workspace_bytes() */
+  SA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} sa_status;
+
+/* Version of this ABI (bumped on any incompatible change). */
+int sa_abi_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* sa_status_string(int status);
+
+/*
+ * sa_qknorm - standalone weightless RMS norm of `rows` rows of length head_dim.
+ *   [post] QK-norm passage; [guide] 8.2.1 (RMSNorm via F.rms_norm, no weight).
+ *   x    : bf16 [rows, head_dim] input (e.g. q or k viewed as [B*T*H, D]).
+ *   y    : bf16 [rows, head_dim] output, y = x / sqrt(mean(x^2) + eps), RNE.
+ *          May alias x (in-place) exactly; partial overlap is not allowed.
+ *   rstd : fp32 [rows] output 1/sqrt(mean(x^2)+eps), or NULL to skip it.
+ *   rows >= 1, head_dim in {64, 128}. rows = 0 is accepted and does nothing.
+ */
+sa_status sa_qknorm(const void* x, void* y, float* rstd, int64_t rows, int head_dim, float eps,
+                    void* stream);
+
+/*
+ * sa_attn_fwd - forward of one attention layer.
+ *   [post] model paragraph (QK-norm, sliding-window/full causal layers);
+ *   [guide] 8.2.1 (GQA, per-layer window).
+ *   Computes, per batch b and query head h with KV head g = h / (Hq/Hkv):
+ *     P_i = softmax_j over the band of S_ij,  o_i = sum_j P_ij v_j,
+ *     lse_i = log sum_{j in band} exp(S_ij).
+ *   q, k, v : inputs (layouts above).  o : bf16 output [B,T,Hq,D].
+ *   lse     : fp32 output [B,Hq,T]; required (the backward needs it).
+ *   Tiles of the band outside every query's window are never loaded.
+ */
+sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int T, int Hq, int Hkv, int head_dim, int window,
+                      float softmax_scale, int qk_norm, float eps, void* stream);
+
+/* Bytes of device workspace sa_attn_bwd needs for these sizes (0 if a size is invalid). */
+size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
+
+/*
+ * sa_attn_bwd - backward of sa_attn_fwd with the same arguments.
+ *   Recomputes the probabilities from q, k and the forward's lse:
+ *     P_ij = exp(S_ij - lse_i),  Delta_i = <dout_i, o_i>,
+ *     dS_ij = P_ij (<dout_i, v_j> - Delta_i),
+ *     dq_hat_i = scale sum_j dS_ij k_hat_j,  dk_hat_j = scale sum_{h in group} sum_i dS_ij q_hat_i,
+ *     dv_j = sum_{h in group} sum_i P_ij dout_i,
+ *   then the RMS-norm backward dx = r (dx_hat - x_hat <dx_hat, x_hat> / D).
+ *   The GQA sums over the query heads of a group happen inside the kernel.
+ *   q, k, v, o, lse, dout : inputs (o and lse as written by sa_attn_fwd).
+ *   dq, dk, dv            : bf16 outputs, fully overwritten.
+ *   workspace             : device buffer of at least
+ *                           sa_attn_bwd_workspace_bytes(B,T,Hq,Hkv,head_dim)
+ *                           bytes, 256-byte aligned; contents on entry are
+ *                           ignored and on return unspecified. Two calls that
+ *                           overlap in time must use different workspaces.
+ */
+sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int T, int Hq, int Hkv, int head_dim, int window,
+                      float softmax_scale, int qk_norm, float eps, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_ATTN_H */

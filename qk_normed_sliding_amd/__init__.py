@@ -1,0 +1,216 @@
+"""Python binding of libsa_attn.so: QK-normed GQA sliding-window attention on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/sa_attn.h. PyTorch provides
+device memory and the current stream. There is no CPU fallback: importing
+this package fails if the library has not been built.
+
+Entry points (same names as the C ABI):
+  sa_qknorm(x, y=None, rstd=None, eps=1e-6)
+  sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None)
+  sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim)
+  sa_attn_bwd(q, k, v, o, lse, dout, window=-1, ..., dq=None, dk=None, dv=None, workspace=None)
+Helpers: attention(...) (autograd), sssl_windows(n_layer, T, pattern).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsa_attn.so")
+
+SA_OK = 0
+ABI_VERSION = 1
+
+
+class SAError(RuntimeError):
+    """A libsa_attn entry point returned a non-zero sa_status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {_lib.sa_status_string(status).decode()}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m qk_normed_sliding_amd.build` "
+            "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.sa_abi_version.restype = i32
+    lib.sa_abi_version.argtypes = []
+    lib.sa_status_string.restype = ctypes.c_char_p
+    lib.sa_status_string.argtypes = [i32]
+    lib.sa_qknorm.restype = i32
+    lib.sa_qknorm.argtypes = [vp, vp, vp, i64, i32, f32, vp]
+    lib.sa_attn_fwd.restype = i32
+    lib.sa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, f32, vp]
+    lib.sa_attn_bwd_workspace_bytes.restype = sz
+    lib.sa_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.sa_attn_bwd.restype = i32
+    lib.sa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                i32, i32, i32, i32, i32, i32, f32, i32, f32, vp]
+    if lib.sa_abi_version() != ABI_VERSION:
+        raise ImportError(f"libsa_attn ABI {lib.sa_abi_version()} != expected {ABI_VERSION}")
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    """The loaded ctypes handle of libsa_attn.so."""
+    return _lib
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, status):
+    if status != SA_OK:
+        raise SAError(fn, status)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q is [B,T,Hq,D] and k, v are [B,T,Hkv,D]")
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    return B, T, Hq, Hkv, D
+
+
+def _scale(softmax_scale, D):
+    return 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+
+
+# ------------------------------------------------------------------ entry points
+
+def sa_qknorm(x, y=None, rstd=None, eps=1e-6, want_rstd=True, stream=None):
+    """Weightless RMS norm of the rows of x ([..., D] bf16). Returns (y, rstd)."""
+    _need(x, "x", torch.bfloat16)
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", torch.bfloat16, x.shape)
+    if rstd is None and want_rstd:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if rstd is not None:
+        _need(rstd, "rstd", torch.float32, x.shape[:-1])
+    _check("sa_qknorm", _lib.sa_qknorm(_ptr(x), _ptr(y), _ptr(rstd), rows, D, float(eps),
+                                       _stream(x.device, stream)))
+    return y, rstd
+
+
+def sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None,
+                stream=None):
+    """Forward of one layer. q [B,T,Hq,D], k/v [B,T,Hkv,D] bf16. Returns (o, lse)."""
+    B, T, Hq, Hkv, D = _dims(q, k)
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, T, Hkv, D))
+    _need(v, "v", torch.bfloat16, (B, T, Hkv, D))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    _check("sa_attn_fwd", _lib.sa_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D, int(window),
+        _scale(softmax_scale, D), int(bool(qk_norm)), float(eps), _stream(q.device, stream)))
+    return o, lse
+
+
+def sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim):
+    return int(_lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim))
+
+
+def sa_attn_bwd(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6,
+                dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of one layer. Returns (dq, dk, dv) with respect to the raw q, k, v."""
+    B, T, Hq, Hkv, D = _dims(q, k)
+    for t, n, shp in ((q, "q", None), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D)),
+                      (o, "o", q.shape), (dout, "dout", q.shape)):
+        _need(t, n, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, q.shape)
+    _need(dk, "dk", torch.bfloat16, k.shape)
+    _need(dv, "dv", torch.bfloat16, v.shape)
+    need = sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check("sa_attn_bwd", _lib.sa_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), workspace.numel(), B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D),
+        int(bool(qk_norm)), float(eps), _stream(q.device, stream)))
+    return dq, dk, dv
+
+
+# ------------------------------------------------------------------ helpers
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, window, softmax_scale, qk_norm, eps):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, lse = sa_attn_fwd(q, k, v, window, softmax_scale, qk_norm, eps)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (window, softmax_scale, qk_norm, eps)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = sa_attn_bwd(q, k, v, o, lse, do.contiguous(), *ctx.args)
+        return dq, dk, dv, None, None, None, None
+
+
+def attention(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6):
+    """Differentiable layer: o = attention(q, k, v); gradients via sa_attn_bwd."""
+    return _Attention.apply(q, k, v, window, softmax_scale, qk_norm, eps)
+
+
+def sssl_windows(n_layer: int, seq_len: int, pattern: str = "SSSL"):
+    """Window of each layer for an S/L pattern: S = seq_len // 2, L = -1 (full causal).
+
+    The pattern repeats over the layers and the last layer is always L
+    ([post] SSSL passage; [guide] 3.4, WINDOW_PATTERN row).
+    """
+    pat = pattern.upper()
+    if not pat or set(pat) - {"S", "L"}:
+        raise ValueError(f"pattern must be a non-empty S/L string, got {pattern!r}")
+    kinds = [pat[i % len(pat)] for i in range(n_layer)]
+    if kinds:
+        kinds[-1] = "L"
+    return [seq_len // 2 if c == "S" else -1 for c in kinds]

@@ -1,0 +1,151 @@
+// C ABI of libsa_attn.so (declared in include/sa_attn.h).
+//
+// Every entry point validates all of its arguments before touching the HIP
+// runtime, so an error return means nothing was enqueued, and the
+// validation paths run on a host without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include "sa_attn.h"
+#include "sa_kernels.h"
+
+#define SA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool valid_dim(int d) { return d == 64 || d == 128; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Validates the shape arguments shared by the forward and the backward.
+sa_status check_shape(int B, int T, int Hq, int Hkv, int head_dim, int window, float scale, float eps) {
+  if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0) return SA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return SA_ERR_SHAPE;
+  if (window < -1) return SA_ERR_SHAPE;
+  if (!isfinite(scale) || !isfinite(eps) || eps < 0.f) return SA_ERR_SHAPE;
+  // element offsets are computed in 64-bit; grids in 32-bit
+  const double elems = (double)B * T * (double)Hq * 128.0;
+  if (elems > 9.0e18) return SA_ERR_SHAPE;
+  if ((double)B * Hq * ((T + 127) / 128) > 2.0e9) return SA_ERR_SHAPE;
+  if (!valid_dim(head_dim)) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+// Logits are bounded by |scale| * D when q and k rows are normed (each normed
+// row has Euclidean norm below sqrt(D)); 2% margin covers bf16 rounding of
+// the normed rows. A fixed maximum is safe while exp2 of the widest logit
+// gap, 2 * bound * log2(e), stays far inside the fp32 normal range.
+bool fixed_max_ok(int qk_norm, float scale, int head_dim, float* c2) {
+  const float bound = fabsf(scale) * (float)head_dim * 1.02f;
+  *c2 = bound * 1.4426950408889634f;
+  return qk_norm != 0 && bound <= 32.f;
+}
+
+}  // namespace
+
+SA_API int sa_abi_version(void) { return kAbiVersion; }
+
+SA_API const char* sa_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_NULL: return "SA_ERR_NULL: a required pointer is NULL";
+    case SA_ERR_SHAPE: return "SA_ERR_SHAPE: invalid size, head ratio, window or scalar argument";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: head_dim must be 64 or 128";
+    case SA_ERR_ALIGN: return "SA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE: workspace missing or too small";
+    case SA_ERR_HIP: return "SA_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown sa_status";
+  }
+}
+
+SA_API sa_status sa_qknorm(const void* x, void* y, float* rstd, int64_t rows, int head_dim, float eps,
+                           void* stream) {
+  if (rows < 0 || !isfinite(eps) || eps < 0.f) return SA_ERR_SHAPE;
+  if (!valid_dim(head_dim)) return SA_ERR_UNSUPPORTED;
+  if (rows == 0) return SA_OK;
+  if (x == nullptr || y == nullptr) return SA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y) || (rstd != nullptr && !aligned4(rstd))) return SA_ERR_ALIGN;
+  if (rows > (int64_t)1 << 56) return SA_ERR_SHAPE;
+  sa::NormParams p{x, y, rstd, rows, eps};
+  return sa::launch_qknorm(p, head_dim, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int T,
+                             int Hq, int Hkv, int head_dim, int window, float softmax_scale, int qk_norm,
+                             float eps, void* stream) {
+  const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
+  if (st != SA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return SA_ERR_ALIGN;
+
+  sa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.T = T;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.window = (window >= T - 1) ? -1 : window;
+  p.c1 = softmax_scale * 1.4426950408889634f;
+  p.eps = eps;
+  const bool fixed = fixed_max_ok(qk_norm, softmax_scale, head_dim, &p.c2);
+  const int hpw = (p.G % 2 == 0) ? 2 : 1;
+  p.nsub = p.G / hpw;
+  p.nqb = (T + 127) / 128;
+  return sa::launch_fwd(p, head_dim, hpw, qk_norm != 0, fixed, (hipStream_t)stream) == hipSuccess ? SA_OK
+                                                                                                    : SA_ERR_HIP;
+}
+
+SA_API size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
+  if (check_shape(B, T, Hq, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
+  const size_t rows = (size_t)B * T * Hq;
+  return round256(rows * head_dim * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                             float softmax_scale, int qk_norm, float eps, void* stream) {
+  const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
+  if (st != SA_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SA_ERR_NULL;
+  const size_t need = sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim);
+  if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return SA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return SA_ERR_ALIGN;
+
+  sa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  const size_t rows = (size_t)B * T * Hq;
+  p.dq_acc = (float*)workspace;
+  p.delta = (float*)((char*)workspace + round256(rows * head_dim * sizeof(float)));
+  p.B = B;
+  p.T = T;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.window = (window >= T - 1) ? -1 : window;
+  p.scale = softmax_scale;
+  p.c1 = softmax_scale * 1.4426950408889634f;
+  p.eps = eps;
+  p.nkb = (T + 127) / 128;
+  return sa::launch_bwd(p, head_dim, qk_norm != 0, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}

@@ -1,0 +1,115 @@
+// Shared device helpers for the gfx950 (CDNA4) attention kernels.
+//
+// Register-layout facts the kernels rely on (64-lane wavefronts):
+//   v_mfma_f32_32x32x16_bf16: A is 32(M)x16(K), B is 16(K)x32(N); lane l holds
+//   8 consecutive-K operands of row/col l%32 in K-half l/32 (the same K
+//   assignment for A and B, so any consistent relabelling of K is a valid
+//   contraction). Accumulator register r = 4i + j of lane l holds
+//   C[8i + 4(l/32) + j][l%32].
+//   ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+//   (i%4) of the 4 x bf16 read by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4.
+//   Reading row-major B[k][n] with lane 4t+q addressing &B[k0+t][n0+4q] hands
+//   lane i the column B[k0..k0+3][n0+i]: a K-major MFMA operand straight
+//   from a row-major LDS tile, with no transposed copy.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+#define SA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 4 x bf16 transposed LDS read (see the header comment for the lane mapping).
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+
+// Sum / max over the lane pair (l, l^32).
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum over aligned groups of 8 or 16 consecutive lanes (DPP row operations).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+  x += dpp<0xB1>(x);                         // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);                         // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+
+__device__ __forceinline__ void unpack8(u32x4 w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  bf16x2 r;
+  r[0] = (bf16)a;
+  r[1] = (bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack2(f[2 * i], f[2 * i + 1]);
+  return w;
+}
+
+// Swap bits 2 and 3 of a 5-bit row index. Reading MFMA A-operand rows in this
+// order makes accumulator registers 8s..8s+7 of a lane hold 8 consecutive
+// rows (16s + 8(l/32) + 0..7), which is exactly the K-slot order of the next
+// MFMA's operand, so P and dS feed the next contraction without a shuffle.
+__device__ __forceinline__ int swap23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+}  // namespace sa

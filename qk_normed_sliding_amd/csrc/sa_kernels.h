@@ -1,0 +1,58 @@
+// Kernel parameter blocks and host-side launchers (internal to libsa_attn.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, T, Hq, Hkv, G;  // G = Hq / Hkv
+  int window;            // -1 = full causal (already normalised by the host)
+  float c1;              // softmax_scale * log2(e): logits in the base-2 domain
+  float c2;              // fixed row maximum (base 2) when the logits are bounded
+  float eps;
+  int nqb;               // number of 128-row query blocks
+  int nsub;              // workgroups per (batch, KV head, query block) = G / heads-per-workgroup
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;  // fp32 [B, T, Hq, D], scale already applied
+  float* delta;   // fp32 [B, Hq, T]
+  int B, T, Hq, Hkv, G;
+  int window;
+  float scale;
+  float c1;       // scale * log2(e)
+  float eps;
+  int nkb;        // number of key blocks
+};
+
+struct NormParams {
+  const void* x;
+  void* y;
+  float* rstd;
+  int64_t rows;
+  float eps;
+};
+
+// Launchers return hipGetLastError() after the launch.
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, bool fixed_max,
+                      hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream);
+hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the HIP runtime
+(so these run on a machine without a GPU; no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa_attn.h")
+LIB = os.path.join(ROOT, "qk_normed_sliding_amd", "libsa_attn.so")
+
+SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_ALIGN, SA_ERR_WORKSPACE, SA_ERR_HIP = range(7)
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not os.path.exists(LIB):
+        from qk_normed_sliding_amd import build as _b
+        _b.build()
+    import qk_normed_sliding_amd as pkg
+    return pkg
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("sa_qknorm", "sa_attn_fwd", "sa_attn_bwd", "sa_attn_bwd_workspace_bytes",
+              "sa_status_string", "sa_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(sa):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in _declared_functions() if n not in exported]
+    assert not missing, missing
+    # nothing else leaks out under an sa_ name
+    extra = sorted(n for n in exported if n.startswith("sa_") and n not in _declared_functions())
+    assert not extra, extra
+
+
+def test_version_and_status_strings(sa):
+    lib = sa.library()
+    assert lib.sa_abi_version() == sa.ABI_VERSION
+    for code in range(7):
+        assert lib.sa_status_string(code)
+    assert b"unknown" in lib.sa_status_string(99)
+
+
+def _fwd(lib, q=16, k=16, v=16, o=16, lse=16, B=1, T=8, Hq=4, Hkv=2, D=64, W=-1, scale=0.125, norm=1, eps=1e-6):
+    P = ctypes.c_void_p
+    return lib.sa_attn_fwd(P(q), P(k), P(v), P(o), P(lse), B, T, Hq, Hkv, D, W, scale, norm, eps, None)
+
+
+def test_forward_validation_paths(sa):
+    lib = sa.library()
+    assert _fwd(lib, q=0) == SA_ERR_NULL
+    assert _fwd(lib, lse=0) == SA_ERR_NULL
+    assert _fwd(lib, B=0) == SA_ERR_SHAPE
+    assert _fwd(lib, T=-1) == SA_ERR_SHAPE
+    assert _fwd(lib, Hq=3, Hkv=2) == SA_ERR_SHAPE
+    assert _fwd(lib, Hkv=0) == SA_ERR_SHAPE
+    assert _fwd(lib, W=-2) == SA_ERR_SHAPE
+    assert _fwd(lib, scale=float("nan")) == SA_ERR_SHAPE
+    assert _fwd(lib, eps=-1.0) == SA_ERR_SHAPE
+    assert _fwd(lib, D=96) == SA_ERR_UNSUPPORTED
+    assert _fwd(lib, D=256) == SA_ERR_UNSUPPORTED
+    assert _fwd(lib, q=24) == SA_ERR_ALIGN
+    assert _fwd(lib, o=8) == SA_ERR_ALIGN
+    assert _fwd(lib, lse=2) == SA_ERR_ALIGN
+
+
+def _bwd(lib, ws=256, ws_bytes=None, B=1, T=8, Hq=4, Hkv=2, D=64, W=-1, dq=16, null_lse=False):
+    P = ctypes.c_void_p
+    need = lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D)
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    lse = 0 if null_lse else 16
+    return lib.sa_attn_bwd(P(16), P(16), P(16), P(16), P(lse), P(16), P(dq), P(16), P(16), P(ws), ws_bytes,
+                           B, T, Hq, Hkv, D, W, 0.125, 1, 1e-6, None)
+
+
+def test_backward_validation_paths(sa):
+    lib = sa.library()
+    assert _bwd(lib, null_lse=True) == SA_ERR_NULL
+    assert _bwd(lib, dq=0) == SA_ERR_NULL
+    assert _bwd(lib, Hq=5, Hkv=2) == SA_ERR_SHAPE
+    assert _bwd(lib, D=32) == SA_ERR_UNSUPPORTED
+    assert _bwd(lib, ws=0) == SA_ERR_WORKSPACE
+    assert _bwd(lib, ws_bytes=16) == SA_ERR_WORKSPACE
+    assert _bwd(lib, ws=128) == SA_ERR_WORKSPACE  # not 256-byte aligned
+    assert _bwd(lib, dq=8) == SA_ERR_ALIGN
+
+
+def test_workspace_size(sa):
+    lib = sa.library()
+    B, T, Hq, Hkv, D = 16, 2048, 6, 3, 128
+    rows = B * T * Hq
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D) == r256(rows * D * 4) + r256(rows * 4)
+    assert lib.sa_attn_bwd_workspace_bytes(B, T, 5, Hkv, D) == 0
+    assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, 80) == 0
+
+
+def test_qknorm_validation_paths(sa):
+    lib = sa.library()
+    P = ctypes.c_void_p
+    assert lib.sa_qknorm(P(16), P(16), None, 0, 128, 1e-6, None) == SA_OK  # empty: nothing to do
+    assert lib.sa_qknorm(None, P(16), None, 4, 128, 1e-6, None) == SA_ERR_NULL
+    assert lib.sa_qknorm(P(16), P(16), None, -1, 128, 1e-6, None) == SA_ERR_SHAPE
+    assert lib.sa_qknorm(P(16), P(16), None, 4, 100, 1e-6, None) == SA_ERR_UNSUPPORTED
+    assert lib.sa_qknorm(P(16), P(20), None, 4, 128, 1e-6, None) == SA_ERR_ALIGN
+    assert lib.sa_qknorm(P(16), P(16), P(6), 4, 128, 1e-6, None) == SA_ERR_ALIGN
+
+
+def test_sssl_windows_host_helper_matches_pages(sa):
+    golden = os.path.join(ROOT, "tests", "golden", "sssl_8layer_map.txt")
+    kinds = [ln.split()[1] for ln in open(golden) if ln.strip() and not ln.startswith("#")]
+    w = sa.sssl_windows(8, 2048)
+    assert ["global" if x == -1 else "local" for x in w] == kinds
+    assert all(x == 1024 for x in w if x != -1)
+    assert sa.sssl_windows(6, 8192)[-1] == -1
+    assert sa.sssl_windows(8, 8192) == [4096, 4096, 4096, -1, 4096, 4096, 4096, -1]
+    with pytest.raises(ValueError):
+        sa.sssl_windows(4, 64, "SQ")
+
+
+def test_binding_rejects_cpu_tensors(sa):
+    import torch
+    q = torch.zeros(1, 8, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sa.sa_attn_fwd(q, k, k)

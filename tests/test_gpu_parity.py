@@ -1,0 +1,201 @@
+"""GPU parity of the HIP path (through the C ABI binding) against the fp64 oracle.
+
+Small cases span several tiles and ragged tails, every kernel variant
+(head_dim 64/128, 1 or 2 heads per workgroup, normed and un-normed, fixed and
+running row maximum) and the degenerate windows. The band-mask probe recovers
+the full inclusion matrix from the kernel and compares it bit-exactly.
+"""
+
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import (compare_backward, compare_forward, gpu_forward, gpu_fwd_bwd, log, max_abs, rel_l2,
+                         set_cpu_threads)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    set_cpu_threads()
+    import qk_normed_sliding_amd as pkg
+    return pkg
+
+
+def test_workload1_forward(sa):
+    w = synth.WORKLOADS[1]
+    q, k, v, _ = synth.layer_inputs(w, 0)
+    log(f"[workload 1] {w.name}")
+    o, lse = gpu_forward(sa, q, k, v, w.windows[0], w.scale, eps=w.eps)
+    assert o.shape == (1, 128, 4, 64)
+    compare_forward(o, lse, q, k, v, w.windows[0], w.scale, eps=w.eps)
+
+
+CASES = [
+    # B, T, Hq, Hkv, D, W, qk_norm, scale (None = 1/sqrt(D))
+    (2, 300, 4, 2, 128, -1, True, None),
+    (2, 300, 4, 2, 128, 100, True, None),
+    (1, 513, 6, 3, 128, 256, True, None),     # G = 3: one head per workgroup
+    (1, 257, 2, 2, 64, 64, True, None),       # MHA, D = 64
+    (1, 130, 4, 1, 64, 0, True, None),        # window 0: self only
+    (1, 1, 2, 1, 128, -1, True, None),        # single position
+    (1, 2, 2, 1, 64, -1, True, None),
+    (2, 200, 4, 2, 128, 1, True, None),
+    (1, 384, 4, 2, 128, 127, True, None),     # window edge on a tile boundary
+    (1, 384, 4, 2, 128, 128, True, None),
+    (1, 300, 4, 2, 128, 298, True, None),     # W = T - 2
+    (1, 300, 4, 2, 128, -1, False, None),     # no QK-norm: running maximum
+    (1, 300, 4, 2, 64, 50, False, 0.3),
+    (1, 200, 4, 2, 128, -1, True, 0.5),       # |scale| D large: running maximum with norm
+    (3, 160, 12, 2, 64, 33, True, None),      # G = 6
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}T{c[1]}Hq{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}n{int(c[6])}" for c in CASES])
+def test_small_forward_backward(sa, case):
+    B, T, Hq, Hkv, D, W, qk_norm, scale = case
+    scale = D ** -0.5 if scale is None else scale
+    log(f"[small] {case}")
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=100 + T)
+    o, lse, dq, dk, dv = gpu_fwd_bwd(sa, q, k, v, do, W, scale, qk_norm)
+    # The stated bounds hold at scale = 1/sqrt(D). Rounding the normed rows to
+    # bf16 moves each logit by an amount proportional to |scale| * |q_hat||k_hat|,
+    # so at a larger scale the forward bounds grow by |scale| sqrt(D).
+    grow = max(1.0, abs(scale) * D ** 0.5) if qk_norm else 1.0
+    compare_forward(o, lse, q, k, v, W, scale, qk_norm, o_tol=2e-2 * grow, lse_tol=2e-2 * grow)
+    compare_backward(dq, dk, dv, q, k, v, do, W, scale, qk_norm)
+
+
+@pytest.mark.parametrize("W", [-1, 0, 1, 63, 64, 127, 128, 129, 1000, 1024, 2046])
+def test_band_mask_bit_exact(sa, W):
+    """Probe: q rows along e0 and k rows along e1 give all-zero logits, so every
+    visible key gets the same weight. Batch b carries one-hot values on keys
+    128b .. 128b+127 (channel = key mod 128), so O[b, i, h, c] > 0 exactly when
+    key 128b + c is visible to query i. exp(LSE_i) counts the visible keys."""
+    B, T, Hq, Hkv, D = 16, 2048, 2, 1, 128
+    q = torch.zeros(B, T, Hq, D, dtype=torch.bfloat16)
+    k = torch.zeros(B, T, Hkv, D, dtype=torch.bfloat16)
+    q[..., 0] = 1.0
+    k[..., 1] = 1.0
+    v = torch.zeros(B, T, Hkv, D, dtype=torch.bfloat16)
+    for b in range(B):
+        for c in range(D):
+            v[b, 128 * b + c, 0, c] = 1.0
+    o, lse = gpu_forward(sa, q, k, v, W, D ** -0.5)
+    o = o.float().cpu()
+    incl = torch.zeros(T, T, dtype=torch.bool)
+    for h in range(Hq):
+        got = (o[:, :, h, :] > 0).permute(1, 0, 2).reshape(T, T)  # [i, 128 b + c]
+        incl = got if h == 0 else incl
+        assert torch.equal(got, incl)
+    ref = oracle.band_mask(T, W)
+    bad = (incl != ref).nonzero()
+    assert bad.numel() == 0, f"first mismatches (i, j): {bad[:5].tolist()}"
+    n = ref.sum(-1).double()
+    counts = torch.exp(lse.double().cpu())
+    assert torch.equal(torch.round(counts), n.view(1, 1, T).expand_as(counts))
+
+
+def test_window_zero_returns_v_and_constant_v(sa):
+    B, T, Hq, Hkv, D = 2, 300, 4, 2, 128
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=5)
+    o, lse, dq, dk, dv = gpu_fwd_bwd(sa, q, k, v, do, 0, D ** -0.5)
+    v_rep = v.repeat_interleave(2, dim=2).float()
+    ulp = torch.maximum(v_rep.abs(), torch.full_like(v_rep, 2.0 ** -126)) * 2.0 ** -7
+    assert bool(((o.float().cpu() - v_rep).abs() <= ulp).all())
+    dv_ref = do.float().view(B, T, Hkv, 2, D).sum(3)
+    assert rel_l2(dv.cpu(), dv_ref) < 1e-2
+    assert float(dq.float().abs().max()) < 1e-1 and float(dk.float().abs().max()) < 1e-1
+    # constant values: every output is 1 up to one bf16 ulp
+    ones = torch.ones_like(v)
+    for W in (-1, 77):
+        o1, _ = gpu_forward(sa, q, k, ones, W, D ** -0.5)
+        assert float((o1.float() - 1).abs().max()) <= 2.0 ** -7
+
+
+def test_gqa_equals_mha_with_repeated_kv(sa):
+    B, T, Hq, Hkv, D = 2, 333, 6, 3, 128
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=9)
+    kr, vr = k.repeat_interleave(2, dim=2), v.repeat_interleave(2, dim=2)
+    for W in (-1, 100):
+        o, lse, dq, dk, dv = gpu_fwd_bwd(sa, q, k, v, do, W, D ** -0.5)
+        om, lsem, dqm, dkm, dvm = gpu_fwd_bwd(sa, q, kr, vr, do, W, D ** -0.5)
+        assert torch.equal(o, om) and torch.equal(lse, lsem)
+        assert rel_l2(dq.cpu(), dqm.cpu()) < 1e-2
+        assert rel_l2(dk.cpu(), dkm.float().cpu().view(B, T, Hkv, 2, D).sum(3)) < 1e-2
+        assert rel_l2(dv.cpu(), dvm.float().cpu().view(B, T, Hkv, 2, D).sum(3)) < 1e-2
+
+
+def test_window_at_least_T_minus_1_is_full_causal(sa):
+    B, T, Hq, Hkv, D = 1, 200, 4, 2, 64
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=11)
+    ref = gpu_fwd_bwd(sa, q, k, v, do, -1, 0.125)
+    for W in (T - 1, T, 10 * T):
+        got = gpu_fwd_bwd(sa, q, k, v, do, W, 0.125)
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b)
+
+
+def test_qknorm_standalone(sa):
+    for D in (64, 128):
+        x = synth.small_case(3, 77, 5, 5, D, seed=D)[0]
+        x[0, 0, 0] = 0  # zero row
+        xd = x.cuda()
+        y, rstd = sa.sa_qknorm(xd)
+        torch.cuda.synchronize()
+        y_ref, r_ref = oracle.qknorm(x.view(-1, D))
+        y_ref = y_ref.view(x.shape)
+        r_ref = r_ref.view(x.shape[:-1])
+        # y is the bf16 rounding of the exact value: within one bf16 ulp
+        assert bool(((y.double().cpu() - y_ref).abs() <= y_ref.abs() * 2.0 ** -7 + 1e-30).all())
+        assert float(((rstd.double().cpu() - r_ref).abs() / r_ref).max()) < 1e-5
+        ms = (y.double().cpu() ** 2).mean(-1)
+        assert float((ms[1:] - 1).abs().max()) < 2 ** -6
+        # in place
+        x2 = xd.clone()
+        sa.sa_qknorm(x2, y=x2, want_rstd=False)
+        torch.cuda.synchronize()
+        assert torch.equal(x2, y)
+
+
+def test_norm_then_plain_attention_matches_fused(sa):
+    B, T, Hq, Hkv, D = 1, 260, 4, 2, 128
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=13)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    qn, _ = sa.sa_qknorm(qd)
+    kn, _ = sa.sa_qknorm(kd)
+    o_split, _ = sa.sa_attn_fwd(qn, kn, vd, window=64, qk_norm=False)
+    o_fused, _ = sa.sa_attn_fwd(qd, kd, vd, window=64, qk_norm=True)
+    torch.cuda.synchronize()
+    # the two paths round differently (row sums of squares in another order,
+    # running vs fixed row maximum): same bound as against the oracle
+    err = max_abs(o_split.cpu(), o_fused.cpu())
+    log(f"  split vs fused O max-abs {err:.3e}")
+    assert err <= 2e-2
+
+
+def test_tiles_outside_the_band_are_never_read(sa):
+    """NaN in K/V rows [0, 512): queries whose windows start at or after row 512
+    (and whose 128-row blocks' bands do too) must stay finite and correct."""
+    B, T, Hq, Hkv, D, W = 1, 2048, 4, 2, 128, 256
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=21)
+    kp, vp = k.clone(), v.clone()
+    kp[:, :512] = float("nan")
+    vp[:, :512] = float("nan")
+    o, lse, dq, dk, dv = gpu_fwd_bwd(sa, q, kp, vp, do, W, D ** -0.5)
+    o_ref, lse_ref = oracle.attn_forward(q, k, v, W, D ** -0.5)
+    rows = slice(896, T)  # block start >= 896 -> first key >= 640
+    assert torch.isfinite(o[:, rows].float()).all()
+    assert max_abs(o[:, rows].cpu(), o_ref[:, rows]) <= 2e-2
+    assert max_abs(lse[:, :, rows].cpu(), lse_ref[:, :, rows]) <= 2e-2
+    # gradients of keys >= 1024 only involve queries >= 1024, whose windows are clean
+    dq_r, dk_r, dv_r = oracle.attn_backward(q, k, v, do, W, D ** -0.5)
+    keys = slice(1024, T)
+    assert torch.isfinite(dk[:, keys].float()).all() and torch.isfinite(dv[:, keys].float()).all()
+    assert rel_l2(dk[:, keys].cpu(), dk_r[:, keys]) < 5e-2
+    assert rel_l2(dv[:, keys].cpu(), dv_r[:, keys]) < 5e-2
+    assert rel_l2(dq[:, 1280:].cpu(), dq_r[:, 1280:]) < 5e-2

@@ -1,0 +1,92 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times (one sa_attn_fwd + sa_attn_bwd call per layer over the whole batch).
+
+The GPU computes every layer at full size; the fp64 oracle recomputes whole
+(batch, KV-head group) slices of it — each slice is an independent instance
+of the same definition (its query heads, its KV head, all T positions) — and
+the slice's outputs and gradients are compared element by element.
+
+Workload 5 scales a seeded 10 % of the head rows of q, k, v and dO by 8. With
+v rows scaled, |O| reaches ~15-26, where one bf16 step is 0.0625-0.125, so
+storing O in bf16 alone can exceed a 2e-2 absolute bound. For that workload O
+is held to |diff| <= 2e-2 + 2^-7 |O_ref| elementwise (one bf16 step relative
+on top of the absolute bound), and a variant that scales only q and k (the
+rows that reach the softmax) is held to the plain 2e-2 bound.
+"""
+
+import pytest
+import torch
+
+import synth
+from gpu_helpers import compare_backward, compare_forward, gpu_fwd_bwd, log, set_cpu_threads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    set_cpu_threads()
+    import qk_normed_sliding_amd as pkg
+    return pkg
+
+
+def _check_slices(w, layer, q, k, v, do, out, slices, o_rel=0.0):
+    o, lse, dq, dk, dv = out
+    W = w.windows[layer]
+    G = w.Hq // w.Hkv
+    for b, g in slices:
+        hs = slice(g * G, (g + 1) * G)
+        ks = slice(g, g + 1)
+        log(f"  layer {layer} W={W} slice b={b} g={g}")
+        qs, kk, vs, ds = q[b:b + 1, :, hs], k[b:b + 1, :, ks], v[b:b + 1, :, ks], do[b:b + 1, :, hs]
+        os_, ls = o[b:b + 1, :, hs], lse[b:b + 1, hs]
+        if o_rel > 0:
+            import oracle
+            o_ref, lse_ref = oracle.attn_forward(qs, kk, vs, W, w.scale, eps=w.eps)
+            diff = (os_.cpu().double() - o_ref).abs()
+            bound = 2e-2 + o_rel * o_ref.abs()
+            log(f"  O max-abs {float(diff.max()):.3e} (mixed bound), LSE max-abs "
+                f"{float((ls.cpu().double() - lse_ref).abs().max()):.3e}")
+            assert bool((diff <= bound).all())
+            assert float((ls.cpu().double() - lse_ref).abs().max()) <= 2e-2
+        else:
+            compare_forward(os_, ls, qs, kk, vs, W, w.scale, eps=w.eps)
+        compare_backward(dq[b:b + 1, :, hs], dk[b:b + 1, :, ks], dv[b:b + 1, :, ks], qs, kk, vs, ds, W, w.scale,
+                         eps=w.eps)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_single_layer_workloads(sa, cfg):
+    w = synth.WORKLOADS[cfg]
+    log(f"[workload {cfg}] {w.name}")
+    q, k, v, do = synth.layer_inputs(w, 0)
+    out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[0], w.scale, eps=w.eps)
+    _check_slices(w, 0, q, k, v, do, out, [(0, 0), (w.B - 1, w.Hkv - 1)])
+
+
+def test_sssl_stack_workload(sa):
+    w = synth.WORKLOADS[4]
+    log(f"[workload 4] {w.name}")
+    for layer in range(w.n_layer):
+        q, k, v, do = synth.layer_inputs(w, layer)
+        out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[layer], w.scale, eps=w.eps)
+        _check_slices(w, layer, q, k, v, do, out, [(layer % w.B, layer % w.Hkv)])
+
+
+@pytest.mark.parametrize("layer", [0, 3])
+def test_long_context_workload(sa, layer):
+    w = synth.WORKLOADS[5]
+    log(f"[workload 5] {w.name} layer {layer}")
+    q, k, v, do = synth.layer_inputs(w, layer)
+    out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[layer], w.scale, eps=w.eps)
+    _check_slices(w, layer, q, k, v, do, out, [(layer % w.B, 1)], o_rel=2.0 ** -7)
+
+
+def test_long_context_qk_rows_only(sa):
+    w = synth.WORKLOADS[5]
+    log(f"[workload 5, q/k rows scaled only] layer 6")
+    q, k, v, do = synth.layer_inputs(w, 6, qk_rows_only=True)
+    out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[6], w.scale, eps=w.eps)
+    _check_slices(w, 6, q, k, v, do, out, [(2, 2)])
