@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Attention fwd+bwd throughput of the 8-layer SSSL stack on one MI355X.
+
+One step = the whole hot path over one batch: the forward of all 8 layers
+(sa_attn_fwd, each layer on its own seeded inputs) followed by the backward of
+all 8 layers in reverse order (sa_attn_bwd). Inputs, outputs and the backward
+workspace are resident in HBM before the timed region starts.
+
+Work is counted on the band only: a (query, key) pair is counted when key j is
+visible to query i (0 <= i - j <= W, or j <= i for a full causal layer), at
+4*D FLOP per pair for the forward (Q K^T and P V) and 10*D for the backward
+(S recompute, dV, dP, dK, dQ). Masked halves of edge tiles and skipped tiles
+count nothing.
+
+Output: one JSON line (see the contract in the repository's documentation),
+with a "roofline" object for the dominant kernel timed with HIP events
+around each of its launches inside the timed region, and a "cpu_baseline"
+object: the fp64 oracle timed on the host cores on a bounded sample of the
+same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 4]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def band_pairs(T: int, W: int) -> int:
+    """Visible (query, key) pairs of one head: rows i >= W see W+1 keys, rows i < W see i+1."""
+    if W < 0 or W >= T - 1:
+        return T * (T + 1) // 2
+    return (W + 1) * (T - W) + W * (W + 1) // 2
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the oracle sample (0 disables the CPU baseline)")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="do not bracket the main kernels with HIP events")
+    return ap.parse_args()
+
+
+class Hip:
+    """Minimal HIP event API from the runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        h = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return h.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, h):
+        self.lib.hipEventDestroy(ctypes.c_void_p(h))
+
+
+def cpu_baseline(w, budget_s):
+    """Time the fp64 oracle (as it stands) on whole (batch, KV-group) slices of
+    one sliding-window layer and one full-causal layer of the workload,
+    alternating, until the budget is used; report band FLOP/s."""
+    import torch
+
+    import oracle
+    import synth
+
+    torch.set_num_threads(max(1, os.cpu_count() or 1))
+    G = w.Hq // w.Hkv
+    local = next(i for i, W in enumerate(w.windows) if W >= 0)
+    full = next(i for i, W in enumerate(w.windows) if W < 0) if -1 in w.windows else local
+    picked = sorted({local, full})
+    inputs = {layer: synth.layer_inputs(w, layer) for layer in picked}
+    flops = spent = 0.0
+    n = {layer: 0 for layer in picked}
+    i = 0
+    while spent < budget_s and i < len(picked) * w.B * w.Hkv:
+        layer = picked[i % len(picked)]
+        b = (i // len(picked)) % w.B
+        g = (i // (len(picked) * w.B)) % w.Hkv
+        q, k, v, do = inputs[layer]
+        hs = slice(g * G, (g + 1) * G)
+        qs, ks, vs, ds = q[b:b + 1, :, hs], k[b:b + 1, :, g:g + 1], v[b:b + 1, :, g:g + 1], do[b:b + 1, :, hs]
+        W = w.windows[layer]
+        t0 = time.perf_counter()
+        oracle.attn_forward(qs, ks, vs, W, w.scale, eps=w.eps)
+        oracle.attn_backward(qs, ks, vs, ds, W, w.scale, eps=w.eps)
+        spent += time.perf_counter() - t0
+        flops += 14.0 * w.D * G * band_pairs(w.T, W)
+        n[layer] += 1
+        i += 1
+    parts = ", ".join(f"{n[layer]} of layer {layer} (window {w.windows[layer]})" for layer in picked)
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": torch.get_num_threads(),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle forward+backward on whole (batch, KV-group) slices ({G} query heads, "
+                   f"T={w.T}) of the same workload: {parts}; {spent:.1f} s of oracle time; "
+                   f"band FLOPs counted as on the GPU"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import qk_normed_sliding_amd as sa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    G = w.Hq // w.Hkv
+
+    layers = []
+    for layer in range(w.n_layer):
+        q, k, v, do = (x.to(dev) for x in synth.layer_inputs(w, layer))
+        layers.append(dict(
+            W=w.windows[layer], q=q, k=k, v=v, do=do,
+            o=torch.empty_like(q), lse=torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev),
+            dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v)))
+    ws = torch.empty(sa.sa_attn_bwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def fwd(L):
+        sa.sa_attn_fwd(L["q"], L["k"], L["v"], window=L["W"], softmax_scale=w.scale, eps=w.eps, o=L["o"], lse=L["lse"])
+
+    def bwd(L):
+        sa.sa_attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=L["W"], softmax_scale=w.scale,
+                       eps=w.eps, dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=ws)
+
+    hip = Hip()
+    use_ev = not args.no_kernel_events
+    # one event pair per launch of each main kernel in the timed region
+    n_ev = args.steps * w.n_layer
+    ev_f = [(hip.event(), hip.event()) for _ in range(n_ev)] if use_ev else []
+    ev_b = [(hip.event(), hip.event()) for _ in range(n_ev)] if use_ev else []
+
+    def step(s=None):
+        for li, L in enumerate(layers):
+            if s is not None and use_ev:
+                sa.sa_set_timing_events(sa.SA_KERNEL_FWD, *ev_f[s * w.n_layer + li])
+            fwd(L)
+        for li in reversed(range(w.n_layer)):
+            if s is not None and use_ev:
+                sa.sa_set_timing_events(sa.SA_KERNEL_BWD_MAIN, *ev_b[s * w.n_layer + li])
+            bwd(layers[li])
+        if use_ev:
+            sa.sa_set_timing_events(sa.SA_KERNEL_FWD, None, None)
+            sa.sa_set_timing_events(sa.SA_KERNEL_BWD_MAIN, None, None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for s in range(args.steps):
+        step(s)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+
+    pairs = [w.B * w.Hq * band_pairs(w.T, L["W"]) for L in layers]
+    flop_fwd = sum(4.0 * w.D * p for p in pairs)
+    flop_bwd = sum(10.0 * w.D * p for p in pairs)
+    flop_step = flop_fwd + flop_bwd
+    tflops = flop_step / (ms_step * 1e-3) / 1e12
+
+    kern = {}
+    if use_ev:
+        tf = sum(hip.elapsed_ms(a, b) for a, b in ev_f) / args.steps
+        tb = sum(hip.elapsed_ms(a, b) for a, b in ev_b) / args.steps
+        kern = {"fwd_kernel_ms_per_step": tf, "bwd_main_kernel_ms_per_step": tb,
+                "fwd_kernel_tflops": flop_fwd / (tf * 1e-3) / 1e12,
+                "bwd_main_kernel_tflops": flop_bwd / (tb * 1e-3) / 1e12,
+                "other_kernels_ms_per_step": ms_step - tf - tb}
+        dom = "bwd" if tb >= tf else "fwd"
+        name = "attn_bwd_kernel" if dom == "bwd" else "attn_fwd_kernel"
+        flop_launch = (flop_bwd if dom == "bwd" else flop_fwd) / w.n_layer
+        avg_ms = (tb if dom == "bwd" else tf) / w.n_layer
+        achieved = flop_launch / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                    "avg_launch_ms": avg_ms, "algorithmic_flop_per_launch": flop_launch}
+        for a, b in ev_f + ev_b:
+            hip.destroy(a)
+            hip.destroy(b)
+    else:
+        roofline = None
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    out = {
+        "metric": "attention fwd+bwd TFLOP/s (band-counted), SSSL 8-layer T=2048; % bf16 MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v/dO of the model shape; no dataset or trained weights)",
+        "config": {
+            "workload": w.name,
+            "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
+            "windows": list(w.windows), "qk_norm": True, "eps": w.eps, "softmax_scale": w.scale,
+            "flop_count": "band pairs x (4D fwd + 10D bwd)",
+            "flop_per_step": flop_step,
+            "parallelism": "single GPU",
+        },
+        "wall_s_timed": wall,
+        "kernels": kern,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

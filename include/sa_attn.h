@@ -40,8 +40,8 @@
  *   - Errors: every argument is validated before anything is launched, so an
  *     error return means nothing was enqueued. Faults inside a kernel surface
  *     at the caller's next synchronisation, as with any stream operation.
- *   - Thread safety: no mutable global state; concurrent calls on different
- *     streams are safe.
+ *   - Thread safety: no mutable global state (the benchmarking hook below is
+ *     per host thread); concurrent calls on different streams are safe.
  */
 #ifndef SA_ATTN_H
 #define SA_ATTN_H
@@ -121,6 +121,22 @@ sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes,
                       int B, int T, int Hq, int Hkv, int head_dim, int window,
                       float softmax_scale, int qk_norm, float eps, void* stream);
+
+/* Main kernels that sa_set_timing_events can bracket. */
+enum { SA_KERNEL_FWD = 0, SA_KERNEL_BWD_MAIN = 1 };
+
+/*
+ * sa_set_timing_events - benchmarking hook (not part of the computation).
+ *   While set, every later sa_attn_fwd (kernel = SA_KERNEL_FWD) or
+ *   sa_attn_bwd (kernel = SA_KERNEL_BWD_MAIN, its dK/dV/dQ kernel) call made
+ *   FROM THE CALLING HOST THREAD records `start` on its stream right before
+ *   that main kernel and `stop` right after it, so hipEventElapsedTime(start,
+ *   stop) is the kernel's own duration. start/stop are hipEvent_t handles
+ *   passed as void*, created and owned by the caller; pass NULL, NULL to clear.
+ *   Returns SA_ERR_SHAPE for an unknown kernel id, SA_ERR_NULL if exactly one
+ *   of start/stop is NULL.
+ */
+sa_status sa_set_timing_events(int kernel, void* start, void* stop);
 
 #ifdef __cplusplus
 }

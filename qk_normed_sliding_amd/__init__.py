@@ -26,6 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libsa_attn.so")
 
 SA_OK = 0
 ABI_VERSION = 1
+SA_KERNEL_FWD = 0
+SA_KERNEL_BWD_MAIN = 1
 
 
 class SAError(RuntimeError):
@@ -56,6 +58,8 @@ def _load():
     lib.sa_attn_bwd.restype = i32
     lib.sa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                 i32, i32, i32, i32, i32, i32, f32, i32, f32, vp]
+    lib.sa_set_timing_events.restype = i32
+    lib.sa_set_timing_events.argtypes = [i32, vp, vp]
     if lib.sa_abi_version() != ABI_VERSION:
         raise ImportError(f"libsa_attn ABI {lib.sa_abi_version()} != expected {ABI_VERSION}")
     return lib
@@ -176,6 +180,14 @@ def sa_attn_bwd(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=Tr
         _ptr(workspace), workspace.numel(), B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D),
         int(bool(qk_norm)), float(eps), _stream(q.device, stream)))
     return dq, dk, dv
+
+
+def sa_set_timing_events(kernel, start_event, stop_event):
+    """Benchmarking hook: record raw hipEvent_t handles (ints, or None to clear)
+    around the main kernel of later calls from this thread."""
+    _check("sa_set_timing_events", _lib.sa_set_timing_events(
+        int(kernel), ctypes.c_void_p(start_event) if start_event else None,
+        ctypes.c_void_p(stop_event) if stop_event else None))
 
 
 # ------------------------------------------------------------------ helpers

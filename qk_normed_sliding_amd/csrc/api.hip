@@ -15,6 +15,10 @@ namespace {
 
 constexpr int kAbiVersion = 1;
 
+// Benchmarking hook: events recorded around the main kernel of later calls
+// made from this host thread (see sa_set_timing_events).
+thread_local sa::TimingEvents tl_events[2];
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 bool valid_dim(int d) { return d == 64 || d == 128; }
@@ -100,8 +104,10 @@ SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* 
   const int hpw = (p.G % 2 == 0) ? 2 : 1;
   p.nsub = p.G / hpw;
   p.nqb = (T + 127) / 128;
-  return sa::launch_fwd(p, head_dim, hpw, qk_norm != 0, fixed, (hipStream_t)stream) == hipSuccess ? SA_OK
-                                                                                                    : SA_ERR_HIP;
+  return sa::launch_fwd(p, head_dim, hpw, qk_norm != 0, fixed, (hipStream_t)stream, tl_events[SA_KERNEL_FWD]) ==
+                 hipSuccess
+             ? SA_OK
+             : SA_ERR_HIP;
 }
 
 SA_API size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
@@ -147,5 +153,15 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
   p.c1 = softmax_scale * 1.4426950408889634f;
   p.eps = eps;
   p.nkb = (T + 127) / 128;
-  return sa::launch_bwd(p, head_dim, qk_norm != 0, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+  return sa::launch_bwd(p, head_dim, qk_norm != 0, (hipStream_t)stream, tl_events[SA_KERNEL_BWD_MAIN]) == hipSuccess
+             ? SA_OK
+             : SA_ERR_HIP;
+}
+
+SA_API sa_status sa_set_timing_events(int kernel, void* start, void* stop) {
+  if (kernel != SA_KERNEL_FWD && kernel != SA_KERNEL_BWD_MAIN) return SA_ERR_SHAPE;
+  if ((start == nullptr) != (stop == nullptr)) return SA_ERR_NULL;
+  tl_events[kernel].start = (hipEvent_t)start;
+  tl_events[kernel].stop = (hipEvent_t)stop;
+  return SA_OK;
 }

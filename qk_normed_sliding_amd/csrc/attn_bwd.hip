@@ -373,26 +373,32 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdParams p) {
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdParams& p, bool qk_norm, hipStream_t stream) {
+static hipError_t launch_bwd_d(const BwdParams& p, bool qk_norm, hipStream_t stream, const TimingEvents& ev) {
   constexpr int BQ = 64;
   const long rows = (long)p.B * p.T * p.Hq;
   const int rpb = 256 / (D / 8);
   const long nblk = (rows + rpb - 1) / rpb;
   const unsigned row_blocks = (unsigned)(nblk < 65536L ? nblk : 65536L);
   hipLaunchKernelGGL((attn_bwd_pre_kernel<D>), dim3(row_blocks), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(p.nkb * p.B * p.Hkv));
-  if (qk_norm) {
+  if (ev.start != nullptr && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
+  if (qk_norm)
     hipLaunchKernelGGL((attn_bwd_kernel<D, BQ, true>), grid, dim3(256), 0, stream, p);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), dim3(row_blocks), dim3(256), 0, stream, p);
-  } else {
+  else
     hipLaunchKernelGGL((attn_bwd_kernel<D, BQ, false>), grid, dim3(256), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev.stop != nullptr && (e = hipEventRecord(ev.stop, stream)) != hipSuccess) return e;
+  if (qk_norm)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), dim3(row_blocks), dim3(256), 0, stream, p);
+  else
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), dim3(row_blocks), dim3(256), 0, stream, p);
-  }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream) {
-  return head_dim == 128 ? launch_bwd_d<128>(p, qk_norm, stream) : launch_bwd_d<64>(p, qk_norm, stream);
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream, const TimingEvents& ev) {
+  return head_dim == 128 ? launch_bwd_d<128>(p, qk_norm, stream, ev) : launch_bwd_d<64>(p, qk_norm, stream, ev);
 }
 
 }  // namespace sa

@@ -262,26 +262,33 @@ __global__ void __launch_bounds__(HPW * 4 * 64) attn_fwd_kernel(FwdParams p) {
 }
 
 template <int D, int HPW>
-static hipError_t launch_fwd_d(const FwdParams& p, bool qk_norm, bool fixed_max, hipStream_t stream) {
+static hipError_t launch_fwd_d(const FwdParams& p, bool qk_norm, bool fixed_max, hipStream_t stream,
+                               const TimingEvents& ev) {
   constexpr int BN = 64;
   const dim3 grid((unsigned)(p.nqb * p.B * p.Hkv * p.nsub));
   const dim3 block(HPW * 4 * 64);
+  if (ev.start != nullptr) {
+    const hipError_t e = hipEventRecord(ev.start, stream);
+    if (e != hipSuccess) return e;
+  }
   if (qk_norm && fixed_max)
     hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, BN, true, true>), grid, block, 0, stream, p);
   else if (qk_norm)
     hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, BN, true, false>), grid, block, 0, stream, p);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, BN, false, false>), grid, block, 0, stream, p);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
+  return e;
 }
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, bool fixed_max,
-                      hipStream_t stream) {
+                      hipStream_t stream, const TimingEvents& ev) {
   if (head_dim == 128)
-    return heads_per_wg == 2 ? launch_fwd_d<128, 2>(p, qk_norm, fixed_max, stream)
-                             : launch_fwd_d<128, 1>(p, qk_norm, fixed_max, stream);
-  return heads_per_wg == 2 ? launch_fwd_d<64, 2>(p, qk_norm, fixed_max, stream)
-                           : launch_fwd_d<64, 1>(p, qk_norm, fixed_max, stream);
+    return heads_per_wg == 2 ? launch_fwd_d<128, 2>(p, qk_norm, fixed_max, stream, ev)
+                             : launch_fwd_d<128, 1>(p, qk_norm, fixed_max, stream, ev);
+  return heads_per_wg == 2 ? launch_fwd_d<64, 2>(p, qk_norm, fixed_max, stream, ev)
+                           : launch_fwd_d<64, 1>(p, qk_norm, fixed_max, stream, ev);
 }
 
 }  // namespace sa

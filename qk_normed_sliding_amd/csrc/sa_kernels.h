@@ -49,10 +49,16 @@ struct NormParams {
   float eps;
 };
 
-// Launchers return hipGetLastError() after the launch.
+// Optional events recorded around a call's main kernel (benchmarking hook).
+struct TimingEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// Launchers return the first HIP error seen (hipGetLastError() after the launches).
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, bool fixed_max,
-                      hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream);
+                      hipStream_t stream, const TimingEvents& ev);
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream, const TimingEvents& ev);
 hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace sa
