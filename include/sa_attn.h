@@ -56,7 +56,8 @@ extern "C" {
 typedef enum {
   SA_OK = 0,
   SA_ERR_NULL = 1,        /* a required pointer is NULL */
-  SA_ERR_SHAPE = 2,       /* a size <= 0, Hq % Hkv != 0, window < -1, or a size overflow */
+  SA_ERR_SHAPE = 2,       /* a size <= 0, Hq % Hkv != 0, window < -1, a non-finite scale or eps,
+                             eps < 0, or T*Hq*128*4 >= 2^31 (per-batch 32-bit addressing) */
   SA_ERR_UNSUPPORTED = 3, /* head_dim not in {64, 128} */
   SA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   SA_ERR_WORKSPACE = 5,   /* backward workspace NULL or smaller than sa_attn_bwd_workspace_bytes() */
@@ -112,9 +113,11 @@ size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
  *   dq, dk, dv            : bf16 outputs, fully overwritten.
  *   workspace             : device buffer of at least
  *                           sa_attn_bwd_workspace_bytes(B,T,Hq,Hkv,head_dim)
- *                           bytes, 256-byte aligned; contents on entry are
- *                           ignored and on return unspecified. Two calls that
- *                           overlap in time must use different workspaces.
+ *                           bytes (an fp32 dQ accumulator, the fp32 Delta rows
+ *                           and the bf16 normed q rows), 256-byte aligned;
+ *                           contents on entry are ignored and on return
+ *                           unspecified. Two calls that overlap in time must
+ *                           use different workspaces.
  */
 sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dout, void* dq, void* dk, void* dv,

@@ -41,7 +41,7 @@ class SAError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m qk_normed_sliding_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python qk_normed_sliding_amd/build.py` "
             "(the HIP library is required; there is no fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t

@@ -1,6 +1,7 @@
 """Build libsa_attn.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-Usage: python -m qk_normed_sliding_amd.build   (always recompiles)
+Usage: python qk_normed_sliding_amd/build.py   (always recompiles; run it as a
+file: importing the package loads the library, which must exist first)
 """
 
 from __future__ import annotations

@@ -35,6 +35,9 @@ sa_status check_shape(int B, int T, int Hq, int Hkv, int head_dim, int window, f
   const double elems = (double)B * T * (double)Hq * 128.0;
   if (elems > 9.0e18) return SA_ERR_SHAPE;
   if ((double)B * Hq * ((T + 127) / 128) > 2.0e9) return SA_ERR_SHAPE;
+  // one batch's rows of q (or k, v, and the fp32 dQ accumulator) are addressed
+  // with 32-bit byte offsets
+  if ((double)T * Hq * 128.0 * 4.0 >= 2147483648.0) return SA_ERR_SHAPE;
   if (!valid_dim(head_dim)) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
@@ -113,7 +116,8 @@ SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* 
 SA_API size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
   if (check_shape(B, T, Hq, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
   const size_t rows = (size_t)B * T * Hq;
-  return round256(rows * head_dim * sizeof(float)) + round256(rows * sizeof(float));
+  // fp32 dQ accumulator, fp32 Delta, bf16 normed q rows
+  return round256(rows * head_dim * sizeof(float)) + round256(rows * sizeof(float)) + round256(rows * head_dim * 2);
 }
 
 SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -143,6 +147,7 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
   const size_t rows = (size_t)B * T * Hq;
   p.dq_acc = (float*)workspace;
   p.delta = (float*)((char*)workspace + round256(rows * head_dim * sizeof(float)));
+  p.qhat = qk_norm ? (void*)((char*)p.delta + round256(rows * sizeof(float))) : (void*)q;
   p.B = B;
   p.T = T;
   p.Hq = Hq;

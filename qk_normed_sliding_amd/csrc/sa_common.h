@@ -78,6 +78,16 @@ __device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_r
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Raw buffer loads: a scalar resource (base, byte range) plus a 32-bit lane
+// offset. Reads at or past `bytes` return zero, which zero-fills ragged tails
+// without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }

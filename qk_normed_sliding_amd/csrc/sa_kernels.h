@@ -31,8 +31,9 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;  // fp32 [B, T, Hq, D], scale already applied
+  float* dq_acc;  // fp32 [B, T, Hq, D]: sum_j dS_ij k_hat_j, before the softmax scale
   float* delta;   // fp32 [B, Hq, T]
+  void* qhat;     // bf16 [B, T, Hq, D]: normed q rows (written by the pre-pass), or q itself without the norm
   int B, T, Hq, Hkv, G;
   int window;
   float scale;
