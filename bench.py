@@ -166,21 +166,23 @@ def main():
     use_ev = not args.no_kernel_events
     # one event pair per launch of each main kernel in the timed region
     n_ev = args.steps * w.n_layer
-    ev_f = [(hip.event(), hip.event()) for _ in range(n_ev)] if use_ev else []
-    ev_b = [(hip.event(), hip.event()) for _ in range(n_ev)] if use_ev else []
+    kinds = ("fwd", "bwd_dq", "bwd_dkdv")
+    hook = {"fwd": sa.SA_KERNEL_FWD, "bwd_dq": sa.SA_KERNEL_BWD_DQ, "bwd_dkdv": sa.SA_KERNEL_BWD_DKDV}
+    ev = {k: [(hip.event(), hip.event()) for _ in range(n_ev)] if use_ev else [] for k in kinds}
 
     def step(s=None):
         for li, L in enumerate(layers):
             if s is not None and use_ev:
-                sa.sa_set_timing_events(sa.SA_KERNEL_FWD, *ev_f[s * w.n_layer + li])
+                sa.sa_set_timing_events(hook["fwd"], *ev["fwd"][s * w.n_layer + li])
             fwd(L)
         for li in reversed(range(w.n_layer)):
             if s is not None and use_ev:
-                sa.sa_set_timing_events(sa.SA_KERNEL_BWD_MAIN, *ev_b[s * w.n_layer + li])
+                sa.sa_set_timing_events(hook["bwd_dq"], *ev["bwd_dq"][s * w.n_layer + li])
+                sa.sa_set_timing_events(hook["bwd_dkdv"], *ev["bwd_dkdv"][s * w.n_layer + li])
             bwd(layers[li])
         if use_ev:
-            sa.sa_set_timing_events(sa.SA_KERNEL_FWD, None, None)
-            sa.sa_set_timing_events(sa.SA_KERNEL_BWD_MAIN, None, None)
+            for k in kinds:
+                sa.sa_set_timing_events(hook[k], None, None)
 
     for _ in range(args.warmup):
         step()
@@ -204,26 +206,31 @@ def main():
     tflops = flop_step / (ms_step * 1e-3) / 1e12
 
     kern = {}
+    roofline = None
     if use_ev:
-        tf = sum(hip.elapsed_ms(a, b) for a, b in ev_f) / args.steps
-        tb = sum(hip.elapsed_ms(a, b) for a, b in ev_b) / args.steps
-        kern = {"fwd_kernel_ms_per_step": tf, "bwd_main_kernel_ms_per_step": tb,
-                "fwd_kernel_tflops": flop_fwd / (tf * 1e-3) / 1e12,
-                "bwd_main_kernel_tflops": flop_bwd / (tb * 1e-3) / 1e12,
-                "other_kernels_ms_per_step": ms_step - tf - tb}
-        dom = "bwd" if tb >= tf else "fwd"
-        name = "attn_bwd_kernel" if dom == "bwd" else "attn_fwd_kernel"
-        flop_launch = (flop_bwd if dom == "bwd" else flop_fwd) / w.n_layer
-        avg_ms = (tb if dom == "bwd" else tf) / w.n_layer
+        # MFMA FLOP each kernel executes per visible pair: the forward 4 D (Q K^T, P V);
+        # the dQ kernel 6 D (S recompute, dP, dQ); the dK/dV kernel 8 D (S recompute,
+        # dP, dV, dK). The headline value counts 4 D + 10 D per pair, so the
+        # backward's duplicated S and dP earn nothing there.
+        per_pair = {"fwd": 4.0, "bwd_dq": 6.0, "bwd_dkdv": 8.0}
+        names = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
+        ms = {k: sum(hip.elapsed_ms(a, b) for a, b in ev[k]) / args.steps for k in kinds}
+        for k in kinds:
+            kern[f"{k}_ms_per_step"] = ms[k]
+            kern[f"{k}_tflops"] = per_pair[k] * w.D * sum(pairs) / (ms[k] * 1e-3) / 1e12
+        kern["other_ms_per_step"] = ms_step - sum(ms.values())
+        dom = max(kinds, key=lambda k: ms[k])
+        flop_launch = per_pair[dom] * w.D * sum(pairs) / w.n_layer
+        avg_ms = ms[dom] / w.n_layer
         achieved = flop_launch / (avg_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+        roofline = {"bound": "mfma", "kernel": names[dom], "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                    "avg_launch_ms": avg_ms, "algorithmic_flop_per_launch": flop_launch}
-        for a, b in ev_f + ev_b:
-            hip.destroy(a)
-            hip.destroy(b)
-    else:
-        roofline = None
+                    "avg_launch_ms": avg_ms, "algorithmic_flop_per_launch": flop_launch,
+                    "flop_per_visible_pair": f"{per_pair[dom]:g} D"}
+        for k in kinds:
+            for a, b in ev[k]:
+                hip.destroy(a)
+                hip.destroy(b)
 
     cpu = None
     if args.cpu_seconds > 0:

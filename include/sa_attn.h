@@ -57,7 +57,7 @@ typedef enum {
   SA_OK = 0,
   SA_ERR_NULL = 1,        /* a required pointer is NULL */
   SA_ERR_SHAPE = 2,       /* a size <= 0, Hq % Hkv != 0, window < -1, a non-finite scale or eps,
-                             eps < 0, or T*Hq*128*4 >= 2^31 (per-batch 32-bit addressing) */
+                             eps < 0, or T*Hq*128*2 >= 2^31 (per-batch 32-bit addressing) */
   SA_ERR_UNSUPPORTED = 3, /* head_dim not in {64, 128} */
   SA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   SA_ERR_WORKSPACE = 5,   /* backward workspace NULL or smaller than sa_attn_bwd_workspace_bytes() */
@@ -108,13 +108,16 @@ size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
  *     dq_hat_i = scale sum_j dS_ij k_hat_j,  dk_hat_j = scale sum_{h in group} sum_i dS_ij q_hat_i,
  *     dv_j = sum_{h in group} sum_i P_ij dout_i,
  *   then the RMS-norm backward dx = r (dx_hat - x_hat <dx_hat, x_hat> / D).
- *   The GQA sums over the query heads of a group happen inside the kernel.
+ *   Two kernels, no atomics: a dQ kernel per query block (it also writes the
+ *   normed q rows and Delta into the workspace) and a dK/dV kernel per key
+ *   block; the GQA sums over the query heads of a group happen inside the
+ *   dK/dV kernel.
  *   q, k, v, o, lse, dout : inputs (o and lse as written by sa_attn_fwd).
  *   dq, dk, dv            : bf16 outputs, fully overwritten.
  *   workspace             : device buffer of at least
  *                           sa_attn_bwd_workspace_bytes(B,T,Hq,Hkv,head_dim)
- *                           bytes (an fp32 dQ accumulator, the fp32 Delta rows
- *                           and the bf16 normed q rows), 256-byte aligned;
+ *                           bytes (the bf16 normed q rows and the fp32 Delta
+ *                           rows), 256-byte aligned;
  *                           contents on entry are ignored and on return
  *                           unspecified. Two calls that overlap in time must
  *                           use different workspaces.
@@ -125,16 +128,17 @@ sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       int B, int T, int Hq, int Hkv, int head_dim, int window,
                       float softmax_scale, int qk_norm, float eps, void* stream);
 
-/* Main kernels that sa_set_timing_events can bracket. */
-enum { SA_KERNEL_FWD = 0, SA_KERNEL_BWD_MAIN = 1 };
+/* Kernels that sa_set_timing_events can bracket. */
+enum { SA_KERNEL_FWD = 0, SA_KERNEL_BWD_DQ = 1, SA_KERNEL_BWD_DKDV = 2 };
 
 /*
  * sa_set_timing_events - benchmarking hook (not part of the computation).
  *   While set, every later sa_attn_fwd (kernel = SA_KERNEL_FWD) or
- *   sa_attn_bwd (kernel = SA_KERNEL_BWD_MAIN, its dK/dV/dQ kernel) call made
- *   FROM THE CALLING HOST THREAD records `start` on its stream right before
- *   that main kernel and `stop` right after it, so hipEventElapsedTime(start,
- *   stop) is the kernel's own duration. start/stop are hipEvent_t handles
+ *   sa_attn_bwd (kernel = SA_KERNEL_BWD_DQ for its dQ kernel,
+ *   SA_KERNEL_BWD_DKDV for its dK/dV kernel) call made FROM THE CALLING HOST
+ *   THREAD records `start` on its stream right before that kernel and `stop`
+ *   right after it, so hipEventElapsedTime(start, stop) is the kernel's own
+ *   duration. start/stop are hipEvent_t handles
  *   passed as void*, created and owned by the caller; pass NULL, NULL to clear.
  *   Returns SA_ERR_SHAPE for an unknown kernel id, SA_ERR_NULL if exactly one
  *   of start/stop is NULL.

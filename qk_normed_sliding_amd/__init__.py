@@ -27,7 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libsa_attn.so")
 SA_OK = 0
 ABI_VERSION = 1
 SA_KERNEL_FWD = 0
-SA_KERNEL_BWD_MAIN = 1
+SA_KERNEL_BWD_DQ = 1
+SA_KERNEL_BWD_DKDV = 2
 
 
 class SAError(RuntimeError):

@@ -17,7 +17,7 @@ constexpr int kAbiVersion = 1;
 
 // Benchmarking hook: events recorded around the main kernel of later calls
 // made from this host thread (see sa_set_timing_events).
-thread_local sa::TimingEvents tl_events[2];
+thread_local sa::TimingEvents tl_events[3];
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -35,9 +35,8 @@ sa_status check_shape(int B, int T, int Hq, int Hkv, int head_dim, int window, f
   const double elems = (double)B * T * (double)Hq * 128.0;
   if (elems > 9.0e18) return SA_ERR_SHAPE;
   if ((double)B * Hq * ((T + 127) / 128) > 2.0e9) return SA_ERR_SHAPE;
-  // one batch's rows of q (or k, v, and the fp32 dQ accumulator) are addressed
-  // with 32-bit byte offsets
-  if ((double)T * Hq * 128.0 * 4.0 >= 2147483648.0) return SA_ERR_SHAPE;
+  // one batch's rows of q (or k, v) are addressed with 32-bit byte offsets
+  if ((double)T * Hq * 128.0 * 2.0 >= 2147483648.0) return SA_ERR_SHAPE;
   if (!valid_dim(head_dim)) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
@@ -116,8 +115,8 @@ SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* 
 SA_API size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
   if (check_shape(B, T, Hq, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
   const size_t rows = (size_t)B * T * Hq;
-  // fp32 dQ accumulator, fp32 Delta, bf16 normed q rows
-  return round256(rows * head_dim * sizeof(float)) + round256(rows * sizeof(float)) + round256(rows * head_dim * 2);
+  // bf16 normed q rows, fp32 Delta
+  return round256(rows * head_dim * 2) + round256(rows * sizeof(float));
 }
 
 SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -145,9 +144,8 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
   p.dk = dk;
   p.dv = dv;
   const size_t rows = (size_t)B * T * Hq;
-  p.dq_acc = (float*)workspace;
-  p.delta = (float*)((char*)workspace + round256(rows * head_dim * sizeof(float)));
-  p.qhat = qk_norm ? (void*)((char*)p.delta + round256(rows * sizeof(float))) : (void*)q;
+  p.qhat = qk_norm ? workspace : (void*)q;
+  p.delta = (float*)((char*)workspace + round256(rows * head_dim * 2));
   p.B = B;
   p.T = T;
   p.Hq = Hq;
@@ -157,14 +155,18 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
   p.scale = softmax_scale;
   p.c1 = softmax_scale * 1.4426950408889634f;
   p.eps = eps;
+  const int hpw = (p.G % 2 == 0) ? 2 : 1;
+  p.nsub = p.G / hpw;
+  p.nqb = (T + 127) / 128;
   p.nkb = (T + 127) / 128;
-  return sa::launch_bwd(p, head_dim, qk_norm != 0, (hipStream_t)stream, tl_events[SA_KERNEL_BWD_MAIN]) == hipSuccess
+  return sa::launch_bwd(p, head_dim, hpw, qk_norm != 0, (hipStream_t)stream, tl_events[SA_KERNEL_BWD_DQ],
+                        tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess
              ? SA_OK
              : SA_ERR_HIP;
 }
 
 SA_API sa_status sa_set_timing_events(int kernel, void* start, void* stop) {
-  if (kernel != SA_KERNEL_FWD && kernel != SA_KERNEL_BWD_MAIN) return SA_ERR_SHAPE;
+  if (kernel != SA_KERNEL_FWD && kernel != SA_KERNEL_BWD_DQ && kernel != SA_KERNEL_BWD_DKDV) return SA_ERR_SHAPE;
   if ((start == nullptr) != (stop == nullptr)) return SA_ERR_NULL;
   tl_events[kernel].start = (hipEvent_t)start;
   tl_events[kernel].stop = (hipEvent_t)stop;

@@ -31,15 +31,16 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;  // fp32 [B, T, Hq, D]: sum_j dS_ij k_hat_j, before the softmax scale
-  float* delta;   // fp32 [B, Hq, T]
-  void* qhat;     // bf16 [B, T, Hq, D]: normed q rows (written by the pre-pass), or q itself without the norm
+  float* delta;   // fp32 [B, Hq, T], written by the dQ kernel
+  void* qhat;     // bf16 [B, T, Hq, D]: normed q rows written by the dQ kernel (q itself without the norm)
   int B, T, Hq, Hkv, G;
   int window;
   float scale;
   float c1;       // scale * log2(e)
   float eps;
-  int nkb;        // number of key blocks
+  int nqb;        // number of 128-row query blocks (dQ kernel)
+  int nsub;       // dQ workgroups per (batch, KV head, query block)
+  int nkb;        // number of 128-key blocks (dK/dV kernel)
 };
 
 struct NormParams {
@@ -59,7 +60,8 @@ struct TimingEvents {
 // Launchers return the first HIP error seen (hipGetLastError() after the launches).
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, bool fixed_max,
                       hipStream_t stream, const TimingEvents& ev);
-hipError_t launch_bwd(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream, const TimingEvents& ev);
+hipError_t launch_bwd(const BwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, hipStream_t stream,
+                      const TimingEvents& dq_ev, const TimingEvents& kv_ev);
 hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace sa

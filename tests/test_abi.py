@@ -104,9 +104,19 @@ def test_workspace_size(sa):
     B, T, Hq, Hkv, D = 16, 2048, 6, 3, 128
     rows = B * T * Hq
     r256 = lambda x: (x + 255) // 256 * 256
-    assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D) == r256(rows * D * 4) + r256(rows * 4) + r256(rows * D * 2)
+    assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D) == r256(rows * D * 2) + r256(rows * 4)
     assert lib.sa_attn_bwd_workspace_bytes(B, T, 5, Hkv, D) == 0
     assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, 80) == 0
+
+
+def test_timing_hook_validation(sa):
+    lib = sa.library()
+    P = ctypes.c_void_p
+    assert lib.sa_set_timing_events(3, None, None) == SA_ERR_SHAPE
+    assert lib.sa_set_timing_events(-1, None, None) == SA_ERR_SHAPE
+    assert lib.sa_set_timing_events(0, P(16), None) == SA_ERR_NULL
+    for k in range(3):
+        assert lib.sa_set_timing_events(k, None, None) == SA_OK
 
 
 def test_qknorm_validation_paths(sa):
