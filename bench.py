@@ -153,10 +153,12 @@ def main():
             o=torch.empty_like(q), lse=torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev),
             dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v)))
     ws = torch.empty(sa.sa_attn_bwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(sa.sa_attn_fwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def fwd(L):
-        sa.sa_attn_fwd(L["q"], L["k"], L["v"], window=L["W"], softmax_scale=w.scale, eps=w.eps, o=L["o"], lse=L["lse"])
+        sa.sa_attn_fwd(L["q"], L["k"], L["v"], window=L["W"], softmax_scale=w.scale, eps=w.eps, o=L["o"], lse=L["lse"],
+                       workspace=ws_f)
 
     def bwd(L):
         sa.sa_attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=L["W"], softmax_scale=w.scale,

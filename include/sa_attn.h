@@ -60,7 +60,7 @@ typedef enum {
                              eps < 0, or T*Hq*128*2 >= 2^31 (per-batch 32-bit addressing) */
   SA_ERR_UNSUPPORTED = 3, /* head_dim not in {64, 128} */
   SA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
-  SA_ERR_WORKSPACE = 5,   /* backward workspace NULL or smaller than sa_attn_bwd_workspace_bytes() */
+  SA_ERR_WORKSPACE = 5,   /* workspace NULL, not 256-byte aligned, or smaller than the *_workspace_bytes() size */
   SA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
 } sa_status;
 
@@ -91,13 +91,20 @@ sa_status sa_qknorm(const void* x, void* y, float* rstd, int64_t rows, int head_
  *     lse_i = log sum_{j in band} exp(S_ij).
  *   q, k, v : inputs (layouts above).  o : bf16 output [B,T,Hq,D].
  *   lse     : fp32 output [B,Hq,T]; required (the backward needs it).
+ *   workspace: device buffer of at least sa_attn_fwd_workspace_bytes(...)
+ *            bytes, 256-byte aligned; it receives the normed k rows and the
+ *            v rows transposed per KV head (keys padded to a multiple of 64).
+ *            May be NULL when qk_norm == 0. Contents on entry are ignored, on return
+ *            unspecified; overlapping calls need different workspaces.
  *   Tiles of the band outside every query's window are never loaded.
  */
+size_t sa_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
 sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes,
                       int B, int T, int Hq, int Hkv, int head_dim, int window,
                       float softmax_scale, int qk_norm, float eps, void* stream);
 
-/* Bytes of device workspace sa_attn_bwd needs for these sizes (0 if a size is invalid). */
+/* Bytes of device workspace sa_attn_fwd / sa_attn_bwd need for these sizes (0 if a size is invalid). */
 size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
 
 /*

@@ -7,7 +7,8 @@ this package fails if the library has not been built.
 
 Entry points (same names as the C ABI):
   sa_qknorm(x, y=None, rstd=None, eps=1e-6)
-  sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None)
+  sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim)
+  sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None, workspace=None)
   sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim)
   sa_attn_bwd(q, k, v, o, lse, dout, window=-1, ..., dq=None, dk=None, dv=None, workspace=None)
 Helpers: attention(...) (autograd), sssl_windows(n_layer, T, pattern).
@@ -25,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa_attn.so")
 
 SA_OK = 0
-ABI_VERSION = 1
+ABI_VERSION = 2
 SA_KERNEL_FWD = 0
 SA_KERNEL_BWD_DQ = 1
 SA_KERNEL_BWD_DKDV = 2
@@ -52,8 +53,10 @@ def _load():
     lib.sa_status_string.argtypes = [i32]
     lib.sa_qknorm.restype = i32
     lib.sa_qknorm.argtypes = [vp, vp, vp, i64, i32, f32, vp]
+    lib.sa_attn_fwd_workspace_bytes.restype = sz
+    lib.sa_attn_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.sa_attn_fwd.restype = i32
-    lib.sa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, f32, vp]
+    lib.sa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, f32, i32, f32, vp]
     lib.sa_attn_bwd_workspace_bytes.restype = sz
     lib.sa_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.sa_attn_bwd.restype = i32
@@ -135,8 +138,12 @@ def sa_qknorm(x, y=None, rstd=None, eps=1e-6, want_rstd=True, stream=None):
     return y, rstd
 
 
+def sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim):
+    return int(_lib.sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim))
+
+
 def sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None,
-                stream=None):
+                workspace=None, stream=None):
     """Forward of one layer. q [B,T,Hq,D], k/v [B,T,Hkv,D] bf16. Returns (o, lse)."""
     B, T, Hq, Hkv, D = _dims(q, k)
     _need(q, "q", torch.bfloat16)
@@ -148,8 +155,13 @@ def sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, 
         lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     _need(o, "o", torch.bfloat16, q.shape)
     _need(lse, "lse", torch.float32, (B, Hq, T))
+    if workspace is None and qk_norm:
+        workspace = torch.empty(sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
     _check("sa_attn_fwd", _lib.sa_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, Hq, Hkv, D, int(window),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), B, T, Hq, Hkv, D, int(window),
         _scale(softmax_scale, D), int(bool(qk_norm)), float(eps), _stream(q.device, stream)))
     return o, lse
 

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 // Benchmarking hook: events recorded around the main kernel of later calls
 // made from this host thread (see sa_set_timing_events).
@@ -80,12 +80,22 @@ SA_API sa_status sa_qknorm(const void* x, void* y, float* rstd, int64_t rows, in
   return sa::launch_qknorm(p, head_dim, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
-SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int T,
-                             int Hq, int Hkv, int head_dim, int window, float softmax_scale, int qk_norm,
-                             float eps, void* stream) {
+SA_API size_t sa_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
+  if (check_shape(B, T, Hq, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
+  const size_t Tp = ((size_t)T + 63) / 64 * 64;
+  // bf16 normed k rows [B,T,Hkv,D], then bf16 transposed v rows [B,Hkv,D,Tp]
+  return round256((size_t)B * T * Hkv * head_dim * 2) + round256((size_t)B * Hkv * head_dim * Tp * 2);
+}
+
+SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                             float softmax_scale, int qk_norm, float eps, void* stream) {
   const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
   if (st != SA_OK) return st;
   if (!q || !k || !v || !o || !lse) return SA_ERR_NULL;
+  if (qk_norm && (workspace == nullptr || workspace_bytes < sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim) ||
+                  ((uintptr_t)workspace & 255u) != 0))
+    return SA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return SA_ERR_ALIGN;
 
   sa::FwdParams p{};
@@ -106,8 +116,18 @@ SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* 
   const int hpw = (p.G % 2 == 0) ? 2 : 1;
   p.nsub = p.G / hpw;
   p.nqb = (T + 127) / 128;
-  return sa::launch_fwd(p, head_dim, hpw, qk_norm != 0, fixed, (hipStream_t)stream, tl_events[SA_KERNEL_FWD]) ==
-                 hipSuccess
+  p.khat = k;
+  const hipStream_t s = (hipStream_t)stream;
+  if (hpw == 2 && fixed) {
+    // prologue: normed k rows and transposed v rows, so the attention kernel copies tiles
+    p.Tp = (T + 63) / 64 * 64;
+    p.khat = workspace;
+    p.vt = (char*)workspace + round256((size_t)B * T * Hkv * head_dim * 2);
+    sa::KvPrepParams kp{k, v, (void*)p.khat, (void*)p.vt, B, T, Hkv, p.Tp, eps};
+    if (sa::launch_kv_prep(kp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+    return sa::launch_fwd_pp(p, head_dim, s, tl_events[SA_KERNEL_FWD]) == hipSuccess ? SA_OK : SA_ERR_HIP;
+  }
+  return sa::launch_fwd(p, head_dim, hpw, qk_norm != 0, fixed, s, tl_events[SA_KERNEL_FWD]) == hipSuccess
              ? SA_OK
              : SA_ERR_HIP;
 }

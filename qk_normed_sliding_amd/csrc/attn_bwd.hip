@@ -35,21 +35,6 @@
 
 namespace sa {
 
-// Swizzle of 16-byte chunks in LDS rows without padding: chunk j of row r is
-// stored at chunk j ^ f(r). For rows of 16 chunks f(r) puts the low two row
-// bits on the high chunk bits and vice versa; for rows of 8 chunks it uses
-// row bits 1..3. Both make 16 consecutive rows read at one logical chunk, and
-// 4 consecutive rows read at 4 consecutive chunks, land on distinct banks.
-template <int CH>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-template <int CH>
-__device__ __forceinline__ int swz_off(int r, int col) {  // element offset of (row, col)
-  return r * CH * 8 + ((((col >> 3) ^ swz<CH>(r)) & (CH - 1)) << 3) + (col & 7);
-}
-
 // ---------------------------------------------------------------- dQ kernel
 template <int D, int HPW, int BN, bool NORM>
 __global__ void __launch_bounds__(HPW * 4 * 64) attn_bwd_dq_kernel(BwdParams p) {

@@ -1,0 +1,69 @@
+// Prologue of the two-warp-group forward: per call, every key row is RMS
+// normed once ([post] QK-norm passage; [guide] 8.2.1) and written as k_hat in
+// the layout of k, and the value rows of each (batch, KV head) are written
+// transposed, as v_t[b][g][d][t] with the key axis padded with zeros to a
+// multiple of 64. After it, the attention kernel's key and value tiles are
+// plain copies that go straight from memory into LDS, and both are read
+// there with 16-byte reads (the value operand of P.V runs along keys).
+// HBM-bound: each k and v element is read once and written once.
+#include "sa_common.h"
+#include "sa_kernels.h"
+
+namespace sa {
+
+template <int D>
+__global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepParams p) {
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;   // rows per pass of the workgroup
+  constexpr int VP = D + 8;        // LDS pitch of the staged value tile (elements)
+  __shared__ __attribute__((aligned(16))) bf16 vs[64 * VP];
+
+  const int t0 = blockIdx.x * 64;
+  const int bg = blockIdx.y;  // b * Hkv + g
+  const int b = bg / p.Hkv, g = bg % p.Hkv;
+  const int sub = threadIdx.x % CPR;
+
+  for (int r = threadIdx.x / CPR; r < 64; r += RPP) {
+    const int t = t0 + r;
+    const bool in = t < p.T;
+    const long off = (((long)b * p.T + (in ? t : 0)) * p.Hkv + g) * D + 8 * sub;
+    u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
+    if (in) {
+      kw = ld16((const bf16*)p.k + off);
+      vw = ld16((const bf16*)p.v + off);
+    }
+    float x[8];
+    unpack8(kw, x);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    const float rs = fast_rsqrt(group_sum<CPR>(ss) * (1.f / D) + p.eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= rs;
+    if (in) st16((bf16*)p.khat + off, pack8(x));
+    *(u32x4*)(vs + r * VP + 8 * sub) = vw;  // rows past T stay zero
+  }
+  __syncthreads();
+
+  // transposed write: thread -> (d, 8-key chunk c); 128 contiguous bytes per d row
+  const unsigned short* vu = (const unsigned short*)vs;
+  const int c = threadIdx.x % 8;
+  for (int d = threadIdx.x / 8; d < D; d += 32) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)vu[(8 * c + 2 * j) * VP + d] | ((uint32_t)vu[(8 * c + 2 * j + 1) * VP + d] << 16);
+    st16((bf16*)p.vt + ((long)bg * D + d) * p.Tp + t0 + 8 * c, w);
+  }
+}
+
+hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.Tp / 64), (unsigned)(p.B * p.Hkv));
+  if (head_dim == 128)
+    hipLaunchKernelGGL((kv_prep_kernel<128>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((kv_prep_kernel<64>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -88,6 +88,36 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// Buffer resource as four dwords (base address, stride 0, size in bytes,
+// flags), uniform across the wave so that it lives in scalar registers.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l fills bytes
+// [16l, 16l+16) after lds_base (a wave-uniform LDS byte address); offsets
+// past the buffer's size read as zero. Issued from inline assembly so that
+// the compiler does not count it as a pending LDS write (it would otherwise
+// wait for it before every later LDS read and barrier): the issuing wave
+// waits for it itself (vmcnt) before the barrier that publishes the data.
+// The byte offset is voff (per lane) + soff (wave-uniform); the range check
+// against the buffer's size applies to voff alone.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");  // m0 is reserved by the compiler, which reloads it before each of its own uses
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(SA_LDS const void*)p;
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
@@ -120,6 +150,21 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 // MFMA's operand, so P and dS feed the next contraction without a shuffle.
 __device__ __forceinline__ int swap23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Swizzle of 16-byte chunks in LDS rows without padding: chunk j of row r is
+// stored at chunk j ^ f(r). For rows of 16 chunks f(r) puts the low two row
+// bits on the high chunk bits and vice versa; for rows of 8 chunks it uses
+// row bits 1..3. Both make 16 consecutive rows read at one logical chunk, and
+// 4 consecutive rows read at 4 consecutive chunks, land on distinct banks.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+template <int CH>
+__device__ __forceinline__ int swz_off(int r, int col) {  // element offset of (row, col)
+  return r * CH * 8 + ((((col >> 3) ^ swz<CH>(r)) & (CH - 1)) << 3) + (col & 7);
 }
 
 }  // namespace sa

@@ -9,7 +9,9 @@ namespace sa {
 struct FwdParams {
   const void* q;
   const void* k;
+  const void* khat;      // normed k rows [B, T, Hkv, D] (prologue kernel output)
   const void* v;
+  const void* vt;        // v transposed per (b, g): [B, Hkv, D, Tp], keys >= T zero (prologue output)
   void* o;
   float* lse;
   int B, T, Hq, Hkv, G;  // G = Hq / Hkv
@@ -19,6 +21,16 @@ struct FwdParams {
   float eps;
   int nqb;               // number of 128-row query blocks
   int nsub;              // workgroups per (batch, KV head, query block) = G / heads-per-workgroup
+  int Tp;                // T rounded up to a multiple of 64 (key axis of vt)
+};
+
+struct KvPrepParams {
+  const void* k;
+  const void* v;
+  void* khat;  // [B, T, Hkv, D]
+  void* vt;    // [B, Hkv, D, Tp]
+  int B, T, Hkv, Tp;
+  float eps;
 };
 
 struct BwdParams {
@@ -60,8 +72,11 @@ struct TimingEvents {
 // Launchers return the first HIP error seen (hipGetLastError() after the launches).
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, bool fixed_max,
                       hipStream_t stream, const TimingEvents& ev);
+// Two-warp-group forward for an even query-heads-per-KV-head ratio with bounded logits.
+hipError_t launch_fwd_pp(const FwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
 hipError_t launch_bwd(const BwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, hipStream_t stream,
                       const TimingEvents& dq_ev, const TimingEvents& kv_ev);
 hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace sa

@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("sa_qknorm", "sa_attn_fwd", "sa_attn_bwd", "sa_attn_bwd_workspace_bytes",
+    for n in ("sa_qknorm", "sa_attn_fwd", "sa_attn_fwd_workspace_bytes", "sa_attn_bwd", "sa_attn_bwd_workspace_bytes",
               "sa_status_string", "sa_abi_version"):
         assert n in names
 
@@ -55,9 +55,13 @@ def test_version_and_status_strings(sa):
     assert b"unknown" in lib.sa_status_string(99)
 
 
-def _fwd(lib, q=16, k=16, v=16, o=16, lse=16, B=1, T=8, Hq=4, Hkv=2, D=64, W=-1, scale=0.125, norm=1, eps=1e-6):
+def _fwd(lib, q=16, k=16, v=16, o=16, lse=16, ws=256, ws_bytes=None, B=1, T=8, Hq=4, Hkv=2, D=64, W=-1,
+         scale=0.125, norm=1, eps=1e-6):
     P = ctypes.c_void_p
-    return lib.sa_attn_fwd(P(q), P(k), P(v), P(o), P(lse), B, T, Hq, Hkv, D, W, scale, norm, eps, None)
+    if ws_bytes is None:
+        ws_bytes = lib.sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D)
+    return lib.sa_attn_fwd(P(q), P(k), P(v), P(o), P(lse), P(ws), ws_bytes, B, T, Hq, Hkv, D, W, scale, norm, eps,
+                           None)
 
 
 def test_forward_validation_paths(sa):
@@ -76,6 +80,9 @@ def test_forward_validation_paths(sa):
     assert _fwd(lib, q=24) == SA_ERR_ALIGN
     assert _fwd(lib, o=8) == SA_ERR_ALIGN
     assert _fwd(lib, lse=2) == SA_ERR_ALIGN
+    assert _fwd(lib, ws=0) == SA_ERR_WORKSPACE
+    assert _fwd(lib, ws_bytes=16) == SA_ERR_WORKSPACE
+    assert _fwd(lib, ws=128) == SA_ERR_WORKSPACE
 
 
 def _bwd(lib, ws=256, ws_bytes=None, B=1, T=8, Hq=4, Hkv=2, D=64, W=-1, dq=16, null_lse=False):
@@ -101,6 +108,10 @@ def test_backward_validation_paths(sa):
 
 def test_workspace_size(sa):
     lib = sa.library()
+    assert lib.sa_attn_fwd_workspace_bytes(16, 2048, 6, 3, 128) == 2 * (16 * 2048 * 3 * 128 * 2)
+    # k_hat (5 rows of 2 x 64, rounded to 256 B) + v_t (2 x 64 rows of 64 padded keys)
+    assert lib.sa_attn_fwd_workspace_bytes(1, 5, 4, 2, 64) == 1280 + 2 * 64 * 64 * 2
+    assert lib.sa_attn_fwd_workspace_bytes(1, 5, 4, 3, 64) == 0
     B, T, Hq, Hkv, D = 16, 2048, 6, 3, 128
     rows = B * T * Hq
     r256 = lambda x: (x + 255) // 256 * 256

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import (compare_backward, compare_forward, gpu_forward, gpu_fwd_bwd, log, max_abs, rel_l2,
+from gpu_helpers import (LSE_MAX_ABS, O_MAX_ABS, compare_backward, compare_forward, gpu_forward, gpu_fwd_bwd, log, max_abs, rel_l2,
                          set_cpu_threads)
 
 pytestmark = pytest.mark.gpu
@@ -118,16 +118,26 @@ def test_window_zero_returns_v_and_constant_v(sa):
 
 
 def test_gqa_equals_mha_with_repeated_kv(sa):
-    B, T, Hq, Hkv, D = 2, 333, 6, 3, 128
+    """Grouping only decides which KV head a query head reads: with every KV head
+    repeated, a grouped layer gives the ungrouped layer's results. Four and two
+    query heads per KV head run the same two-head kernel, so their forward bits
+    agree exactly; one query head per KV head runs the single-head kernel, whose
+    rounding order differs, so that pair is held to the forward tolerance."""
+    B, T, Hq, Hkv, D = 2, 333, 8, 2, 128
     q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=9)
-    kr, vr = k.repeat_interleave(2, dim=2), v.repeat_interleave(2, dim=2)
     for W in (-1, 100):
         o, lse, dq, dk, dv = gpu_fwd_bwd(sa, q, k, v, do, W, D ** -0.5)
-        om, lsem, dqm, dkm, dvm = gpu_fwd_bwd(sa, q, kr, vr, do, W, D ** -0.5)
-        assert torch.equal(o, om) and torch.equal(lse, lsem)
-        assert rel_l2(dq.cpu(), dqm.cpu()) < 1e-2
-        assert rel_l2(dk.cpu(), dkm.float().cpu().view(B, T, Hkv, 2, D).sum(3)) < 1e-2
-        assert rel_l2(dv.cpu(), dvm.float().cpu().view(B, T, Hkv, 2, D).sum(3)) < 1e-2
+        for rep, exact in ((2, True), (4, False)):
+            kr, vr = k.repeat_interleave(rep, dim=2), v.repeat_interleave(rep, dim=2)
+            om, lsem, dqm, dkm, dvm = gpu_fwd_bwd(sa, q, kr, vr, do, W, D ** -0.5)
+            if exact:
+                assert torch.equal(o, om) and torch.equal(lse, lsem)
+            else:
+                assert float((o.float() - om.float()).abs().max()) <= O_MAX_ABS
+                assert float((lse - lsem).abs().max()) <= LSE_MAX_ABS
+            assert rel_l2(dq.cpu(), dqm.cpu()) < 1e-2
+            assert rel_l2(dk.cpu(), dkm.float().cpu().view(B, T, Hkv, rep, D).sum(3)) < 1e-2
+            assert rel_l2(dv.cpu(), dvm.float().cpu().view(B, T, Hkv, rep, D).sum(3)) < 1e-2
 
 
 def test_window_at_least_T_minus_1_is_full_causal(sa):
