@@ -118,13 +118,14 @@ size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
  *   Two kernels, no atomics: a dQ kernel per query block (it also writes the
  *   normed q rows and Delta into the workspace) and a dK/dV kernel per key
  *   block; the GQA sums over the query heads of a group happen inside the
- *   dK/dV kernel.
+ *   dK/dV kernel. With an even number of query heads per KV head a norm
+ *   pass first writes the normed k rows into the workspace for the dQ kernel.
  *   q, k, v, o, lse, dout : inputs (o and lse as written by sa_attn_fwd).
  *   dq, dk, dv            : bf16 outputs, fully overwritten.
  *   workspace             : device buffer of at least
  *                           sa_attn_bwd_workspace_bytes(B,T,Hq,Hkv,head_dim)
- *                           bytes (the bf16 normed q rows and the fp32 Delta
- *                           rows), 256-byte aligned;
+ *                           bytes (the bf16 normed q rows, the fp32 Delta
+ *                           rows and the bf16 normed k rows), 256-byte aligned;
  *                           contents on entry are ignored and on return
  *                           unspecified. Two calls that overlap in time must
  *                           use different workspaces.

@@ -25,6 +25,7 @@ bool valid_dim(int d) { return d == 64 || d == 128; }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+
 // Validates the shape arguments shared by the forward and the backward.
 sa_status check_shape(int B, int T, int Hq, int Hkv, int head_dim, int window, float scale, float eps) {
   if (B <= 0 || T <= 0 || Hq <= 0 || Hkv <= 0) return SA_ERR_SHAPE;
@@ -83,7 +84,7 @@ SA_API sa_status sa_qknorm(const void* x, void* y, float* rstd, int64_t rows, in
 SA_API size_t sa_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
   if (check_shape(B, T, Hq, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
   const size_t Tp = ((size_t)T + 63) / 64 * 64;
-  // bf16 normed k rows [B,T,Hkv,D], then bf16 transposed v rows [B,Hkv,D,Tp]
+  // bf16 normed k rows [B,T,Hkv,D], bf16 transposed v rows [B,Hkv,D,Tp]
   return round256((size_t)B * T * Hkv * head_dim * 2) + round256((size_t)B * Hkv * head_dim * Tp * 2);
 }
 
@@ -135,8 +136,9 @@ SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* 
 SA_API size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
   if (check_shape(B, T, Hq, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
   const size_t rows = (size_t)B * T * Hq;
-  // bf16 normed q rows, fp32 Delta
-  return round256(rows * head_dim * 2) + round256(rows * sizeof(float));
+  // bf16 normed q rows, fp32 Delta, bf16 normed k rows
+  return round256(rows * head_dim * 2) + round256(rows * sizeof(float)) +
+         round256((size_t)B * T * Hkv * head_dim * 2);
 }
 
 SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -179,7 +181,22 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
   p.nsub = p.G / hpw;
   p.nqb = (T + 127) / 128;
   p.nkb = (T + 127) / 128;
-  return sa::launch_bwd(p, head_dim, hpw, qk_norm != 0, (hipStream_t)stream, tl_events[SA_KERNEL_BWD_DQ],
+  const hipStream_t s = (hipStream_t)stream;
+  p.khat = k;
+  if (hpw == 2) {
+    // two-warp-group dQ kernel over k_hat tiles copied straight into LDS
+    if (qk_norm) {
+      void* khat = (char*)workspace + round256(rows * head_dim * 2) + round256(rows * sizeof(float));
+      sa::NormParams np{k, khat, nullptr, (int64_t)B * T * Hkv, eps};
+      if (sa::launch_qknorm(np, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+      p.khat = khat;
+    }
+    if (sa::launch_bwd_dq_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DQ]) != hipSuccess) return SA_ERR_HIP;
+    return sa::launch_bwd_dkdv(p, head_dim, qk_norm != 0, s, tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess
+               ? SA_OK
+               : SA_ERR_HIP;
+  }
+  return sa::launch_bwd(p, head_dim, hpw, qk_norm != 0, s, tl_events[SA_KERNEL_BWD_DQ],
                         tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess
              ? SA_OK
              : SA_ERR_HIP;

@@ -550,20 +550,10 @@ __global__ void __launch_bounds__(256, 1) attn_bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
-template <int D, int HPW>
-static hipError_t launch_bwd_d(const BwdParams& p, bool qk_norm, hipStream_t stream, const TimingEvents& dq_ev,
-                               const TimingEvents& kv_ev) {
-  constexpr int BN = 64;
+template <int D>
+static hipError_t launch_dkdv_d(const BwdParams& p, bool qk_norm, hipStream_t stream, const TimingEvents& kv_ev) {
   constexpr int BQ = 64;
   hipError_t e;
-  const dim3 qgrid((unsigned)(p.nqb * p.B * p.Hkv * p.nsub));
-  if (dq_ev.start != nullptr && (e = hipEventRecord(dq_ev.start, stream)) != hipSuccess) return e;
-  if (qk_norm)
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, HPW, BN, true>), qgrid, dim3(HPW * 256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, HPW, BN, false>), qgrid, dim3(HPW * 256), 0, stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (dq_ev.stop != nullptr && (e = hipEventRecord(dq_ev.stop, stream)) != hipSuccess) return e;
   const dim3 kgrid((unsigned)(p.nkb * p.B * p.Hkv));
   if (kv_ev.start != nullptr && (e = hipEventRecord(kv_ev.start, stream)) != hipSuccess) return e;
   if (qk_norm)
@@ -573,6 +563,27 @@ static hipError_t launch_bwd_d(const BwdParams& p, bool qk_norm, hipStream_t str
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (kv_ev.stop != nullptr && (e = hipEventRecord(kv_ev.stop, stream)) != hipSuccess) return e;
   return hipSuccess;
+}
+
+template <int D, int HPW>
+static hipError_t launch_bwd_d(const BwdParams& p, bool qk_norm, hipStream_t stream, const TimingEvents& dq_ev,
+                               const TimingEvents& kv_ev) {
+  constexpr int BN = 64;
+  hipError_t e;
+  const dim3 qgrid((unsigned)(p.nqb * p.B * p.Hkv * p.nsub));
+  if (dq_ev.start != nullptr && (e = hipEventRecord(dq_ev.start, stream)) != hipSuccess) return e;
+  if (qk_norm)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, HPW, BN, true>), qgrid, dim3(HPW * 256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, HPW, BN, false>), qgrid, dim3(HPW * 256), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (dq_ev.stop != nullptr && (e = hipEventRecord(dq_ev.stop, stream)) != hipSuccess) return e;
+  return launch_dkdv_d<D>(p, qk_norm, stream, kv_ev);
+}
+
+hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream,
+                           const TimingEvents& kv_ev) {
+  return head_dim == 128 ? launch_dkdv_d<128>(p, qk_norm, stream, kv_ev) : launch_dkdv_d<64>(p, qk_norm, stream, kv_ev);
 }
 
 hipError_t launch_bwd(const BwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, hipStream_t stream,

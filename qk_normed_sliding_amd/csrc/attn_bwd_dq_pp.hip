@@ -1,0 +1,376 @@
+// dQ kernel of the backward for an even number of query heads per KV head,
+// organised like attn_fwd_pp.hip: two warp groups (one query head each, 32
+// query rows per wave) alternate M-phases and V-phases between workgroup
+// barriers, and the key and value tiles arrive as plain buffer-to-LDS copies
+// (k_hat from a norm prologue, v as stored). Same gradient as the dQ kernel
+// in attn_bwd.hip ([post] QK-norm and SSSL passages; [guide] 8.2.1):
+//   S = K_hat q_hat^T, dP = V dO^T        (one query row per lane)
+//   P = exp(S - LSE), dS = P (dP - Delta)  (V-phase)
+//   dq_hat^T += K_hat^T dS^T                (next M-phase; K_hat read K-major
+//                                             by the LDS transpose read)
+// A key tile is read in the M-phase of its own tile (S) and of the next one
+// (dQ), so K uses four LDS slots and V three.
+#include "sa_common.h"
+#include "sa_kernels.h"
+
+#include <type_traits>
+
+namespace sa {
+
+template <int KST, int NPAIR, int RPM>
+__device__ __forceinline__ void sched_dq_group() {
+  // NPAIR MFMAs, each followed by RPM LDS reads of an operand group further on
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+}
+
+template <int D>
+__global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
+  constexpr int NBK = 4, NBV = 3;
+  constexpr int BN = 64;
+  constexpr int BM = 128;
+  constexpr int KST = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int TILE = BN * D;
+  constexpr int KRPI = 64 / CPR;       // rows per direct-to-LDS instruction (1 KB)
+  constexpr int IPW = BN / KRPI / 4;   // instructions per loading wave, per tile
+  static_assert(KST == 2 * NDB, "operand groups of S/dP and dQ chunks have the same size");
+
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[NBK][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[NBV][TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int grp = wave >> 2;
+  const int rw = wave & 3;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int per_qb = p.B * p.Hkv * p.nsub;
+  const int bid = blockIdx.x;
+  const int qb = p.nqb - 1 - bid / per_qb;  // heavy query blocks first
+  int rem = bid % per_qb;
+  const int sub = rem % p.nsub;
+  rem /= p.nsub;
+  const int g = rem % p.Hkv;
+  const int b = rem / p.Hkv;
+  const int head = g * p.G + sub * 2 + grp;
+  const int r0 = qb * BM + rw * 32;
+  const int T = p.T;
+  const int W = p.window;
+  const uint32_t Wm = W < 0 ? 0x7fffffffu : (uint32_t)W;
+  const int qstride = p.Hq * D;
+  const int kvstride = p.Hkv * D;
+  const bool wave_active = r0 < T;
+  const int row = r0 + l32;
+  const bool norm = p.qhat != p.q;  // q_hat is written (and the norm backward applied) only with the QK-norm
+
+  // ---- prologue: q_hat and dO fragments (B operands), Delta, LSE of this lane's row
+  bf16x8 qf[KST], df[KST];
+  float r_q = 1.f, delta, lse2;
+  {
+    const long first = ((long)b * T * p.Hq + head) * D;
+    const uint32_t bytes = (uint32_t)T * qstride * 2;
+    const auto rq = make_rsrc((const bf16*)p.q + first, bytes);
+    const auto rd = make_rsrc((const bf16*)p.dout + first, bytes);
+    const auto ro = make_rsrc((const bf16*)p.o + first, bytes);
+    const uint32_t off = (uint32_t)(row * qstride + 8 * half) * 2;
+    float x[KST][8];
+    float ss = 0.f, dd = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      unpack8(bload16(rq, off + 32 * kk), x[kk]);
+      const u32x4 dw = bload16(rd, off + 32 * kk);
+      df[kk] = __builtin_bit_cast(bf16x8, dw);
+      float dv[8], ov[8];
+      unpack8(dw, dv);
+      unpack8(bload16(ro, off + 32 * kk), ov);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss += x[kk][e] * x[kk][e];
+        dd += dv[e] * ov[e];
+      }
+    }
+    delta = pair_sum(dd);
+    if (norm) r_q = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps);
+    bf16* qh = (bf16*)p.qhat + first + (long)row * qstride + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[kk][e] *= r_q;
+      const u32x4 w = pack8(x[kk]);
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+      if (norm && row < T) st16(qh + 16 * kk, w);
+    }
+    const long lrow = ((long)b * p.Hq + head) * T + row;
+    lse2 = row < T ? p.lse[lrow] * kLog2e : INFINITY;
+    if (half == 0 && row < T) p.delta[lrow] = delta;
+  }
+
+  // ---- key tiles that intersect the band of this block's rows
+  const int row_lo = qb * BM;
+  const int row_hi = min(T, row_lo + BM) - 1;
+  const int key_lo = (W < 0) ? 0 : max(0, row_lo - W);
+  const int n_lo = key_lo / BN;
+  const int ntile = row_hi / BN - n_lo + 1;
+
+  // ---- direct-to-LDS loads (same row layout for K_hat and V): instruction j
+  // of wave rw fills the 1 KB block m = 4j + rw of the tile, rows m*KRPI + lane/CPR.
+  const long kvfirst = ((long)b * T * p.Hkv + g) * D;
+  const u32x4 rk = rsrc_words((const bf16*)p.khat + kvfirst, (uint32_t)T * kvstride * 2);
+  const u32x4 rv = rsrc_words((const bf16*)p.v + kvfirst, (uint32_t)T * kvstride * 2);
+  uint32_t ldo;
+  {
+    const int r = rw * KRPI + lane / CPR;  // same swizzle as every block m = 4j + rw
+    ldo = (uint32_t)((lane / CPR) * kvstride + 8 * ((lane % CPR) ^ swz<CPR>(r))) * 2;
+  }
+  const uint32_t ks_lds = lds_addr(&Ks[0][0]);
+  const uint32_t vs_lds = lds_addr(&Vs[0][0]);
+  auto issue = [&](u32x4 rs, uint32_t slot_lds, int tau) {
+    const uint32_t toff = (uint32_t)((n_lo + tau) * BN) * kvstride * 2;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int m = 4 * j + rw;
+      dma16(rs, uniform((int)(slot_lds + m * 1024)), ldo + toff + (uint32_t)(m * KRPI * kvstride * 2), 0u);
+    }
+  };
+  auto issue_k = [&](int tau) { issue(rk, ks_lds + (uint32_t)((tau % NBK) * TILE * 2), tau); };
+  auto issue_v = [&](int tau) { issue(rv, vs_lds + (uint32_t)((tau % NBV) * TILE * 2), tau); };
+
+  // ---- LDS operand reads. Rows 32c + swap23(l32), head_dim 16kk + 8half
+  // (16-byte reads; address = (slot + base) ^ (kk << 5)), and the transpose
+  // reads of K_hat rows 32c + 16ks + 8half + tq (+4), columns 32db + 16g1 + 4qq.
+  const uint32_t ra_base = (uint32_t)(swap23(l32) * D * 2 + (((half ^ swz<CPR>(swap23(l32))) & (CPR - 1)) << 4));
+  // (For another db only chunk bits 2.. change, and the swizzle XORs them, so the
+  // address of block db is that of block 0 XOR (db << 6).)
+  uint32_t kt_base[2];
+  {
+    const int tq = (lane >> 2) & 3, g1 = (lane >> 4) & 1, qq = lane & 3;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) kt_base[hi] = (uint32_t)swz_off<CPR>(8 * half + tq + 4 * hi, 16 * g1 + 4 * qq) * 2;
+  }
+  auto lds_ld16 = [](uint32_t addr) { return *(SA_LDS const bf16x8*)(uintptr_t)addr; };
+  auto lds_tr = [](uint32_t addr) { return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4*)(uintptr_t)addr); };
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+  f32x16 s[2], dp[2];   // S and dP of the tile between its M- and V-phase
+  bf16x8 dsf[2][2];     // dS of the previous tile (B operand of the dQ MFMAs)
+
+  auto rows_load = [&](uint32_t slot, int c, bf16x8 (&a)[KST]) {
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) a[kk] = lds_ld16(((slot + ra_base) ^ (uint32_t)(kk << 5)) + c * 32 * D * 2);
+  };
+  auto dq_load = [&](uint32_t slot, int c, bf16x8 (&a)[KST]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint32_t rb = slot + (uint32_t)((32 * c + 16 * ks) * D * 2);
+        a[ks * NDB + db] = cat(lds_tr(rb + (kt_base[0] ^ (uint32_t)(db << 6))), lds_tr(rb + (kt_base[1] ^ (uint32_t)(db << 6))));
+      }
+  };
+  auto chain = [&](const bf16x8 (&a)[KST], const bf16x8 (&bv)[KST]) {
+    f32x16 acc = mfma32(a[0], bv[0], f32x16{});
+#pragma unroll
+    for (int kk = 1; kk < KST; ++kk) acc = mfma32(a[kk], bv[kk], acc);
+    return acc;
+  };
+  auto dq_mfma = [&](int c, const bf16x8 (&a)[KST]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dq[db] = mfma32(a[ks * NDB + db], dsf[c][ks], dq[db]);
+  };
+
+  // Tiles of the block that hold keys visible to some row of this wave.
+  const int ta = (W < 0 ? 0 : max(0, r0 - W) / BN) - n_lo;
+  const int tb = min(r0 + 31, row_hi) / BN - n_lo;
+
+  // M-phase of tile tau: dQ of tile tau-1, then S and dP of tile tau; the
+  // operand reads of each group are in flight behind the MFMAs of the one
+  // before (a window of KST reads).
+  enum { M_SKIP = 0, M_SD = 1, M_FULL = 2, M_DQ = 3 };
+  auto m_phase = [&](int tau, auto kind) {
+    constexpr int K = decltype(kind)::value;
+    const uint32_t Kp = ks_lds + (uint32_t)(((tau + NBK - 1) % NBK) * TILE * 2);
+    const uint32_t Kc = ks_lds + (uint32_t)((tau % NBK) * TILE * 2);
+    const uint32_t Vc = vs_lds + (uint32_t)((tau % NBV) * TILE * 2);
+    bf16x8 a0[KST], a1[KST];
+    if constexpr (K == M_DQ || K == M_FULL) {
+      dq_load(Kp, 0, a0);
+      dq_load(Kp, 1, a1);
+      dq_mfma(0, a0);
+      if constexpr (K == M_FULL) rows_load(Kc, 0, a0);
+      dq_mfma(1, a1);
+    }
+    if constexpr (K == M_SD) rows_load(Kc, 0, a0);
+    if constexpr (K == M_SD || K == M_FULL) {
+      rows_load(Kc, 1, a1);
+      s[0] = chain(a0, qf);
+      rows_load(Vc, 0, a0);
+      s[1] = chain(a1, qf);
+      rows_load(Vc, 1, a1);
+      dp[0] = chain(a0, df);
+      dp[1] = chain(a1, df);
+    }
+    // Scheduling: MFMA i consumes operand i (a dQ operand is two transpose
+    // reads, an S/dP operand one 16-byte read); the reads of operand i + LEAD
+    // follow MFMA i, so LEAD operands are in flight.
+    constexpr int LEAD = 3;
+    if constexpr (K == M_FULL) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KST - LEAD; ++i) sched_dq_group<KST, 1, 2>();
+#pragma unroll
+      for (int i = 0; i < 4 * KST; ++i) sched_dq_group<KST, 1, 1>();
+      __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
+    } else if constexpr (K == M_SD) {
+      __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * KST - LEAD; ++i) sched_dq_group<KST, 1, 1>();
+      __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
+    } else if constexpr (K == M_DQ) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LEAD, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KST - LEAD; ++i) sched_dq_group<KST, 1, 2>();
+      __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
+    }
+  };
+
+  // V-phase of tile tau: P against the forward's LSE, dS, bf16 operands for dQ.
+  // Register r of chunk c: key (n_lo+tau)*64 + 32c + 16(r>>3) + 8half + (r&7).
+  auto chunk_edge = [&](int t, int c) {  // not every (row, key) of the chunk is inside the band
+    const int kc = t * BN + 32 * c;
+    return !(kc + 31 <= r0 && (W < 0 || r0 + 31 - kc <= W));
+  };
+  auto v_phase = [&](int tau) {
+    const int t = n_lo + tau;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float ds[16];
+      if (chunk_edge(t, c)) {
+        const uint32_t rk0 = (uint32_t)(row - (t * BN + 32 * c + 8 * half));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = rk0 - (uint32_t)(16 * (r >> 3) + (r & 7)) <= Wm;
+          const float pe = ok ? fast_exp2(__builtin_fmaf(s[c][r], p.c1, -lse2)) : 0.f;
+          ds[r] = pe * (dp[c][r] - delta);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(__builtin_fmaf(s[c][r], p.c1, -lse2)) * (dp[c][r] - delta);
+      }
+      dsf[c][0] = __builtin_bit_cast(bf16x8, pack8(ds));
+      dsf[c][1] = __builtin_bit_cast(bf16x8, pack8(ds + 8));
+    }
+  };
+
+  // ---- prologue loads: K tiles 0..2 by group 1, V tiles 0..1 by group 0
+  if (grp == 1) {
+    for (int tau = 0; tau < 3 && tau < ntile; ++tau) issue_k(tau);
+  } else {
+    for (int tau = 0; tau < 2 && tau < ntile; ++tau) issue_v(tau);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // ---- phases: group 0 runs M(tau) in interval 2tau and V(tau) in 2tau+1,
+  // group 1 one interval later; every wave passes 2*ntile + 2 barriers. In
+  // its V-phase a loading group waits for the loads it issued two intervals
+  // earlier, then issues the next: group 1 the K tile 3 ahead of the tile it
+  // finished (its slot held the tile read by both groups' M-phases up to the
+  // interval before), group 0 the V tile 2 ahead.
+  auto step = [&](int tau, auto kind) {
+    constexpr int K = decltype(kind)::value;
+    if constexpr (K != M_SKIP) {
+      __builtin_amdgcn_s_setprio(1);
+      m_phase(tau, kind);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __syncthreads();
+    if (grp == 1 && tau == ntile) return;
+    if constexpr (K == M_SD || K == M_FULL) v_phase(tau);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (grp == 0) {
+      if (tau + 2 < ntile) issue_v(tau + 2);
+    } else {
+      if (tau + 3 < ntile) issue_k(tau + 3);
+    }
+    __syncthreads();
+  };
+  using skip_t = std::integral_constant<int, M_SKIP>;
+  if (grp == 1) __syncthreads();
+  const int t_first = wave_active ? ta : ntile + 1;
+  int tau = 0;
+#pragma clang loop unroll(disable)
+  for (; tau < t_first; ++tau) step(tau, skip_t{});
+  if (wave_active) {
+    step(tau++, std::integral_constant<int, M_SD>{});
+#pragma clang loop unroll(disable)
+    for (; tau <= tb; ++tau) step(tau, std::integral_constant<int, M_FULL>{});
+    step(tau++, std::integral_constant<int, M_DQ>{});
+#pragma clang loop unroll(disable)
+    for (; tau <= ntile; ++tau) step(tau, skip_t{});
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- epilogue: dq = r (dq_hat - q_hat <dq_hat, q_hat> / D), dq_hat = scale * acc.
+  // The accumulator holds head_dim 32db + 8i + 4half + j of this lane's row.
+  if (!wave_active || row >= T) return;
+  const long rowoff = ((long)b * T + row) * qstride + (long)head * D + 4 * half;
+  float qx[NDB][16];
+  float dot = 0.f;
+  if (norm) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x2 w = *(const u32x2*)((const bf16*)p.q + rowoff + 32 * db + 8 * i);
+        qx[db][4 * i + 0] = __uint_as_float(w[0] << 16) * r_q;
+        qx[db][4 * i + 1] = __uint_as_float(w[0] & 0xffff0000u) * r_q;
+        qx[db][4 * i + 2] = __uint_as_float(w[1] << 16) * r_q;
+        qx[db][4 * i + 3] = __uint_as_float(w[1] & 0xffff0000u) * r_q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dot += dq[db][4 * i + j] * qx[db][4 * i + j];
+      }
+    dot = pair_sum(dot) * p.scale * (1.f / D);
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gh = p.scale * dq[db][4 * i + j];
+        v[j] = norm ? r_q * (gh - qx[db][4 * i + j] * dot) : gh;
+      }
+      u32x2 w;
+      w[0] = pack2(v[0], v[1]);
+      w[1] = pack2(v[2], v[3]);
+      *(u32x2*)((bf16*)p.dq + rowoff + 32 * db + 8 * i) = w;
+    }
+}
+
+hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
+  const dim3 grid((unsigned)(p.nqb * p.B * p.Hkv * p.nsub));
+  if (ev.start != nullptr) {
+    const hipError_t e = hipEventRecord(ev.start, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (head_dim == 128)
+    hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<128>), grid, dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<64>), grid, dim3(512), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
+  return e;
+}
+
+}  // namespace sa

@@ -42,8 +42,11 @@ __device__ __forceinline__ void sched_pairs() {
   __builtin_amdgcn_sched_group_barrier(0x008, KST, 0);
 }
 
+// One 128-row query block of two query heads (the work of one workgroup).
+// Ks and Vt are the LDS tile slots.
 template <int D, int NB>
-__global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
+__device__ __forceinline__ void fwd_pp_block(const FwdParams& p, const int bid, bf16 (*Ks)[D * 64],
+                                             bf16 (*Vt)[D * 64]) {
   constexpr int BN = 64;              // keys per tile
   constexpr int BM = 128;             // query rows per block (per head)
   constexpr int KST = D / 16;         // MFMA k-steps over head_dim = operand registers per 32-key chunk
@@ -57,9 +60,6 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   static_assert(KIPW >= 1 && VIPW >= 1, "tile rows must split over the 4 waves of a group");
   static_assert(NB >= 3, "loads run two phases ahead of their first use");
 
-  __shared__ __attribute__((aligned(1024))) bf16 Ks[NB][TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 Vt[NB][TILE];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -70,7 +70,6 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
 
   // Heavy query blocks first (the causal triangle makes late blocks longest).
   const int per_qb = p.B * p.Hkv * p.nsub;
-  const int bid = blockIdx.x;
   const int qb = p.nqb - 1 - bid / per_qb;
   int rem = bid % per_qb;
   const int sub = rem % p.nsub;
@@ -87,28 +86,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   const bool wave_active = r0 < T;
   const int row = r0 + l32;
 
-  // ---- Q fragment: lane holds row r0 + l32, head_dim 16*kk + 8*half + 0..7, normed.
-  bf16x8 qf[KST];
-  {
-    const bf16* qbase = (const bf16*)p.q + ((long)b * T * p.Hq + head) * D;
-    const auto rq = make_rsrc(qbase, (uint32_t)T * qstride * 2);
-    const uint32_t off = (uint32_t)(row * qstride + 8 * half) * 2;
-    float x[KST][8];
-    float ss = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KST; ++kk) {
-      unpack8(bload16(rq, off + 32 * kk), x[kk]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
-    }
-    const float r = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps);
-#pragma unroll
-    for (int kk = 0; kk < KST; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[kk][e] *= r;
-      qf[kk] = __builtin_bit_cast(bf16x8, pack8(x[kk]));
-    }
-  }
+  bf16x8 qf[KST];  // q_hat rows (B operand of S), filled below
 
   // ---- key tiles that intersect the band of this block's rows
   const int row_lo = qb * BM;
@@ -278,6 +256,29 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   } else {
     for (int tau = 0; tau < NB - 1 && tau < ntile; ++tau) issue_v(tau);
   }
+  // ---- Q fragment (loaded while the first tiles are in flight): lane holds
+  // row r0 + l32, head_dim 16*kk + 8*half + 0..7, normed.
+  {
+    const bf16* qbase = (const bf16*)p.q + ((long)b * T * p.Hq + head) * D;
+    const auto rq = make_rsrc(qbase, (uint32_t)T * qstride * 2);
+    const uint32_t off = (uint32_t)(row * qstride + 8 * half) * 2;
+    float x[KST][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      unpack8(bload16(rq, off + 32 * kk), x[kk]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
+    }
+    const float r = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps);
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[kk][e] *= r;
+      qf[kk] = __builtin_bit_cast(bf16x8, pack8(x[kk]));
+    }
+  }
+
   __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed in LDS
   __syncthreads();
 
@@ -341,6 +342,13 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
       *(u32x2*)(dst + 32 * db + 8 * i) = w;
     }
   if (half == 0) p.lse[((long)b * p.Hq + head) * T + row] = (p.c2 + fast_log2(l_tot)) * kLn2;
+}
+
+template <int D, int NB>
+__global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[NB][D * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 Vt[NB][D * 64];
+  fwd_pp_block<D, NB>(p, blockIdx.x, Ks, Vt);
 }
 
 hipError_t launch_fwd_pp(const FwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {

@@ -36,6 +36,7 @@ struct KvPrepParams {
 struct BwdParams {
   const void* q;
   const void* k;
+  const void* khat;   // normed k rows [B, T, Hkv, D] (k itself without the norm)
   const void* v;
   const void* o;
   const float* lse;
@@ -76,6 +77,10 @@ hipError_t launch_fwd(const FwdParams& p, int head_dim, int heads_per_wg, bool q
 hipError_t launch_fwd_pp(const FwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
 hipError_t launch_bwd(const BwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, hipStream_t stream,
                       const TimingEvents& dq_ev, const TimingEvents& kv_ev);
+// Two-warp-group dQ kernel for an even query-heads-per-KV-head ratio (reads p.khat).
+hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream,
+                           const TimingEvents& kv_ev);
 hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream);
 
