@@ -1,0 +1,396 @@
+// dK/dV kernel of the backward with the work of a key block split between
+// two warp groups that share LDS ([post] QK-norm and SSSL passages; [guide]
+// 8.2.1; same gradients as the dK/dV kernel in attn_bwd.hip):
+//   group A (waves 0-3) keeps k_hat of its 32 keys and the dV accumulator:
+//     S = Q_hat K_hat^T -> P = exp(S - LSE) (masked to the band) -> P to LDS,
+//     dV^T += dO^T P
+//   group B (waves 4-7) keeps v of the same keys and the dK accumulator:
+//     dP = dO V^T, P from LDS -> dS = P (dP - Delta), dK^T += Q_hat^T dS
+// so each wave holds half of the per-key state the single-group kernel
+// needs, two waves share every SIMD, and the matrix cores of a SIMD see 16
+// MFMAs from each of them per 32-row query chunk. A chunk's S/P and dP
+// happen in one interval, its dV and dS/dK in the next; intervals end in a
+// workgroup barrier. q_hat and dO tiles of 64 rows (plus their LSE and
+// Delta) stream into three LDS slots as direct buffer-to-LDS copies, two
+// tiles ahead; rows are XOR-swizzled so that the 16-byte row reads (S, dP)
+// and the transpose reads (dV, dK) are bank-conflict free.
+#include "sa_common.h"
+#include "sa_kernels.h"
+
+#include <type_traits>
+
+namespace sa {
+
+// Scheduling of an operand stream: N1 operands of one 16-byte read each,
+// then N2 operands of two transpose reads each, consumed in that order by
+// one MFMA per operand. PRE other reads and the first LEAD operands are
+// issued up front; after MFMA i come the reads of operand i + LEAD, so LEAD
+// operands are in flight while the register footprint stays small.
+template <int N1, int N2, int LEAD, int PRE>
+__device__ __forceinline__ void sched_stream() {
+  static_assert(LEAD <= N1, "the lead covers one-read operands only");
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE + LEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N1 - LEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < N2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
+}
+
+template <int D>
+__global__ void __launch_bounds__(512) attn_bwd_dkdv_split_kernel(BwdParams p) {
+  constexpr int NB = 3;
+  constexpr int BQ = 64;               // query rows per tile (two 32-row chunks)
+  constexpr int BK = 128;              // keys per workgroup (32 per wave of a group)
+  constexpr int KST = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int TILE = BQ * D;
+  constexpr int RPI = 64 / CPR;        // rows per direct-to-LDS instruction (1 KB)
+  constexpr int IPW = BQ / RPI / 4;    // instructions per wave, per tile
+  static_assert(KST == 2 * NDB, "operand groups of the row and transpose MFMAs have the same size");
+
+  __shared__ __attribute__((aligned(1024))) bf16 Qs[NB][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 Os[NB][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 Xs[2][4][2 * 512];  // P of a chunk, per wave pair
+  __shared__ __attribute__((aligned(16))) float Ls[NB][BQ];           // LSE of the tile's rows
+  __shared__ __attribute__((aligned(16))) float Dl[NB][BQ];           // Delta of the tile's rows
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int grp = wave >> 2;           // 0: S, P, dV   1: dP, dS, dK
+  const int rw = wave & 3;             // 32-key slice
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int T = p.T;
+  const int W = p.window;
+  const uint32_t Wm = W < 0 ? 0x7fffffffu : (uint32_t)W;
+  const int qstride = p.Hq * D;
+  const int kvstride = p.Hkv * D;
+
+  // key blocks in ascending order: the first blocks see the most queries
+  const int bid = blockIdx.x;
+  const int kb = bid / (p.B * p.Hkv);
+  const int g = (bid / p.B) % p.Hkv;
+  const int b = bid % p.B;
+  const int kb0 = kb * BK;
+  const int kw0 = kb0 + 32 * rw;       // first key of this wave
+  const int key = kw0 + l32;
+
+  // query blocks whose rows can see at least one key of this block
+  const int q_hi = (W < 0) ? T - 1 : min(T - 1, kb0 + BK - 1 + W);
+  const int qb_lo = kb0 / BQ;
+  const int nqb = q_hi / BQ - qb_lo + 1;
+  const int nit = p.G * nqb;           // tiles: (query head of the group, query block)
+
+  // ---- tile loads: instruction j of wave rw fills block m = 4j + rw, rows m*RPI + lane/CPR
+  uint32_t ldo;
+  {
+    const int r = rw * RPI + lane / CPR;
+    ldo = (uint32_t)((lane / CPR) * qstride + 8 * ((lane % CPR) ^ swz<CPR>(r))) * 2;
+  }
+  const uint32_t qs_lds = lds_addr(&Qs[0][0]);
+  const uint32_t os_lds = lds_addr(&Os[0][0]);
+  auto issue = [&](int it) {  // group A: q_hat rows and LSE; group B: dO rows and Delta
+    const int hh = it / nqb;
+    const int row0 = (qb_lo + it % nqb) * BQ;
+    const int head = g * p.G + hh;
+    const long first = ((long)b * T * p.Hq + head) * D;
+    const u32x4 rs = rsrc_words((const bf16*)(grp == 0 ? p.qhat : p.dout) + first, (uint32_t)T * qstride * 2);
+    const uint32_t slot = (grp == 0 ? qs_lds : os_lds) + (uint32_t)((it % NB) * TILE * 2);
+    const uint32_t toff = (uint32_t)row0 * qstride * 2;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int m = 4 * j + rw;
+      dma16(rs, uniform((int)(slot + m * 1024)), ldo + toff + (uint32_t)(m * RPI * qstride * 2), 0u);
+    }
+    if (rw == 0) {
+      const float* src = (grp == 0 ? p.lse : p.delta) + ((long)b * p.Hq + head) * T;
+      const u32x4 rl = rsrc_words(src, (uint32_t)T * 4);
+      const uint32_t dst = lds_addr(grp == 0 ? &Ls[it % NB][0] : &Dl[it % NB][0]);
+      dma4(rl, uniform((int)dst), (uint32_t)(row0 + lane) * 4);
+    }
+  };
+
+  // ---- per-key fragments (B operands of S and dP): key l32, head_dim 16kk + 8half
+  bf16x8 kf[KST];  // group A: k_hat;  group B: v
+  {
+    const long first = ((long)b * T * p.Hkv + g) * D + (long)kb0 * kvstride;
+    const uint32_t bytes = (uint32_t)max(0, T - kb0) * kvstride * 2;
+    const auto rk = make_rsrc((const bf16*)(grp == 0 ? p.k : p.v) + first, bytes);
+    const uint32_t off = (uint32_t)((32 * rw + l32) * kvstride + 8 * half) * 2;
+    float x[KST][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      unpack8(bload16(rk, off + 32 * kk), x[kk]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
+    }
+    const bool norm_here = grp == 0 && p.qhat != p.q;
+    const float r = norm_here ? fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps) : 1.f;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[kk][e] *= r;
+      kf[kk] = __builtin_bit_cast(bf16x8, pack8(x[kk]));
+    }
+  }
+
+  // ---- LDS read addresses (bytes): row reads of rows 32qc + swap23(l32),
+  // head_dim 16kk + 8half: (slot + base) ^ (kk << 5); transpose reads of rows
+  // 32qc + 16ks + 8half + tq (+4), columns 32db + 16g1 + 4qq: base ^ (db << 6).
+  const uint32_t ra_base = (uint32_t)(swap23(l32) * D * 2 + (((half ^ swz<CPR>(swap23(l32))) & (CPR - 1)) << 4));
+  uint32_t tr_base[2];
+  {
+    const int tq = (lane >> 2) & 3, g1 = (lane >> 4) & 1, qq = lane & 3;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) tr_base[hi] = (uint32_t)swz_off<CPR>(8 * half + tq + 4 * hi, 16 * g1 + 4 * qq) * 2;
+  }
+  auto lds_ld16 = [](uint32_t addr) { return *(SA_LDS const bf16x8*)(uintptr_t)addr; };
+  auto lds_tr = [](uint32_t addr) { return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4*)(uintptr_t)addr); };
+  auto rows_load = [&](uint32_t slot, int qc, bf16x8 (&a)[KST]) {
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) a[kk] = lds_ld16(((slot + ra_base) ^ (uint32_t)(kk << 5)) + qc * 32 * D * 2);
+  };
+  auto tr_load = [&](uint32_t slot, int qc, bf16x8 (&a)[KST]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint32_t rb = slot + (uint32_t)((32 * qc + 16 * ks) * D * 2);
+        a[ks * NDB + db] = cat(lds_tr(rb + (tr_base[0] ^ (uint32_t)(db << 6))), lds_tr(rb + (tr_base[1] ^ (uint32_t)(db << 6))));
+      }
+  };
+
+  f32x16 acc[NDB];  // group A: dV^T, group B: dK^T (head_dim 32db + 8i + 4half + j, key l32)
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  f32x16 dp_prev;     // group B: dP of the previous chunk
+  bf16x8 pb[2];       // group A: P of the previous chunk (B operand of dV)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dp_prev[r] = 0.f;
+  pb[0] = pb[1] = bf16x8{};
+
+  // band test of chunk c = (tile it, chunk qc): register r of a lane holds
+  // query row q0 + 16(r>>3) + 8half + (r&7) and key `key`
+  auto chunk_q0 = [&](int c) { return (qb_lo + (c >> 1) % nqb) * BQ + 32 * (c & 1); };
+  auto chunk_edge = [&](int q0) {  // not every (row, key) pair of the chunk is inside the band
+    return !(q0 >= kw0 + 31 && (W < 0 || q0 + 31 - kw0 <= W)) || q0 + 31 >= T;
+  };
+  auto band_ok = [&](int q0, int r) {  // bitwise and: no branch per element
+    const int q = q0 + 16 * (r >> 3) + 8 * half + (r & 7);
+    return ((uint32_t)(q - key) <= Wm) & (q < T);
+  };
+  auto xs_addr = [&](int c, int ks) { return lds_addr(&Xs[c & 1][rw][ks * 512 + 8 * lane]); };
+
+  // ---- interval c: chunk c's S/P (A) or dP (B), chunk c-1's dV (A) or
+  // dS/dK (B). The first interval has no chunk c-1, the last no chunk c; the
+  // three kinds are separate straight-line bodies with their LDS reads issued
+  // ahead of the MFMAs that consume them.
+  enum { I_FIRST = 0, I_MID = 1, I_LAST = 2 };
+  auto interval_a = [&](int c, auto kind) {
+    constexpr int K = decltype(kind)::value;
+    constexpr bool CUR = K != I_LAST, PREV = K != I_FIRST;
+    const int cp = c - 1;
+    {
+      bf16x8 a[KST], t[KST];
+      f32x16 s;
+      if constexpr (CUR) rows_load(qs_lds + (uint32_t)(((c >> 1) % NB) * TILE * 2), c & 1, a);
+      if constexpr (PREV) tr_load(os_lds + (uint32_t)(((cp >> 1) % NB) * TILE * 2), cp & 1, t);
+      if constexpr (CUR) {
+        s = mfma32(a[0], kf[0], f32x16{});
+#pragma unroll
+        for (int kk = 1; kk < KST; ++kk) s = mfma32(a[kk], kf[kk], s);
+      }
+      if constexpr (PREV) {  // dV^T += dO^T P of chunk c-1
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(t[ks * NDB + db], pb[ks], acc[db]);
+      }
+      if constexpr (CUR) {  // P of chunk c, kept for the next dV and handed to group B
+        const int q0 = chunk_q0(c);
+        const float* lse = &Ls[(c >> 1) % NB][32 * (c & 1)];
+        float pr[16];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f32x4 l0 = *(const f32x4*)(lse + 16 * ks + 8 * half);
+          const f32x4 l1 = *(const f32x4*)(lse + 16 * ks + 8 * half + 4);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pr[8 * ks + e] = fast_exp2(__builtin_fmaf(s[8 * ks + e], p.c1, -(e < 4 ? l0[e] : l1[e - 4]) * kLog2e));
+        }
+        if (chunk_edge(q0)) {  // one branch per chunk; the mask itself is a select per element
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pr[r] = band_ok(q0, r) ? pr[r] : 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 w = pack8(pr + 8 * ks);
+          pb[ks] = __builtin_bit_cast(bf16x8, w);
+          *(SA_LDS u32x4*)(uintptr_t)xs_addr(c, ks) = w;
+        }
+      }
+      // reads: S operands first, then the dV operands behind the S MFMAs
+      if constexpr (CUR && PREV) sched_stream<KST, KST, 3, 0>();
+    }
+  };
+  auto interval_b = [&](int c, auto kind) {
+    constexpr int K = decltype(kind)::value;
+    constexpr bool CUR = K != I_LAST, PREV = K != I_FIRST;
+    const int cp = c - 1;
+    {
+      bf16x8 a[KST], t[KST];
+      f32x16 dp;
+      bf16x8 dsb[2];
+      if constexpr (PREV) {  // dS of chunk c-1 from its P (group A, previous interval)
+        const float* dl = &Dl[(cp >> 1) % NB][32 * (cp & 1)];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 w = *(SA_LDS const u32x4*)(uintptr_t)xs_addr(cp, ks);
+          float pr[8];
+          unpack8(w, pr);
+          const f32x4 d0 = *(const f32x4*)(dl + 16 * ks + 8 * half);
+          const f32x4 d1 = *(const f32x4*)(dl + 16 * ks + 8 * half + 4);
+          float ds[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ds[e] = pr[e] * (dp_prev[8 * ks + e] - (e < 4 ? d0[e] : d1[e - 4]));
+          dsb[ks] = __builtin_bit_cast(bf16x8, pack8(ds));
+        }
+      }
+      if constexpr (CUR) rows_load(os_lds + (uint32_t)(((c >> 1) % NB) * TILE * 2), c & 1, a);
+      if constexpr (PREV) tr_load(qs_lds + (uint32_t)(((cp >> 1) % NB) * TILE * 2), cp & 1, t);
+      if constexpr (CUR) {
+        dp = mfma32(a[0], kf[0], f32x16{});
+#pragma unroll
+        for (int kk = 1; kk < KST; ++kk) dp = mfma32(a[kk], kf[kk], dp);
+      }
+      if constexpr (PREV) {  // dK^T += Q_hat^T dS of chunk c-1
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(t[ks * NDB + db], dsb[ks], acc[db]);
+      }
+      if constexpr (CUR) dp_prev = dp;
+      if constexpr (CUR && PREV) sched_stream<KST, KST, 3, 6>();  // after the P and Delta reads
+    }
+  };
+
+  // ---- schedule: tile it is read in intervals 2it .. 2it+2, so tile it+3
+  // may refill its slot from interval 2it+3 on. In odd interval 2t+1 each
+  // wave waits for the loads it issued two intervals earlier (tile t+1, first
+  // read in interval 2t+2 after the barrier) and issues tile t+2.
+  for (int it = 0; it < 2 && it < nit; ++it) issue(it);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  auto after = [&](int c) {
+    if (c & 1) {
+      __builtin_amdgcn_s_waitcnt(0);
+      const int t = c >> 1;
+      if (t + 2 < nit) issue(t + 2);
+    }
+    __syncthreads();
+  };
+  const int nch = 2 * nit;
+  // the two groups run separate copies of the interval loop (same barrier
+  // count), so each keeps its accumulators in place across iterations
+  auto run = [&](auto interval) {
+    interval(0, std::integral_constant<int, I_FIRST>{});
+    after(0);
+#pragma clang loop unroll(disable)
+    for (int c = 1; c < nch; ++c) {
+      interval(c, std::integral_constant<int, I_MID>{});
+      after(c);
+    }
+    interval(nch, std::integral_constant<int, I_LAST>{});
+    after(nch);
+  };
+  if (grp == 0)
+    run(interval_a);
+  else
+    run(interval_b);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- epilogue (the accumulators hold head_dim 32db + 8i + 4half + j of key `key`)
+  if (key >= T) return;
+  const long rowoff = ((long)b * T + key) * kvstride + (long)g * D + 4 * half;
+  if (grp == 0) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w;
+        w[0] = pack2(acc[db][4 * i], acc[db][4 * i + 1]);
+        w[1] = pack2(acc[db][4 * i + 2], acc[db][4 * i + 3]);
+        *(u32x2*)((bf16*)p.dv + rowoff + 32 * db + 8 * i) = w;
+      }
+    return;
+  }
+  // dk = r (dk_hat - k_hat <dk_hat, k_hat> / D), dk_hat = scale * acc; the
+  // lane pair (l, l^32) holds the whole k row, so r comes from its squares
+  const bool norm = p.qhat != p.q;
+  float kx[NDB][16];
+  float dot = 0.f, ss = 0.f, r_k = 1.f;
+  if (norm) {
+    const bf16* kp = (const bf16*)p.k + rowoff;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x2 w = *(const u32x2*)(kp + 32 * db + 8 * i);
+        kx[db][4 * i + 0] = __uint_as_float(w[0] << 16);
+        kx[db][4 * i + 1] = __uint_as_float(w[0] & 0xffff0000u);
+        kx[db][4 * i + 2] = __uint_as_float(w[1] << 16);
+        kx[db][4 * i + 3] = __uint_as_float(w[1] & 0xffff0000u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ss += kx[db][4 * i + j] * kx[db][4 * i + j];
+          dot += acc[db][4 * i + j] * kx[db][4 * i + j];
+        }
+      }
+    r_k = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps);
+    dot = pair_sum(dot) * r_k * p.scale * (1.f / D);  // <dk_hat, k_hat> / D with k_hat = r k
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gh = p.scale * acc[db][4 * i + j];
+        v[j] = norm ? r_k * (gh - kx[db][4 * i + j] * r_k * dot) : gh;
+      }
+      u32x2 w;
+      w[0] = pack2(v[0], v[1]);
+      w[1] = pack2(v[2], v[3]);
+      *(u32x2*)((bf16*)p.dk + rowoff + 32 * db + 8 * i) = w;
+    }
+}
+
+hipError_t launch_bwd_dkdv_split(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
+  const dim3 grid((unsigned)(p.nkb * p.B * p.Hkv));
+  if (ev.start != nullptr) {
+    const hipError_t e = hipEventRecord(ev.start, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (head_dim == 128)
+    hipLaunchKernelGGL((attn_bwd_dkdv_split_kernel<128>), grid, dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_bwd_dkdv_split_kernel<64>), grid, dim3(512), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
+  return e;
+}
+
+}  // namespace sa

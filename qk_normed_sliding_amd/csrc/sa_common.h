@@ -114,6 +114,13 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_base, uint32_t vo
                : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory");  // m0 is reserved by the compiler, which reloads it before each of its own uses
 }
+// As dma16 with 4 bytes per lane: lane l fills bytes [4l, 4l+4) after lds_base.
+__device__ __forceinline__ void dma4(u32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(SA_LDS const void*)p;
 }
