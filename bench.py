@@ -19,20 +19,45 @@ object: the fp64 oracle timed on the host cores on a bounded sample of the
 same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 4]
+       python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (CPU only: turns two
+       rocprofv3 --pmc runs of this script into profiles/traffic_<workload>.json)
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
+import glob
+import hashlib
 import json
-import math
 import os
 import sys
 import time
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "qk_normed_sliding_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_PROBE_BYTES = 1 << 30  # bytes read (and written) by the copy probe: 4x the 256 MB last-level cache
+
+# The kernel behind each timed slot for an even query-to-KV head ratio with
+# QK-norm (the workloads here), and the source files its code comes from.
+KERNELS = {
+    "fwd": ("attn_fwd_pp_kernel", ("attn_fwd_pp.hip", "sa_common.h")),
+    "bwd_dq": ("attn_bwd_dq_pp_kernel", ("attn_bwd_dq_pp.hip", "sa_common.h")),
+    "bwd_dkdv": ("attn_bwd_dkdv_split_kernel", ("attn_bwd_dkdv_split.hip", "sa_common.h")),
+}
+
+
+def source_hash(files) -> str:
+    """sha256 over a kernel's source files: identifies the code that counters were taken on."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def band_pairs(T: int, W: int) -> int:
@@ -40,6 +65,98 @@ def band_pairs(T: int, W: int) -> int:
     if W < 0 or W >= T - 1:
         return T * (T + 1) // 2
     return (W + 1) * (T - W) + W * (W + 1) // 2
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
+
+
+def traffic_bytes(workload: str, kernel: str, files):
+    """HBM bytes per launch (FETCH + WRITE, scaled by the copy probe) of `kernel`
+    from the committed counter summary, or None if there is none or the
+    kernel's source has changed since the counters were taken."""
+    try:
+        with open(traffic_file(workload)) as fh:
+            rec = json.load(fh)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source") != source_hash(files):
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
+def _pmc_rows(d):
+    """Per-dispatch counter values of one rocprofv3 --pmc output directory."""
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """{kernel name: [value of `counter` per dispatch]} (values summed over a dispatch's rows)."""
+    acc = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in acc.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def summarize_pmc(fetch_dir, write_dir, workload):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernels by
+    what the same counters read for the copy probe (COPY_PROBE_BYTES in, same out),
+    and write profiles/traffic_<workload>.json."""
+    fetch = _per_dispatch(_pmc_rows(fetch_dir), "FETCH_SIZE")
+    write = _per_dispatch(_pmc_rows(write_dir), "WRITE_SIZE")
+
+    def find(table, needle):
+        hits = [k for k in table if needle in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {needle!r}, found {hits}")
+        return table[hits[0]]
+
+    probe_f = find(fetch, "neg_kernel")
+    probe_w = find(write, "neg_kernel")
+    f_scale = COPY_PROBE_BYTES / (sum(probe_f) / len(probe_f) * 1024.0)
+    w_scale = COPY_PROBE_BYTES / (sum(probe_w) / len(probe_w) * 1024.0)
+    kernels = {}
+    for slot, (name, files) in KERNELS.items():
+        vf, vw = find(fetch, f"{name}<"), find(write, f"{name}<")
+        kernels[name] = {
+            "source": source_hash(files),
+            "launches_averaged": len(vf),
+            "fetch_kib_per_launch_raw": sum(vf) / len(vf),
+            "write_kib_per_launch_raw": sum(vw) / len(vw),
+            "fetch_bytes_per_launch": sum(vf) / len(vf) * 1024.0 * f_scale,
+            "write_bytes_per_launch": sum(vw) / len(vw) * 1024.0 * w_scale,
+        }
+    rec = {
+        "workload": workload,
+        "copy_probe": {"bytes_each_way": COPY_PROBE_BYTES,
+                       "fetch_kib_raw": sum(probe_f) / len(probe_f), "write_kib_raw": sum(probe_w) / len(probe_w),
+                       "fetch_scale": f_scale, "write_scale": w_scale},
+        "kernels": kernels,
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o pmc -- python -u bench.py --steps 2 "
+            "--warmup 1 --cpu-seconds 0 --no-kernel-events --copy-probe",
+            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o pmc -- python -u bench.py --steps 2 "
+            "--warmup 1 --cpu-seconds 0 --no-kernel-events --copy-probe",
+            "python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+        ],
+    }
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(workload), "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
 
 
 def parse():
@@ -52,6 +169,12 @@ def parse():
                     help="wall-clock budget of the oracle sample (0 disables the CPU baseline)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="do not bracket the main kernels with HIP events")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB device copy (bf16 negation) three times: "
+                         "the reference that scales FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-probe` into profiles/ and exit (no GPU needed)")
     return ap.parse_args()
 
 
@@ -127,6 +250,11 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        import synth
+
+        summarize_pmc(*args.summarize_pmc, synth.WORKLOADS[args.workload].name)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
@@ -143,7 +271,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.WORKLOADS[args.workload]
-    G = w.Hq // w.Hkv
+    if (w.Hq // w.Hkv) % 2 != 0:
+        raise SystemExit("the kernel table of bench.py describes an even query-to-KV head ratio")
 
     layers = []
     for layer in range(w.n_layer):
@@ -215,7 +344,6 @@ def main():
         # dP, dV, dK). The headline value counts 4 D + 10 D per pair, so the
         # backward's duplicated S and dP earn nothing there.
         per_pair = {"fwd": 4.0, "bwd_dq": 6.0, "bwd_dkdv": 8.0}
-        names = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
         ms = {k: sum(hip.elapsed_ms(a, b) for a, b in ev[k]) / args.steps for k in kinds}
         for k in kinds:
             kern[f"{k}_ms_per_step"] = ms[k]
@@ -225,14 +353,25 @@ def main():
         flop_launch = per_pair[dom] * w.D * sum(pairs) / w.n_layer
         avg_ms = ms[dom] / w.n_layer
         achieved = flop_launch / (avg_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": names[dom], "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+        name, files = KERNELS[dom]
+        roofline = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                    "traffic": traffic_bytes(w.name, name, files),
                     "avg_launch_ms": avg_ms, "algorithmic_flop_per_launch": flop_launch,
                     "flop_per_visible_pair": f"{per_pair[dom]:g} D"}
         for k in kinds:
             for a, b in ev[k]:
                 hip.destroy(a)
                 hip.destroy(b)
+
+    if args.copy_probe:
+        # plain device copy of known size: one read and one write of COPY_PROBE_BYTES per launch
+        src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_seconds > 0:
