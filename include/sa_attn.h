@@ -153,6 +153,18 @@ enum { SA_KERNEL_FWD = 0, SA_KERNEL_BWD_DQ = 1, SA_KERNEL_BWD_DKDV = 2 };
  */
 sa_status sa_set_timing_events(int kernel, void* start, void* stop);
 
+/*
+ * sa_set_max_workgroups - testing hook (not part of the computation).
+ *   The attention kernels run persistently: one workgroup per compute unit,
+ *   each taking a fixed share of the work items (query blocks or key blocks).
+ *   While n > 0, every later sa_attn_fwd / sa_attn_bwd call made FROM THE
+ *   CALLING HOST THREAD launches at most n workgroups, so that small problems
+ *   can exercise workgroups that process many items in a row. n = 0 restores
+ *   the default (one per compute unit). Results do not depend on n.
+ *   Returns SA_ERR_SHAPE for n < 0.
+ */
+sa_status sa_set_max_workgroups(int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,8 @@ def _load():
                                 i32, i32, i32, i32, i32, i32, f32, i32, f32, vp]
     lib.sa_set_timing_events.restype = i32
     lib.sa_set_timing_events.argtypes = [i32, vp, vp]
+    lib.sa_set_max_workgroups.restype = i32
+    lib.sa_set_max_workgroups.argtypes = [i32]
     if lib.sa_abi_version() != ABI_VERSION:
         raise ImportError(f"libsa_attn ABI {lib.sa_abi_version()} != expected {ABI_VERSION}")
     return lib
@@ -201,6 +203,12 @@ def sa_set_timing_events(kernel, start_event, stop_event):
     _check("sa_set_timing_events", _lib.sa_set_timing_events(
         int(kernel), ctypes.c_void_p(start_event) if start_event else None,
         ctypes.c_void_p(stop_event) if stop_event else None))
+
+
+def sa_set_max_workgroups(n):
+    """Testing hook: launch at most n workgroups per persistent kernel from this
+    thread (0 = one per compute unit)."""
+    _check("sa_set_max_workgroups", _lib.sa_set_max_workgroups(int(n)))
 
 
 # ------------------------------------------------------------------ helpers

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "sa_attn.h"
 #include "sa_kernels.h"
 
@@ -18,12 +20,36 @@ constexpr int kAbiVersion = 2;
 // Benchmarking hook: events recorded around the main kernel of later calls
 // made from this host thread (see sa_set_timing_events).
 thread_local sa::TimingEvents tl_events[3];
+// Testing hook: cap on the workgroups of a persistent launch (0 = none).
+thread_local int tl_max_wg = 0;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 bool valid_dim(int d) { return d == 64 || d == 128; }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Compute units of the current device (cached per device). 0 on a runtime error.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Workgroups of a persistent launch: one per compute unit, or the cap set
+// with sa_set_max_workgroups. 0 on a runtime error.
+int persistent_wgs() {
+  const int n = cu_count();
+  return (tl_max_wg > 0 && tl_max_wg < n) ? tl_max_wg : n;
+}
 
 
 // Validates the shape arguments shared by the forward and the backward.
@@ -36,8 +62,9 @@ sa_status check_shape(int B, int T, int Hq, int Hkv, int head_dim, int window, f
   const double elems = (double)B * T * (double)Hq * 128.0;
   if (elems > 9.0e18) return SA_ERR_SHAPE;
   if ((double)B * Hq * ((T + 127) / 128) > 2.0e9) return SA_ERR_SHAPE;
-  // one batch's rows of q (or k, v) are addressed with 32-bit byte offsets
-  if ((double)T * Hq * 128.0 * 2.0 >= 2147483648.0) return SA_ERR_SHAPE;
+  // one batch's rows of q (or k, v) are addressed with 32-bit byte offsets,
+  // including the rows of the last 128-row block that lie past T
+  if (((double)T + 128.0) * Hq * 128.0 * 2.0 >= 2147483648.0) return SA_ERR_SHAPE;
   if (!valid_dim(head_dim)) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
@@ -122,6 +149,8 @@ SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* 
   if (hpw == 2 && fixed) {
     // prologue: normed k rows and transposed v rows, so the attention kernel copies tiles
     p.Tp = (T + 63) / 64 * 64;
+    p.nwg = persistent_wgs();
+    if (p.nwg <= 0) return SA_ERR_HIP;
     p.khat = workspace;
     p.vt = (char*)workspace + round256((size_t)B * T * Hkv * head_dim * 2);
     sa::KvPrepParams kp{k, v, (void*)p.khat, (void*)p.vt, B, T, Hkv, p.Tp, eps};
@@ -206,5 +235,11 @@ SA_API sa_status sa_set_timing_events(int kernel, void* start, void* stop) {
   if ((start == nullptr) != (stop == nullptr)) return SA_ERR_NULL;
   tl_events[kernel].start = (hipEvent_t)start;
   tl_events[kernel].stop = (hipEvent_t)stop;
+  return SA_OK;
+}
+
+SA_API sa_status sa_set_max_workgroups(int n) {
+  if (n < 0) return SA_ERR_SHAPE;
+  tl_max_wg = n;
   return SA_OK;
 }

@@ -2,17 +2,27 @@
 // the main shape class: an even number of query heads per KV head, bounded
 // logits (fixed row maximum), head_dim 64 or 128. Same computation as
 // attn_fwd.hip ([post] QK-norm and SSSL passages; [guide] 8.2.1), organised
-// for gfx950 as two warp groups that take turns on the matrix cores:
+// for gfx950 as a persistent kernel of two warp groups that take turns on
+// the matrix cores:
 //
-//   - One workgroup = one 128-row query block of 2 query heads sharing a KV
+//   - A work item is one 128-row query block of 2 query heads sharing a KV
 //     head; waves 0-3 (group 0) own the first head's rows, waves 4-7 (group
-//     1) the second's, 32 rows per wave, q_hat normed in registers.
+//     1) the second's, 32 rows per wave, q_hat normed in registers. One
+//     workgroup runs per compute unit and takes the items of a fixed
+//     heavy-first "snake" order (round k: item k*G + w, or k*G + G-1-w on
+//     odd rounds), which balances the causal triangle as well as a dynamic
+//     queue would, without a counter.
 //   - A prologue kernel has written k_hat (normed key rows) and v_t (value
 //     rows transposed to [D, keys]), so both tiles of 64 keys are plain
 //     copies, issued as buffer loads straight into LDS (no registers, no
 //     VALU) and XOR-swizzled so that the 16-byte operand reads of S = K Q^T
 //     and of O^T += V^T P^T are bank-conflict free. Three buffers per operand
-//     let the loads run two phases ahead of their use.
+//     let the loads run two phases ahead of their use. The tiles of all the
+//     workgroup's items form one stream: the loads of the next item start
+//     while the current one computes, its q rows are prefetched into
+//     registers a whole item ahead, and an item's epilogue (O / l, LSE) runs
+//     inside the next item's first vector phase, so the pipeline never
+//     drains between items.
 //   - Work per wave is split into an M-phase (the P.V MFMAs of the previous
 //     tile plus the S MFMAs of the current one, with the LDS reads of the
 //     next MFMA group in flight behind the current group) and a V-phase (the
@@ -23,32 +33,27 @@
 #include "sa_common.h"
 #include "sa_kernels.h"
 
-#include <type_traits>
-
 namespace sa {
 
-// Instruction order of an M-phase for the scheduler: the first operand
-// group's LDS reads, then NPAIR groups in which every MFMA is followed by one
-// read of the next group, then the last group's MFMAs. Each read so has a
-// whole group of MFMAs (KST x 32 cycles) to land before it is used.
-template <int KST, int NPAIR>
-__device__ __forceinline__ void sched_pairs() {
-  __builtin_amdgcn_sched_group_barrier(0x100, KST, 0);  // DS reads
+// Instruction order of an M-phase for the scheduler: LEAD operand reads,
+// then N - LEAD pairs of (MFMA, read of the operand LEAD places ahead), then
+// the last LEAD MFMAs. Each read so has LEAD MFMAs (LEAD x 32 cycles) to land
+// before it is used, while only about LEAD operands occupy registers.
+template <int N, int LEAD>
+__device__ __forceinline__ void sched_ring() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);  // DS reads
 #pragma unroll
-  for (int i = 0; i < NPAIR * KST; ++i) {
+  for (int i = 0; i < N - LEAD; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, KST, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
 }
 
-// One 128-row query block of two query heads (the work of one workgroup).
-// Ks and Vt are the LDS tile slots.
 template <int D, int NB>
-__device__ __forceinline__ void fwd_pp_block(const FwdParams& p, const int bid, bf16 (*Ks)[D * 64],
-                                             bf16 (*Vt)[D * 64]) {
+__global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   constexpr int BN = 64;              // keys per tile
-  constexpr int BM = 128;             // query rows per block (per head)
+  constexpr int BM = 128;             // query rows per item (per head)
   constexpr int KST = D / 16;         // MFMA k-steps over head_dim = operand registers per 32-key chunk
   constexpr int NDB = D / 32;         // 32-wide head_dim blocks of O
   constexpr int CPR = D / 8;          // 16-byte chunks per K row
@@ -60,50 +65,63 @@ __device__ __forceinline__ void fwd_pp_block(const FwdParams& p, const int bid, 
   static_assert(KIPW >= 1 && VIPW >= 1, "tile rows must split over the 4 waves of a group");
   static_assert(NB >= 3, "loads run two phases ahead of their first use");
 
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[NB][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 Vt[NB][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 Qn[8][32 * D];  // next item's q rows, per wave
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int grp = wave >> 2;           // warp group = query head within the pair
-  const int rw = wave & 3;             // 32-row slice of the block
+  const int rw = wave & 3;             // 32-row slice of an item
   const int half = lane >> 5;
   const int l32 = lane & 31;
-
-  // Heavy query blocks first (the causal triangle makes late blocks longest).
-  const int per_qb = p.B * p.Hkv * p.nsub;
-  const int qb = p.nqb - 1 - bid / per_qb;
-  int rem = bid % per_qb;
-  const int sub = rem % p.nsub;
-  rem /= p.nsub;
-  const int g = rem % p.Hkv;
-  const int b = rem / p.Hkv;
-  const int head = g * p.G + sub * 2 + grp;
-  const int r0 = qb * BM + rw * 32;    // first query row of this wave
   const int T = p.T;
   const int W = p.window;
   const uint32_t Wm = W < 0 ? 0x7fffffffu : (uint32_t)W;
   const int qstride = p.Hq * D;
   const int kvstride = p.Hkv * D;
-  const bool wave_active = r0 < T;
-  const int row = r0 + l32;
 
-  bf16x8 qf[KST];  // q_hat rows (B operand of S), filled below
+  // ---- the workgroup's items (heavy query blocks first, snake order)
+  const int per_qb = p.B * p.Hkv * p.nsub;
+  const int n_items = p.nqb * per_qb;
+  const int G = gridDim.x;
+  const int w = blockIdx.x;
+  auto item_index = [&](int k) { return k * G + ((k & 1) ? G - 1 - w : w); };
+  int nk = 0;
+  while (item_index(nk) < n_items) ++nk;
+  if (nk == 0) return;  // whole workgroup: no barrier has been passed
 
-  // ---- key tiles that intersect the band of this block's rows
-  const int row_lo = qb * BM;
-  const int row_hi = min(T, row_lo + BM) - 1;
-  const int key_lo = (W < 0) ? 0 : max(0, row_lo - W);
-  const int n_lo = key_lo / BN;
-  const int ntile = row_hi / BN - n_lo + 1;
+  struct Item {
+    int b, g, head, qb, n_lo, ntile;
+  };
+  auto item = [&](int k) {
+    const int i = item_index(k);
+    Item it;
+    it.qb = p.nqb - 1 - i / per_qb;
+    int rem = i % per_qb;
+    const int sub = rem % p.nsub;
+    rem /= p.nsub;
+    it.g = rem % p.Hkv;
+    it.b = rem / p.Hkv;
+    it.head = it.g * p.G + sub * 2 + grp;
+    const int row_lo = it.qb * BM;
+    const int row_hi = min(T, row_lo + BM) - 1;
+    const int key_lo = (W < 0) ? 0 : max(0, row_lo - W);
+    it.n_lo = key_lo / BN;
+    it.ntile = row_hi / BN - it.n_lo + 1;
+    return it;
+  };
+  int n_steps = 0;
+  for (int k = 0; k < nk; ++k) n_steps += item(k).ntile;
 
   // ---- direct-to-LDS loads. Instruction j of wave rw fills the 1 KB block
-  // m = 4j + rw of the tile: K rows m*KRPI + lane/CPR, V^T rows 8m + lane/8.
+  // m = 4j + rw of a tile: K rows m*KRPI + lane/CPR, V^T rows 8m + lane/8.
   // The lane's physical chunk holds logical chunk (physical ^ swizzle(row));
   // with this block order the swizzle depends on rw and the lane only, so a
   // lane's offset is one per-lane base plus a uniform part. The whole offset
   // goes in the per-lane operand: the buffer's range check (rows past T read
   // as zero) covers that operand only.
-  const u32x4 rk = rsrc_words((const bf16*)p.khat + ((long)b * T * p.Hkv + g) * D, (uint32_t)T * kvstride * 2);
-  const u32x4 rv = rsrc_words((const bf16*)p.vt + ((long)b * p.Hkv + g) * D * p.Tp, (uint32_t)D * p.Tp * 2);
   uint32_t kdo, vdo;
   {
     const int r = rw * KRPI + lane / CPR;  // row of block m = rw (same swizzle as every m = 4j + rw)
@@ -113,22 +131,46 @@ __device__ __forceinline__ void fwd_pp_block(const FwdParams& p, const int bid, 
   }
   const uint32_t ks_lds = lds_addr(&Ks[0][0]);
   const uint32_t vt_lds = lds_addr(&Vt[0][0]);
-  auto issue_k = [&](int tau) {
-    const uint32_t toff = (uint32_t)((n_lo + tau) * BN) * kvstride * 2;
-    const uint32_t base = ks_lds + (uint32_t)((tau % NB) * TILE * 2);
-#pragma unroll
-    for (int j = 0; j < KIPW; ++j) {
-      const int m = 4 * j + rw;
-      dma16(rk, uniform((int)(base + m * 1024)), kdo + toff + (uint32_t)(m * KRPI * kvstride * 2), 0u);
-    }
+
+  // Load cursor: the next tile of the stream this wave's group loads (group 1
+  // the K tiles, group 0 the V^T tiles), as (item, tile of the item).
+  struct Cursor {
+    int k, tau, ntile, n_lo;
+    u32x4 rsrc;
   };
-  auto issue_v = [&](int tau) {
-    const uint32_t toff = (uint32_t)((n_lo + tau) * BN) * 2;
-    const uint32_t base = vt_lds + (uint32_t)((tau % NB) * TILE * 2);
+  auto cursor_item = [&](Cursor& c) {
+    const Item it = item(c.k);
+    c.ntile = it.ntile;
+    c.n_lo = it.n_lo;
+    if (grp == 1)
+      c.rsrc = rsrc_words((const bf16*)p.khat + ((long)it.b * T * p.Hkv + it.g) * D, (uint32_t)T * kvstride * 2);
+    else
+      c.rsrc = rsrc_words((const bf16*)p.vt + ((long)it.b * p.Hkv + it.g) * D * p.Tp, (uint32_t)D * p.Tp * 2);
+  };
+  Cursor cur{0, 0, 0, 0, {0u, 0u, 0u, 0u}};
+  cursor_item(cur);
+  // issues the cursor's tile into LDS slot `s % NB` (s = its index in the stream) and advances
+  auto issue = [&](int s) {
+    if (grp == 1) {
+      const uint32_t toff = (uint32_t)((cur.n_lo + cur.tau) * BN) * kvstride * 2;
+      const uint32_t base = ks_lds + (uint32_t)((s % NB) * TILE * 2);
 #pragma unroll
-    for (int j = 0; j < VIPW; ++j) {
-      const int m = 4 * j + rw;
-      dma16(rv, uniform((int)(base + m * 1024)), vdo + toff + (uint32_t)(m * 8 * p.Tp * 2), 0u);
+      for (int j = 0; j < KIPW; ++j) {
+        const int m = 4 * j + rw;
+        dma16(cur.rsrc, uniform((int)(base + m * 1024)), kdo + toff + (uint32_t)(m * KRPI * kvstride * 2), 0u);
+      }
+    } else {
+      const uint32_t toff = (uint32_t)((cur.n_lo + cur.tau) * BN) * 2;
+      const uint32_t base = vt_lds + (uint32_t)((s % NB) * TILE * 2);
+#pragma unroll
+      for (int j = 0; j < VIPW; ++j) {
+        const int m = 4 * j + rw;
+        dma16(cur.rsrc, uniform((int)(base + m * 1024)), vdo + toff + (uint32_t)(m * 8 * p.Tp * 2), 0u);
+      }
+    }
+    if (++cur.tau == cur.ntile) {
+      cur.tau = 0;
+      if (++cur.k < nk) cursor_item(cur);
     }
   };
 
@@ -139,6 +181,8 @@ __device__ __forceinline__ void fwd_pp_block(const FwdParams& p, const int bid, 
   const uint32_t ka_base = (uint32_t)(swap23(l32) * D * 2 + (((half ^ swz<CPR>(swap23(l32))) & (CPR - 1)) << 4));
   // V^T: row l32 (+32db), keys 32c + 16ks + 8half -> chunk (4c + 2ks + half) ^ swz8(row)
   const uint32_t va_base = (uint32_t)(l32 * 128 + ((half ^ swz<8>(l32)) << 4));
+
+  bf16x8 qf[KST];  // q_hat rows of the current item (B operand of S)
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -148,212 +192,270 @@ __device__ __forceinline__ void fwd_pp_block(const FwdParams& p, const int bid, 
   f32x16 s[2];          // logits of the tile between its M- and V-phase
   bf16x8 pf[2][2];      // probabilities of the previous tile (P.V operand)
 
-  auto chunk_edge = [&](int t, int c) {  // not every (row, key) of the chunk is inside the band
-    const int kc = t * BN + 32 * c;
-    return !(kc + 31 <= r0 && (W < 0 || r0 + 31 - kc <= W));
+  // q rows of an item for this wave: rows r0 .. r0+31 of its head. The next
+  // item's rows are copied into the wave's own LDS region (row r, 16-byte
+  // chunk j at chunk j ^ (r mod CPR), so that the row reads below are
+  // conflict free) while the current item runs; the first item's go straight
+  // to registers. A lane holds row r0 + l32, head_dim 16*kk + 8*half + 0..7.
+  constexpr int QRPI = 64 / CPR;  // q rows per direct-to-LDS instruction (1 KB)
+  const uint32_t qn_lds = lds_addr(&Qn[wave][0]);
+  auto q_rsrc = [&](const Item& it) {
+    return rsrc_words((const bf16*)p.q + ((long)it.b * T * p.Hq + it.head) * D, (uint32_t)T * qstride * 2);
   };
-
-  // operand groups of one 32-key chunk: P.V (A = V^T rows, B = P^T) and S (A = K rows, B = Q^T)
-  auto lds_ld16 = [](uint32_t addr) { return *(SA_LDS const bf16x8*)(uintptr_t)addr; };
-  auto pv_load = [&](uint32_t vslot, int c, bf16x8 (&a)[KST]) {
+  auto q_prefetch = [&](const Item& it) {
+    const u32x4 rq = q_rsrc(it);
+    const int r0 = it.qb * BM + rw * 32;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t ad = (vslot + va_base) ^ (uint32_t)((4 * c + 2 * ks) << 4);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) a[ks * NDB + db] = lds_ld16(ad + db * 32 * 128);
+    for (int m = 0; m < 32 / QRPI; ++m) {
+      const int r = QRPI * m + lane / CPR;
+      const uint32_t off = (uint32_t)((r0 + r) * qstride + 8 * ((lane % CPR) ^ (r % CPR))) * 2;
+      dma16(rq, uniform((int)(qn_lds + m * 1024)), off, 0u);
     }
   };
-  auto pv_mfma = [&](int c, const bf16x8 (&a)[KST]) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(a[ks * NDB + db], pf[c][ks], oacc[db]);
-  };
-  auto s_load = [&](uint32_t kslot, int c, bf16x8 (&a)[KST]) {
-#pragma unroll
-    for (int kk = 0; kk < KST; ++kk) a[kk] = lds_ld16(((kslot + ka_base) ^ (uint32_t)(kk << 5)) + c * 32 * D * 2);
-  };
-  auto s_mfma = [&](int c, const bf16x8 (&a)[KST]) {
-    f32x16 acc = mfma32(a[0], qf[0], f32x16{});
-#pragma unroll
-    for (int kk = 1; kk < KST; ++kk) acc = mfma32(a[kk], qf[kk], acc);
-    s[c] = acc;
-  };
-
-  // Tiles of the block that hold keys visible to some row of this wave.
-  const int ta = (W < 0 ? 0 : max(0, r0 - W) / BN) - n_lo;
-  const int tb = min(r0 + 31, row_hi) / BN - n_lo;
-
-  // M-phase of tile tau: P.V of tile tau-1, then S of tile tau, each over
-  // both 32-key chunks without masking (the V-phase zeroes probabilities of
-  // keys outside the band). Straight-line: the reads of each operand group
-  // are issued before the MFMAs of the group ahead of it. The first tile of
-  // the wave has no P.V, the step after its last tile no S.
-  enum { M_SKIP = 0, M_S = 1, M_FULL = 2, M_PV = 3 };
-  auto m_phase = [&](int tau, auto kind) {
-    constexpr int K = decltype(kind)::value;
-    const uint32_t Vb = vt_lds + (uint32_t)(((tau + NB - 1) % NB) * TILE * 2);
-    const uint32_t Kb = ks_lds + (uint32_t)((tau % NB) * TILE * 2);
-    bf16x8 a0[KST], a1[KST];
-    if constexpr (K == M_S) {
-      s_load(Kb, 0, a0);
-      s_load(Kb, 1, a1);
-      s_mfma(0, a0);
-      s_mfma(1, a1);
-      sched_pairs<KST, 1>();
-    } else if constexpr (K == M_PV) {
-      pv_load(Vb, 0, a0);
-      pv_load(Vb, 1, a1);
-      pv_mfma(0, a0);
-      pv_mfma(1, a1);
-      sched_pairs<KST, 1>();
-    } else if constexpr (K == M_FULL) {
-      pv_load(Vb, 0, a0);
-      pv_load(Vb, 1, a1);
-      pv_mfma(0, a0);
-      s_load(Kb, 0, a0);
-      pv_mfma(1, a1);
-      s_load(Kb, 1, a1);
-      s_mfma(0, a0);
-      s_mfma(1, a1);
-      sched_pairs<KST, 3>();
-    }
-  };
-
-  // V-phase of tile tau: probabilities against the fixed row maximum c2 (the
-  // logits are bounded by |scale| * D), their bf16 operands and row sums.
-  // Subtracting the bound keeps every probability <= 1, which measurably
-  // improves the accuracy of the bf16 P.V products over leaving them
-  // unshifted, even though both stay inside the fp32 range.
-  auto v_phase = [&](int tau) {
-    const int t = n_lo + tau;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float pv[16];
-      if (chunk_edge(t, c)) {  // crosses the diagonal or the window start, or lies outside the band
-        const uint32_t rk0 = (uint32_t)(row - (t * BN + 32 * c + 8 * half));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool ok = rk0 - (uint32_t)(16 * (r >> 3) + (r & 7)) <= Wm;
-          pv[r] = ok ? fast_exp2(__builtin_fmaf(s[c][r], p.c1, -p.c2)) : 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(s[c][r], p.c1, -p.c2));
-      }
-      pf[c][0] = __builtin_bit_cast(bf16x8, pack8(pv));
-      pf[c][1] = __builtin_bit_cast(bf16x8, pack8(pv + 8));
-      float part[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) part[k] = (pv[4 * k] + pv[4 * k + 1]) + (pv[4 * k + 2] + pv[4 * k + 3]);
-      l_run += (part[0] + part[1]) + (part[2] + part[3]);
-    }
-  };
-
-  // ---- prologue loads: K tiles 0..NB-1 by group 1, V tiles 0..NB-2 by group 0
-  if (grp == 1) {
-    for (int tau = 0; tau < NB && tau < ntile; ++tau) issue_k(tau);
-  } else {
-    for (int tau = 0; tau < NB - 1 && tau < ntile; ++tau) issue_v(tau);
-  }
-  // ---- Q fragment (loaded while the first tiles are in flight): lane holds
-  // row r0 + l32, head_dim 16*kk + 8*half + 0..7, normed.
-  {
-    const bf16* qbase = (const bf16*)p.q + ((long)b * T * p.Hq + head) * D;
-    const auto rq = make_rsrc(qbase, (uint32_t)T * qstride * 2);
-    const uint32_t off = (uint32_t)(row * qstride + 8 * half) * 2;
-    float x[KST][8];
+  auto q_norm = [&](const u32x4 (&x)[KST]) {
     float ss = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
-      unpack8(bload16(rq, off + 32 * kk), x[kk]);
+      float f[8];
+      unpack8(x[kk], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
     }
-    const float r = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps);
+    // q_hat carries the factor c1 = scale * log2(e), so S comes out of the
+    // MFMAs already in the base-2 logit domain
+    const float r = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps) * p.c1;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
+      float f[8];
+      unpack8(x[kk], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[kk][e] *= r;
-      qf[kk] = __builtin_bit_cast(bf16x8, pack8(x[kk]));
+      for (int e = 0; e < 8; ++e) f[e] *= r;
+      qf[kk] = __builtin_bit_cast(bf16x8, pack8(f));
     }
-  }
+  };
+  auto q_from_lds = [&]() {
+    u32x4 x[KST];
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      x[kk] = *(SA_LDS const u32x4*)(uintptr_t)(qn_lds + (uint32_t)(l32 * D * 2 + (((2 * kk + half) ^ (l32 % CPR)) << 4)));
+    q_norm(x);
+  };
 
+  // The operands of an M-phase form one stream of 16-byte LDS reads, each
+  // consumed by one MFMA: the P.V operands of tile st-1 (chunk c, k-step ks,
+  // head_dim block db: A = V^T rows, B = P^T) and then the S operands of
+  // tile st (chunk c, k-step kk: A = K rows, B = Q^T). S needs no mask here:
+  // the V-phase zeroes probabilities of keys outside the band.
+  constexpr int NPV = 2 * KST;        // P.V operands of a tile (2 chunks)
+  constexpr int LEAD = 6;             // operand reads in flight ahead of the MFMAs
+  auto lds_ld16 = [](uint32_t addr) { return *(SA_LDS const bf16x8*)(uintptr_t)addr; };
+  auto pv_read = [&](uint32_t vslot, int i) {  // i = (c * 2 + ks) * NDB + db
+    const int db = i % NDB, ks = (i / NDB) & 1, c = i / (2 * NDB);
+    return lds_ld16(((vslot + va_base) ^ (uint32_t)((4 * c + 2 * ks) << 4)) + db * 32 * 128);
+  };
+  auto pv_op = [&](int i, bf16x8 a) {
+    const int db = i % NDB, ks = (i / NDB) & 1, c = i / (2 * NDB);
+    oacc[db] = mfma32(a, pf[c][ks], oacc[db]);
+  };
+  auto s_read = [&](uint32_t kslot, int i) {  // i = c * KST + kk
+    const int kk = i % KST, c = i / KST;
+    return lds_ld16(((kslot + ka_base) ^ (uint32_t)(kk << 5)) + c * 32 * D * 2);
+  };
+  auto s_op = [&](int i, bf16x8 a) {
+    const int kk = i % KST, c = i / KST;
+    s[c] = mfma32(a, qf[kk], kk == 0 ? f32x16{} : s[c]);
+  };
+
+  // M-phase of stream step st: P.V of tile st-1 (if it was one of this
+  // wave's), then S of tile st (if it is). Each part is straight-line with
+  // its operand reads LEAD MFMAs ahead of their use, and updates its
+  // accumulators in place.
+  auto m_phase = [&](int st, bool do_pv, bool do_s) {
+    const uint32_t Vb = vt_lds + (uint32_t)(((st + NB - 1) % NB) * TILE * 2);
+    const uint32_t Kb = ks_lds + (uint32_t)((st % NB) * TILE * 2);
+    __builtin_amdgcn_s_setprio(1);
+    if (do_pv) {
+      bf16x8 ring[LEAD];
+#pragma unroll
+      for (int i = 0; i < LEAD; ++i) ring[i] = pv_read(Vb, i);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const bf16x8 a = ring[i % LEAD];
+        pv_op(i, a);
+        if (i + LEAD < NPV) ring[i % LEAD] = pv_read(Vb, i + LEAD);
+      }
+      sched_ring<NPV, LEAD>();
+    }
+    if (do_s) {
+      constexpr int N = 2 * KST;
+      bf16x8 ring[LEAD];
+#pragma unroll
+      for (int i = 0; i < LEAD; ++i) ring[i] = s_read(Kb, i);
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const bf16x8 a = ring[i % LEAD];
+        s_op(i, a);
+        if (i + LEAD < N) ring[i % LEAD] = s_read(Kb, i + LEAD);
+      }
+      sched_ring<N, LEAD>();
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // V-phase of tile t (key tile index) for rows r0 .. r0+31: probabilities
+  // p = 2^S, their bf16 operands and row sums. The logits are bounded
+  // (|S| <= c2, the bound |scale| * D in base 2), so no running maximum is
+  // needed, and no shift either: softmax is invariant to a common factor, and
+  // 2^(+-c2) stays far inside the normal fp32 and bf16 range (c2 <= 46), as
+  // does a row sum over any number of keys. The row sum adds up the same
+  // bf16-rounded probabilities that P.V multiplies (unpacked from the
+  // operand registers), so the weights O is normalised with sum to one
+  // exactly, and a row that sees few keys is not left with the rounding of
+  // its probabilities.
+  auto v_phase = [&](int t, int r0) {
+    const int row = r0 + l32;
+    float lsum[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float pv[16];
+      const int kc = t * BN + 32 * c;
+      if (!(kc + 31 <= r0 && (W < 0 || r0 + 31 - kc <= W))) {
+        // the chunk crosses the diagonal or the window start: mask per element
+        const uint32_t rk0 = (uint32_t)(row - (kc + 8 * half));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = rk0 - (uint32_t)(16 * (r >> 3) + (r & 7)) <= Wm;
+          pv[r] = ok ? fast_exp2(s[c][r]) : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(s[c][r]);
+      }
+      uint32_t wd[8];
+      float t8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        wd[i] = pack2(pv[2 * i], pv[2 * i + 1]);
+        t8[i] = __uint_as_float(wd[i] << 16) + __uint_as_float(wd[i] & 0xffff0000u);
+      }
+      lsum[c] = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+      pf[c][0] = __builtin_bit_cast(bf16x8, u32x4{wd[0], wd[1], wd[2], wd[3]});
+      pf[c][1] = __builtin_bit_cast(bf16x8, u32x4{wd[4], wd[5], wd[6], wd[7]});
+    }
+    l_run += lsum[0] + lsum[1];
+  };
+
+  // Epilogue of a finished item: O / l -> bf16, LSE (natural log); then the
+  // accumulators start over for the next item.
+  struct Epi {
+    long o_off;    // element offset of (b, row, head, 4 half) in o
+    long lse_off;  // index of (b, head, row) in lse
+    bool ok;       // row < T
+  };
+  Epi epi{0, 0, false};
+  auto epilogue = [&]() {
+    const float l_tot = pair_sum(l_run);
+    if (epi.ok) {
+      const float inv = 1.f / l_tot;
+      bf16* dst = (bf16*)p.o + epi.o_off;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x2 v;
+          v[0] = pack2(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
+          v[1] = pack2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+          *(u32x2*)(dst + 32 * db + 8 * i) = v;
+        }
+      if (half == 0) p.lse[epi.lse_off] = fast_log2(l_tot) * kLn2;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    l_run = 0.f;
+  };
+
+  // ---- prologue: the first tiles of the stream (K tiles 0..NB-1 by group
+  // 1, V tiles 0..NB-2 by group 0) and the first item's q rows, whose
+  // latencies overlap
+  if (grp == 1) {
+    for (int st = 0; st < NB && st < n_steps; ++st) issue(st);
+  } else {
+    for (int st = 0; st < NB - 1 && st < n_steps; ++st) issue(st);
+  }
+  {
+    const Item it = item(0);
+    const auto rq = make_rsrc((const bf16*)p.q + ((long)it.b * T * p.Hq + it.head) * D, (uint32_t)T * qstride * 2);
+    const uint32_t off = (uint32_t)((it.qb * BM + rw * 32 + l32) * qstride + 8 * half) * 2;
+    u32x4 x[KST];
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) x[kk] = bload16(rq, off + 32 * kk);
+    q_norm(x);
+  }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed in LDS
   __syncthreads();
 
-  // ---- phases. Group 0 runs M(tau) in interval 2tau and V(tau) in 2tau+1;
-  // group 1 runs one interval later. Every wave passes the same 2*ntile + 2
-  // barriers. In each V-phase the loading group first waits for the loads it
-  // issued two intervals earlier (the barrier after it publishes them), then
-  // issues the next: group 1 the K tile NB ahead of the tile it just
-  // finished, group 0 the V tile NB-2 ahead. A K tile is read in the two
-  // M-phases of its own tile, a V tile in the two that follow, and a slot is
-  // refilled only after both, so no slot is overwritten while read.
-  // The wave's own work covers tiles ta..tb; the steps before, at ta, inside,
-  // at tb+1 and after run as separate loops, so that each loop body is
-  // straight-line in the accumulators.
-  auto step = [&](int tau, auto kind) {
-    constexpr int K = decltype(kind)::value;
-    if constexpr (K != M_SKIP) {
-      __builtin_amdgcn_s_setprio(1);
-      m_phase(tau, kind);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    __syncthreads();
-    if (grp == 1 && tau == ntile) return;  // group 1 ends on its last M-phase
-    if constexpr (K == M_S || K == M_FULL) v_phase(tau);
-    __builtin_amdgcn_s_waitcnt(0);
-    if (grp == 0) {
-      if (tau >= 1 && tau + NB - 2 < ntile) issue_v(tau + NB - 2);
-    } else {
-      if (tau + NB < ntile) issue_k(tau + NB);
-    }
-    __syncthreads();
-  };
-  using skip_t = std::integral_constant<int, M_SKIP>;
+  // ---- stream steps. Group 0 runs M(st) in interval 2st and V(st) in
+  // 2st+1; group 1 runs one interval later. Every wave passes the same
+  // 2*n_steps + 2 barriers. In each V-phase the loading group first waits
+  // for the loads it issued two intervals earlier (the barrier after it
+  // publishes them), then issues the next: group 1 the K tile NB ahead of the
+  // tile it just finished, group 0 the V tile NB-2 ahead. A K tile is read
+  // in the two M-phases of its own step, a V tile in the two that follow,
+  // and a slot is refilled only after both, so no slot is overwritten while
+  // read. The next item's q rows are copied into the wave's LDS region in
+  // the first V-phase of an item (and waited for with the tiles), then read
+  // back and normed in its last.
   if (grp == 1) __syncthreads();
-  const int t_first = wave_active ? ta : ntile + 1;  // idle waves only pass barriers
-  int tau = 0;
+  bool pend_pv = false, pend_epi = false;
+  int st = 0;
+  for (int k = 0; k < nk; ++k) {
+    const Item it = item(k);
+    const int r0 = it.qb * BM + rw * 32;  // first query row of this wave
+    const int row_hi = min(T, it.qb * BM + BM) - 1;
+    // tiles of the item that hold keys visible to some row of this wave
+    const int ta = r0 < T ? (W < 0 ? 0 : max(0, r0 - W) / BN) - it.n_lo : 1;
+    const int tb = r0 < T ? min(r0 + 31, row_hi) / BN - it.n_lo : 0;
+    const Epi here{((long)it.b * T + r0 + l32) * qstride + (long)it.head * D + 4 * half,
+                   ((long)it.b * p.Hq + it.head) * T + r0 + l32, r0 + l32 < T};
 #pragma clang loop unroll(disable)
-  for (; tau < t_first; ++tau) step(tau, skip_t{});
-  if (wave_active) {
-    step(tau++, std::integral_constant<int, M_S>{});
-#pragma clang loop unroll(disable)
-    for (; tau <= tb; ++tau) step(tau, std::integral_constant<int, M_FULL>{});
-    step(tau++, std::integral_constant<int, M_PV>{});
-#pragma clang loop unroll(disable)
-    for (; tau <= ntile; ++tau) step(tau, skip_t{});
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-
-  if (!wave_active) return;
-  const float l_tot = pair_sum(l_run);
-  if (row >= T) return;
-  const float inv = 1.f / l_tot;
-  bf16* dst = (bf16*)p.o + ((long)b * T + row) * qstride + (long)head * D + 4 * half;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x2 w;
-      w[0] = pack2(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
-      w[1] = pack2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
-      *(u32x2*)(dst + 32 * db + 8 * i) = w;
+    for (int tau = 0; tau < it.ntile; ++tau, ++st) {
+      const bool act = tau >= ta && tau <= tb;
+      m_phase(st, pend_pv, act);
+      __syncthreads();
+      if (pend_epi) epilogue();
+      if (act) v_phase(it.n_lo + tau, r0);
+      pend_pv = act;
+      pend_epi = act && tau == tb;
+      if (pend_epi) epi = here;
+      __builtin_amdgcn_s_waitcnt(0);
+      if (k + 1 < nk) {
+        if (tau == 0) q_prefetch(item(k + 1));
+        if (tau == it.ntile - 1) {
+          if (it.ntile == 1) __builtin_amdgcn_s_waitcnt(0);
+          q_from_lds();
+        }
+      }
+      if (grp == 1 || st >= 1) {
+        if (cur.k < nk) issue(st + (grp == 1 ? NB : NB - 2));
+      }
+      __syncthreads();
     }
-  if (half == 0) p.lse[((long)b * p.Hq + head) * T + row] = (p.c2 + fast_log2(l_tot)) * kLn2;
-}
-
-template <int D, int NB>
-__global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(1024))) bf16 Ks[NB][D * 64];
-  __shared__ __attribute__((aligned(1024))) bf16 Vt[NB][D * 64];
-  fwd_pp_block<D, NB>(p, blockIdx.x, Ks, Vt);
+  }
+  // final step: P.V of the last tile; group 1 ends on its M-phase barrier
+  m_phase(st, pend_pv, false);
+  __syncthreads();
+  if (pend_epi) epilogue();
+  if (grp == 1) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 hipError_t launch_fwd_pp(const FwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
   constexpr int NB = 3;
-  const dim3 grid((unsigned)(p.nqb * p.B * p.Hkv * p.nsub));
+  const int n_items = p.nqb * p.B * p.Hkv * p.nsub;
+  const dim3 grid((unsigned)min(n_items, p.nwg));
   if (ev.start != nullptr) {
     const hipError_t e = hipEventRecord(ev.start, stream);
     if (e != hipSuccess) return e;

@@ -22,6 +22,7 @@ struct FwdParams {
   int nqb;               // number of 128-row query blocks
   int nsub;              // workgroups per (batch, KV head, query block) = G / heads-per-workgroup
   int Tp;                // T rounded up to a multiple of 64 (key axis of vt)
+  int nwg;               // workgroups of a persistent launch (one per compute unit)
 };
 
 struct KvPrepParams {
@@ -54,6 +55,7 @@ struct BwdParams {
   int nqb;        // number of 128-row query blocks (dQ kernel)
   int nsub;       // dQ workgroups per (batch, KV head, query block)
   int nkb;        // number of 128-key blocks (dK/dV kernel)
+  int nwg;        // workgroups of a persistent launch (one per compute unit)
 };
 
 struct NormParams {

@@ -127,6 +127,9 @@ def test_timing_hook_validation(sa):
     assert lib.sa_set_timing_events(3, None, None) == SA_ERR_SHAPE
     assert lib.sa_set_timing_events(-1, None, None) == SA_ERR_SHAPE
     assert lib.sa_set_timing_events(0, P(16), None) == SA_ERR_NULL
+    assert lib.sa_set_max_workgroups(-1) == SA_ERR_SHAPE
+    assert lib.sa_set_max_workgroups(3) == SA_OK
+    assert lib.sa_set_max_workgroups(0) == SA_OK
     for k in range(3):
         assert lib.sa_set_timing_events(k, None, None) == SA_OK
 

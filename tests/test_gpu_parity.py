@@ -209,3 +209,34 @@ def test_tiles_outside_the_band_are_never_read(sa):
     assert rel_l2(dk[:, keys].cpu(), dk_r[:, keys]) < 5e-2
     assert rel_l2(dv[:, keys].cpu(), dv_r[:, keys]) < 5e-2
     assert rel_l2(dq[:, 1280:].cpu(), dq_r[:, 1280:]) < 5e-2
+
+
+PERSIST_CASES = [
+    # B, T, Hq, Hkv, D, W, max workgroups
+    (3, 390, 4, 2, 128, -1, 1),     # one workgroup runs every item in turn
+    (3, 390, 4, 2, 128, 100, 3),
+    (2, 700, 4, 2, 128, 256, 5),
+    (4, 50, 4, 2, 128, -1, 2),      # single-tile items back to back
+    (2, 333, 12, 2, 64, 40, 4),     # G = 6: three head pairs per KV head
+    (2, 260, 4, 2, 64, 0, 3),
+]
+
+
+@pytest.mark.parametrize("case", PERSIST_CASES,
+                         ids=[f"B{c[0]}T{c[1]}Hq{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}wg{c[6]}" for c in PERSIST_CASES])
+def test_persistent_workgroups_many_items(sa, case):
+    """The persistent kernels give each workgroup a fixed share of the work
+    items; capping the grid makes every workgroup run many items of different
+    sizes in a row (tile stream, prefetched q rows and epilogues crossing item
+    boundaries). Results must match the oracle as for any other launch."""
+    B, T, Hq, Hkv, D, W, nwg = case
+    scale = D ** -0.5
+    log(f"[persistent] {case}")
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=500 + T)
+    sa.sa_set_max_workgroups(nwg)
+    try:
+        o, lse, dq, dk, dv = gpu_fwd_bwd(sa, q, k, v, do, W, scale)
+    finally:
+        sa.sa_set_max_workgroups(0)
+    compare_forward(o, lse, q, k, v, W, scale)
+    compare_backward(dq, dk, dv, q, k, v, do, W, scale)
