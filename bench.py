@@ -47,7 +47,7 @@ COPY_PROBE_BYTES = 1 << 30  # bytes read (and written) by the copy probe: 4x the
 KERNELS = {
     "fwd": ("attn_fwd_pp_kernel", ("attn_fwd_pp.hip", "sa_common.h")),
     "bwd_dq": ("attn_bwd_dq_pp_kernel", ("attn_bwd_dq_pp.hip", "sa_common.h")),
-    "bwd_dkdv": ("attn_bwd_dkdv_split_kernel", ("attn_bwd_dkdv_split.hip", "sa_common.h")),
+    "bwd_dkdv": ("attn_bwd_dkdv_pp_kernel", ("attn_bwd_dkdv_pp.hip", "sa_common.h")),
 }
 
 

@@ -221,7 +221,7 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
       p.khat = khat;
     }
     if (sa::launch_bwd_dq_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DQ]) != hipSuccess) return SA_ERR_HIP;
-    return sa::launch_bwd_dkdv_split(p, head_dim, s, tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess ? SA_OK
+    return sa::launch_bwd_dkdv_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess ? SA_OK
                                                                                                 : SA_ERR_HIP;
   }
   return sa::launch_bwd(p, head_dim, hpw, qk_norm != 0, s, tl_events[SA_KERNEL_BWD_DQ],

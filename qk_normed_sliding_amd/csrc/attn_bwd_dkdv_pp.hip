@@ -1,19 +1,22 @@
-// dK/dV kernel of the backward with the work of a key block split between
-// two warp groups that share LDS ([post] QK-norm and SSSL passages; [guide]
-// 8.2.1; same gradients as the dK/dV kernel in attn_bwd.hip):
-//   group A (waves 0-3) keeps k_hat of its 32 keys and the dV accumulator:
-//     S = Q_hat K_hat^T -> P = exp(S - LSE) (masked to the band) -> P to LDS,
-//     dV^T += dO^T P
-//   group B (waves 4-7) keeps v of the same keys and the dK accumulator:
-//     dP = dO V^T, P from LDS -> dS = P (dP - Delta), dK^T += Q_hat^T dS
-// so each wave holds half of the per-key state the single-group kernel
-// needs, two waves share every SIMD, and the matrix cores of a SIMD see 16
-// MFMAs from each of them per 32-row query chunk. A chunk's S/P and dP
-// happen in one interval, its dV and dS/dK in the next; intervals end in a
-// workgroup barrier. q_hat and dO tiles of 64 rows (plus their LSE and
-// Delta) stream into three LDS slots as direct buffer-to-LDS copies, two
-// tiles ahead; rows are XOR-swizzled so that the 16-byte row reads (S, dP)
-// and the transpose reads (dV, dK) are bank-conflict free.
+// dK/dV kernel of the backward ([post] QK-norm and SSSL passages; [guide]
+// 8.2.1; same gradients as the dK/dV kernel in attn_bwd.hip), organised like
+// the forward as two warp groups that take turns on the matrix cores. One
+// workgroup owns 128 keys of one KV head (32 per wave of a group) and walks
+// the query tiles (64 rows of one query head of the group) whose rows see
+// them; the per-key state is split by role:
+//   group A (waves 0-3) keeps k_hat and the dV accumulator:
+//     M-phase of tile t: dV^T += dO^T P of tile t-1, S = Q_hat K_hat^T of tile t
+//     V-phase of tile t: P = exp(S - LSE) (masked to the band), kept as the
+//                        next dV operand and written to LDS for group B
+//   group B (waves 4-7) keeps v and the dK accumulator:
+//     M-phase of tile t: dK^T += Q_hat^T dS of tile t-1, dP = dO V^T of tile t
+//     V-phase of tile t: dS = P (dP - Delta) with P from group A
+// Group A runs M(t) in interval 2t and V(t) in 2t+1, group B one interval
+// later, with a workgroup barrier between intervals: on every SIMD one wave
+// works the matrix cores while its partner does the vector work. q_hat and
+// dO tiles of 64 rows (plus their LSE and Delta) stream into three LDS slots
+// as direct buffer-to-LDS copies; rows are XOR-swizzled so that the 16-byte
+// row reads (S, dP) and the transpose reads (dV, dK) are bank-conflict free.
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -21,15 +24,12 @@
 
 namespace sa {
 
-// Scheduling of an operand stream: N1 operands of one 16-byte read each,
-// then N2 operands of two transpose reads each, consumed in that order by
-// one MFMA per operand. PRE other reads and the first LEAD operands are
-// issued up front; after MFMA i come the reads of operand i + LEAD, so LEAD
-// operands are in flight while the register footprint stays small.
-template <int N1, int N2, int LEAD, int PRE>
-__device__ __forceinline__ void sched_stream() {
-  static_assert(LEAD <= N1, "the lead covers one-read operands only");
-  __builtin_amdgcn_sched_group_barrier(0x100, PRE + LEAD, 0);
+// M-phase order for the scheduler: N1 operands of one 16-byte read each,
+// then N2 operands of two transpose reads each, consumed in that order by one
+// MFMA per operand, with the reads of operand i + LEAD issued after MFMA i.
+template <int N1, int N2, int LEAD>
+__device__ __forceinline__ void sched_mphase() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
 #pragma unroll
   for (int i = 0; i < N1 - LEAD; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -44,7 +44,7 @@ __device__ __forceinline__ void sched_stream() {
 }
 
 template <int D>
-__global__ void __launch_bounds__(512) attn_bwd_dkdv_split_kernel(BwdParams p) {
+__global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   constexpr int NB = 3;
   constexpr int BQ = 64;               // query rows per tile (two 32-row chunks)
   constexpr int BK = 128;              // keys per workgroup (32 per wave of a group)
@@ -54,13 +54,14 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_split_kernel(BwdParams p) {
   constexpr int TILE = BQ * D;
   constexpr int RPI = 64 / CPR;        // rows per direct-to-LDS instruction (1 KB)
   constexpr int IPW = BQ / RPI / 4;    // instructions per wave, per tile
+  constexpr int LEAD = 4;              // operands in flight ahead of the MFMAs
   static_assert(KST == 2 * NDB, "operand groups of the row and transpose MFMAs have the same size");
 
   __shared__ __attribute__((aligned(1024))) bf16 Qs[NB][TILE];
   __shared__ __attribute__((aligned(1024))) bf16 Os[NB][TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 Xs[2][4][2 * 512];  // P of a chunk, per wave pair
-  __shared__ __attribute__((aligned(16))) float Ls[NB][BQ];           // LSE of the tile's rows
-  __shared__ __attribute__((aligned(16))) float Dl[NB][BQ];           // Delta of the tile's rows
+  __shared__ __attribute__((aligned(1024))) bf16 Xs[4][2][2 * 512];  // P of a tile (2 chunks), per wave pair
+  __shared__ __attribute__((aligned(16))) float Ls[NB][BQ];          // LSE of the tile's rows
+  __shared__ __attribute__((aligned(16))) float Dl[NB][BQ];          // Delta of the tile's rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -156,9 +157,14 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_split_kernel(BwdParams p) {
   }
   auto lds_ld16 = [](uint32_t addr) { return *(SA_LDS const bf16x8*)(uintptr_t)addr; };
   auto lds_tr = [](uint32_t addr) { return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4*)(uintptr_t)addr); };
-  auto rows_load = [&](uint32_t slot, int qc, bf16x8 (&a)[KST]) {
+  // both chunks' rows, interleaved (chunk 0 k-step 0, chunk 1 k-step 0, ...),
+  // the order in which the two S (or dP) chains consume them
+  auto rows_load2 = [&](uint32_t slot, bf16x8 (&a0)[KST], bf16x8 (&a1)[KST]) {
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk) a[kk] = lds_ld16(((slot + ra_base) ^ (uint32_t)(kk << 5)) + qc * 32 * D * 2);
+    for (int kk = 0; kk < KST; ++kk) {
+      a0[kk] = lds_ld16(((slot + ra_base) ^ (uint32_t)(kk << 5)));
+      a1[kk] = lds_ld16(((slot + ra_base) ^ (uint32_t)(kk << 5)) + 32 * D * 2);
+    }
   };
   auto tr_load = [&](uint32_t slot, int qc, bf16x8 (&a)[KST]) {
 #pragma unroll
@@ -175,15 +181,12 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_split_kernel(BwdParams p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  f32x16 dp_prev;     // group B: dP of the previous chunk
-  bf16x8 pb[2];       // group A: P of the previous chunk (B operand of dV)
-#pragma unroll
-  for (int r = 0; r < 16; ++r) dp_prev[r] = 0.f;
-  pb[0] = pb[1] = bf16x8{};
+  f32x16 sc[2];     // S (A) or dP (B) of the current tile, from its M-phase to its V-phase
+  bf16x8 op[2][2];  // P (A) or dS (B) of the previous tile: B operands of dV / dK
 
-  // band test of chunk c = (tile it, chunk qc): register r of a lane holds
-  // query row q0 + 16(r>>3) + 8half + (r&7) and key `key`
-  auto chunk_q0 = [&](int c) { return (qb_lo + (c >> 1) % nqb) * BQ + 32 * (c & 1); };
+  // band test of chunk qc of tile it: register r of a lane holds query row
+  // q0 + 16(r>>3) + 8half + (r&7) and key `key`
+  auto chunk_q0 = [&](int it, int qc) { return (qb_lo + it % nqb) * BQ + 32 * qc; };
   auto chunk_edge = [&](int q0) {  // not every (row, key) pair of the chunk is inside the band
     return !(q0 >= kw0 + 31 && (W < 0 || q0 + 31 - kw0 <= W)) || q0 + 31 >= T;
   };
@@ -191,36 +194,60 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_split_kernel(BwdParams p) {
     const int q = q0 + 16 * (r >> 3) + 8 * half + (r & 7);
     return ((uint32_t)(q - key) <= Wm) & (q < T);
   };
-  auto xs_addr = [&](int c, int ks) { return lds_addr(&Xs[c & 1][rw][ks * 512 + 8 * lane]); };
+  auto xs_addr = [&](int qc, int ks) { return lds_addr(&Xs[rw][qc][ks * 512 + 8 * lane]); };
 
-  // ---- interval c: chunk c's S/P (A) or dP (B), chunk c-1's dV (A) or
-  // dS/dK (B). The first interval has no chunk c-1, the last no chunk c; the
-  // three kinds are separate straight-line bodies with their LDS reads issued
-  // ahead of the MFMAs that consume them.
-  enum { I_FIRST = 0, I_MID = 1, I_LAST = 2 };
-  auto interval_a = [&](int c, auto kind) {
+  // ---- M-phase of tile t (both groups): the row-operand chains of tile t
+  // (A: S from q_hat rows, B: dP from dO rows; B operand kf), then the
+  // transpose-operand MFMAs of tile t-1 (A: dV from dO^T and P, B: dK from
+  // q_hat^T and dS). The first step has no tile t-1, the last no tile t.
+  enum { K_FIRST = 0, K_MID = 1, K_LAST = 2 };
+  auto m_phase = [&](int t, auto kind) {
     constexpr int K = decltype(kind)::value;
-    constexpr bool CUR = K != I_LAST, PREV = K != I_FIRST;
-    const int cp = c - 1;
-    {
-      bf16x8 a[KST], t[KST];
-      f32x16 s;
-      if constexpr (CUR) rows_load(qs_lds + (uint32_t)(((c >> 1) % NB) * TILE * 2), c & 1, a);
-      if constexpr (PREV) tr_load(os_lds + (uint32_t)(((cp >> 1) % NB) * TILE * 2), cp & 1, t);
-      if constexpr (CUR) {
-        s = mfma32(a[0], kf[0], f32x16{});
+    constexpr bool CUR = K != K_LAST, PREV = K != K_FIRST;
+    const uint32_t rows_slot = (grp == 0 ? qs_lds : os_lds) + (uint32_t)((t % NB) * TILE * 2);
+    const uint32_t tr_slot = (grp == 0 ? os_lds : qs_lds) + (uint32_t)(((t + NB - 1) % NB) * TILE * 2);
+    bf16x8 a0[KST], a1[KST], u0[KST], u1[KST];
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (CUR) rows_load2(rows_slot, a0, a1);
+    if constexpr (PREV) {
+      tr_load(tr_slot, 0, u0);
+      tr_load(tr_slot, 1, u1);
+    }
+    if constexpr (CUR) {
+      f32x16 c0 = mfma32(a0[0], kf[0], f32x16{});
+      f32x16 c1 = mfma32(a1[0], kf[0], f32x16{});
 #pragma unroll
-        for (int kk = 1; kk < KST; ++kk) s = mfma32(a[kk], kf[kk], s);
+      for (int kk = 1; kk < KST; ++kk) {
+        c0 = mfma32(a0[kk], kf[kk], c0);
+        c1 = mfma32(a1[kk], kf[kk], c1);
       }
-      if constexpr (PREV) {  // dV^T += dO^T P of chunk c-1
+      sc[0] = c0;
+      sc[1] = c1;
+    }
+    if constexpr (PREV) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(t[ks * NDB + db], pb[ks], acc[db]);
-      }
-      if constexpr (CUR) {  // P of chunk c, kept for the next dV and handed to group B
-        const int q0 = chunk_q0(c);
-        const float* lse = &Ls[(c >> 1) % NB][32 * (c & 1)];
+        for (int db = 0; db < NDB; ++db) acc[db] = mfma32(u0[ks * NDB + db], op[0][ks], acc[db]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = mfma32(u1[ks * NDB + db], op[1][ks], acc[db]);
+    }
+    if constexpr (CUR && PREV) sched_mphase<2 * KST, 2 * KST, LEAD>();
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- V-phase of tile t. A: P of tile t from S and the rows' LSE, masked
+  // on chunks that cross the band edge; kept as the next dV operand and
+  // written to LDS. B: dS of tile t = P (dP - Delta), P from LDS (written by A
+  // one interval earlier).
+  auto v_phase = [&](int t) {
+    if (grp == 0) {
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+        const int q0 = chunk_q0(t, qc);
+        const float* lse = &Ls[t % NB][32 * qc];
         float pr[16];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -228,7 +255,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_split_kernel(BwdParams p) {
           const f32x4 l1 = *(const f32x4*)(lse + 16 * ks + 8 * half + 4);
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            pr[8 * ks + e] = fast_exp2(__builtin_fmaf(s[8 * ks + e], p.c1, -(e < 4 ? l0[e] : l1[e - 4]) * kLog2e));
+            pr[8 * ks + e] = fast_exp2(__builtin_fmaf(sc[qc][8 * ks + e], p.c1, -(e < 4 ? l0[e] : l1[e - 4]) * kLog2e));
         }
         if (chunk_edge(q0)) {  // one branch per chunk; the mask itself is a select per element
 #pragma unroll
@@ -237,88 +264,62 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_split_kernel(BwdParams p) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const u32x4 w = pack8(pr + 8 * ks);
-          pb[ks] = __builtin_bit_cast(bf16x8, w);
-          *(SA_LDS u32x4*)(uintptr_t)xs_addr(c, ks) = w;
+          op[qc][ks] = __builtin_bit_cast(bf16x8, w);
+          *(SA_LDS u32x4*)(uintptr_t)xs_addr(qc, ks) = w;
         }
       }
-      // reads: S operands first, then the dV operands behind the S MFMAs
-      if constexpr (CUR && PREV) sched_stream<KST, KST, 3, 0>();
-    }
-  };
-  auto interval_b = [&](int c, auto kind) {
-    constexpr int K = decltype(kind)::value;
-    constexpr bool CUR = K != I_LAST, PREV = K != I_FIRST;
-    const int cp = c - 1;
-    {
-      bf16x8 a[KST], t[KST];
-      f32x16 dp;
-      bf16x8 dsb[2];
-      if constexpr (PREV) {  // dS of chunk c-1 from its P (group A, previous interval)
-        const float* dl = &Dl[(cp >> 1) % NB][32 * (cp & 1)];
+    } else {
+      const float* dl = &Dl[t % NB][0];
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const u32x4 w = *(SA_LDS const u32x4*)(uintptr_t)xs_addr(cp, ks);
+          const u32x4 w = *(SA_LDS const u32x4*)(uintptr_t)xs_addr(qc, ks);
           float pr[8];
           unpack8(w, pr);
-          const f32x4 d0 = *(const f32x4*)(dl + 16 * ks + 8 * half);
-          const f32x4 d1 = *(const f32x4*)(dl + 16 * ks + 8 * half + 4);
+          const f32x4 e0 = *(const f32x4*)(dl + 32 * qc + 16 * ks + 8 * half);
+          const f32x4 e1 = *(const f32x4*)(dl + 32 * qc + 16 * ks + 8 * half + 4);
           float ds[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ds[e] = pr[e] * (dp_prev[8 * ks + e] - (e < 4 ? d0[e] : d1[e - 4]));
-          dsb[ks] = __builtin_bit_cast(bf16x8, pack8(ds));
+          for (int e = 0; e < 8; ++e) ds[e] = pr[e] * (sc[qc][8 * ks + e] - (e < 4 ? e0[e] : e1[e - 4]));
+          op[qc][ks] = __builtin_bit_cast(bf16x8, pack8(ds));
         }
-      }
-      if constexpr (CUR) rows_load(os_lds + (uint32_t)(((c >> 1) % NB) * TILE * 2), c & 1, a);
-      if constexpr (PREV) tr_load(qs_lds + (uint32_t)(((cp >> 1) % NB) * TILE * 2), cp & 1, t);
-      if constexpr (CUR) {
-        dp = mfma32(a[0], kf[0], f32x16{});
-#pragma unroll
-        for (int kk = 1; kk < KST; ++kk) dp = mfma32(a[kk], kf[kk], dp);
-      }
-      if constexpr (PREV) {  // dK^T += Q_hat^T dS of chunk c-1
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(t[ks * NDB + db], dsb[ks], acc[db]);
-      }
-      if constexpr (CUR) dp_prev = dp;
-      if constexpr (CUR && PREV) sched_stream<KST, KST, 3, 6>();  // after the P and Delta reads
     }
   };
 
-  // ---- schedule: tile it is read in intervals 2it .. 2it+2, so tile it+3
-  // may refill its slot from interval 2it+3 on. In odd interval 2t+1 each
-  // wave waits for the loads it issued two intervals earlier (tile t+1, first
-  // read in interval 2t+2 after the barrier) and issues tile t+2.
-  for (int it = 0; it < 2 && it < nit; ++it) issue(it);
+  // ---- schedule. Tile t is read in intervals 2t (A: q_hat rows), 2t+1 (A:
+  // LSE; B: dO rows), 2t+2 (A: dO^T; B: Delta) and 2t+3 (B: q_hat^T). At the
+  // start of its M-phase of tile s each group issues its half of tile s+1
+  // (into the slot of tile s-2, last read in interval 2s-1), and waits for it
+  // at the end of its V-phase of tile s, before the barrier that publishes
+  // it. Group A runs M(t) in interval 2t and V(t) in 2t+1, group B one
+  // interval later; every wave passes 2*nit + 3 barriers (group B one at the
+  // start, group A one after its last, empty, V-phase).
+  issue(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  auto after = [&](int c) {
-    if (c & 1) {
+  if (grp == 1) __syncthreads();
+  auto run = [&]() {
+    if (1 < nit) issue(1);
+    m_phase(0, std::integral_constant<int, K_FIRST>{});
+    __syncthreads();
+    v_phase(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma clang loop unroll(disable)
+    for (int t = 1; t < nit; ++t) {
+      if (t + 1 < nit) issue(t + 1);
+      m_phase(t, std::integral_constant<int, K_MID>{});
+      __syncthreads();
+      v_phase(t);
       __builtin_amdgcn_s_waitcnt(0);
-      const int t = c >> 1;
-      if (t + 2 < nit) issue(t + 2);
+      __syncthreads();
     }
+    m_phase(nit, std::integral_constant<int, K_LAST>{});
     __syncthreads();
   };
-  const int nch = 2 * nit;
-  // the two groups run separate copies of the interval loop (same barrier
-  // count), so each keeps its accumulators in place across iterations
-  auto run = [&](auto interval) {
-    interval(0, std::integral_constant<int, I_FIRST>{});
-    after(0);
-#pragma clang loop unroll(disable)
-    for (int c = 1; c < nch; ++c) {
-      interval(c, std::integral_constant<int, I_MID>{});
-      after(c);
-    }
-    interval(nch, std::integral_constant<int, I_LAST>{});
-    after(nch);
-  };
-  if (grp == 0)
-    run(interval_a);
-  else
-    run(interval_b);
+  run();
+  if (grp == 0) __syncthreads();  // group A's last (empty) V-phase interval
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue (the accumulators hold head_dim 32db + 8i + 4half + j of key `key`)
@@ -378,16 +379,16 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_split_kernel(BwdParams p) {
     }
 }
 
-hipError_t launch_bwd_dkdv_split(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
+hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
   const dim3 grid((unsigned)(p.nkb * p.B * p.Hkv));
   if (ev.start != nullptr) {
     const hipError_t e = hipEventRecord(ev.start, stream);
     if (e != hipSuccess) return e;
   }
   if (head_dim == 128)
-    hipLaunchKernelGGL((attn_bwd_dkdv_split_kernel<128>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_bwd_dkdv_split_kernel<64>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64>), grid, dim3(512), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
   return e;

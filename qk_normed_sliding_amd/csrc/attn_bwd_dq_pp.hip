@@ -39,6 +39,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
 
   __shared__ __attribute__((aligned(1024))) bf16 Ks[NBK][TILE];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[NBV][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 St[6][32 * D];  // prologue staging of waves 0-5
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -67,47 +68,22 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   const int row = r0 + l32;
   const bool norm = p.qhat != p.q;  // q_hat is written (and the norm backward applied) only with the QK-norm
 
-  // ---- prologue: q_hat and dO fragments (B operands), Delta, LSE of this lane's row
+  // ---- prologue: q_hat and dO fragments (B operands), r_q, Delta and LSE of
+  // this lane's row. The q, dO and o rows of the wave are read with coalesced
+  // 16-byte loads, QRPI whole rows per instruction (lane l: row QRPI*m +
+  // l/CPR, chunk l%CPR); row sums of squares and of dO*o are reduced over
+  // the CPR lanes of a row. q_hat is stored to the workspace from that same
+  // layout, and q_hat and dO reach the MFMA operand layout (lane = row) through
+  // a per-wave LDS staging area (row r's 16-byte chunk j at chunk j ^ (r mod
+  // CPR): conflict-free in both directions). Waves 6 and 7 stage in K slot
+  // NBK-1 and the per-row scalars go to V slot NBV-1; neither slot is loaded
+  // before the first barrier.
+  constexpr int QRPI = 64 / CPR;                // rows per coalesced instruction
+  constexpr int QM = 32 / QRPI;                 // instructions per 32 rows
+  const uint32_t stage = wave < 6 ? lds_addr(&St[wave][0]) : lds_addr(&Ks[NBK - 1][(wave - 6) * 32 * D]);
+  float* scal = (float*)&Vs[NBV - 1][0] + wave * 64;  // [0, 32): r_q, [32, 64): Delta
   bf16x8 qf[KST], df[KST];
-  float r_q = 1.f, delta, lse2;
-  {
-    const long first = ((long)b * T * p.Hq + head) * D;
-    const uint32_t bytes = (uint32_t)T * qstride * 2;
-    const auto rq = make_rsrc((const bf16*)p.q + first, bytes);
-    const auto rd = make_rsrc((const bf16*)p.dout + first, bytes);
-    const auto ro = make_rsrc((const bf16*)p.o + first, bytes);
-    const uint32_t off = (uint32_t)(row * qstride + 8 * half) * 2;
-    float x[KST][8];
-    float ss = 0.f, dd = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KST; ++kk) {
-      unpack8(bload16(rq, off + 32 * kk), x[kk]);
-      const u32x4 dw = bload16(rd, off + 32 * kk);
-      df[kk] = __builtin_bit_cast(bf16x8, dw);
-      float dv[8], ov[8];
-      unpack8(dw, dv);
-      unpack8(bload16(ro, off + 32 * kk), ov);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ss += x[kk][e] * x[kk][e];
-        dd += dv[e] * ov[e];
-      }
-    }
-    delta = pair_sum(dd);
-    if (norm) r_q = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps);
-    bf16* qh = (bf16*)p.qhat + first + (long)row * qstride + 8 * half;
-#pragma unroll
-    for (int kk = 0; kk < KST; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[kk][e] *= r_q;
-      const u32x4 w = pack8(x[kk]);
-      qf[kk] = __builtin_bit_cast(bf16x8, w);
-      if (norm && row < T) st16(qh + 16 * kk, w);
-    }
-    const long lrow = ((long)b * p.Hq + head) * T + row;
-    lse2 = row < T ? p.lse[lrow] * kLog2e : INFINITY;
-    if (half == 0 && row < T) p.delta[lrow] = delta;
-  }
+  float r_q = 1.f, delta = 0.f, lse2 = 0.f;
 
   // ---- key tiles that intersect the band of this block's rows
   const int row_lo = qb * BM;
@@ -277,6 +253,69 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   } else {
     for (int tau = 0; tau < 2 && tau < ntile; ++tau) issue_v(tau);
   }
+  // the rows of this wave (in flight together with the tiles)
+  {
+    const long first = ((long)b * T * p.Hq + head) * D;
+    const uint32_t bytes = (uint32_t)T * qstride * 2;
+    const auto rq = make_rsrc((const bf16*)p.q + first, bytes);
+    const auto rd = make_rsrc((const bf16*)p.dout + first, bytes);
+    const auto ro = make_rsrc((const bf16*)p.o + first, bytes);
+    const int crow = lane / CPR, cch = lane % CPR;  // row within an instruction, chunk
+    u32x4 xq[QM], xd[QM], xo[QM];
+#pragma unroll
+    for (int m = 0; m < QM; ++m) {
+      const uint32_t off = (uint32_t)((r0 + QRPI * m + crow) * qstride + 8 * cch) * 2;
+      xq[m] = bload16(rq, off);
+      xd[m] = bload16(rd, off);
+      xo[m] = bload16(ro, off);
+    }
+    bf16* qh = (bf16*)p.qhat + first;
+#pragma unroll
+    for (int m = 0; m < QM; ++m) {
+      const int r = QRPI * m + crow;  // row within the wave's 32
+      float f[8], dv[8], ov[8];
+      unpack8(xq[m], f);
+      unpack8(xd[m], dv);
+      unpack8(xo[m], ov);
+      float ss = 0.f, dd = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss += f[e] * f[e];
+        dd += dv[e] * ov[e];
+      }
+      ss = group_sum<CPR>(ss);
+      dd = group_sum<CPR>(dd);
+      const float rr = norm ? fast_rsqrt(ss * (1.f / D) + p.eps) : 1.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] *= rr;
+      const u32x4 w = pack8(f);
+      if (norm && r0 + r < T) st16(qh + (long)(r0 + r) * qstride + 8 * cch, w);
+      const uint32_t at = stage + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4));
+      *(SA_LDS u32x4*)(uintptr_t)at = norm ? w : xq[m];
+      if (cch == 0) {
+        scal[r] = rr;
+        scal[32 + r] = dd;
+      }
+    }
+    // lane = row reads (the same wave wrote them; LDS keeps a wave's order)
+    const uint32_t rbase = stage + (uint32_t)(l32 * D * 2);
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      qf[kk] = *(SA_LDS const bf16x8*)(uintptr_t)(rbase + (uint32_t)((((2 * kk + half) ^ (l32 % CPR))) << 4));
+    r_q = scal[l32];
+    delta = scal[32 + l32];
+#pragma unroll
+    for (int m = 0; m < QM; ++m) {
+      const int r = QRPI * m + crow;
+      *(SA_LDS u32x4*)(uintptr_t)(stage + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4))) = xd[m];
+    }
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      df[kk] = *(SA_LDS const bf16x8*)(uintptr_t)(rbase + (uint32_t)((((2 * kk + half) ^ (l32 % CPR))) << 4));
+    const long lrow = ((long)b * p.Hq + head) * T + row;
+    lse2 = row < T ? p.lse[lrow] * kLog2e : INFINITY;
+    if (half == 0 && row < T) p.delta[lrow] = delta;
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -321,24 +360,40 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- epilogue: dq = r (dq_hat - q_hat <dq_hat, q_hat> / D), dq_hat = scale * acc.
-  // The accumulator holds head_dim 32db + 8i + 4half + j of this lane's row.
+  // The accumulator holds head_dim 32db + 8i + 4half + j of this lane's row;
+  // q_hat (bf16, as the S MFMAs used it) comes from the operand registers,
+  // which hold head_dim 16kk + 8half + e. With i = 2a + c, the element sits in
+  // register kk = 2db + a, element 4half + j, of lane half' = c: this lane's
+  // own quad for c = half, the partner lane's (l ^ 32) for c != half. One
+  // lane-pair swap per dword of (low quad, high quad) delivers, in the low
+  // quad register, the elements for c = 0 and in the high quad register those
+  // for c = 1, in both lane halves.
   if (!wave_active || row >= T) return;
   const long rowoff = ((long)b * T + row) * qstride + (long)head * D + 4 * half;
   float qx[NDB][16];
   float dot = 0.f;
   if (norm) {
 #pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      const u32x4 w = __builtin_bit_cast(u32x4, qf[kk]);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+      const int db = kk >> 1, a = kk & 1;
+      // c = 0: i = 2a; c = 1: i = 2a + 1
+      const uint32_t lo[2] = {(uint32_t)s0[0], (uint32_t)s1[0]};
+      const uint32_t hi[2] = {(uint32_t)s0[1], (uint32_t)s1[1]};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        qx[db][4 * (2 * a) + 2 * t] = __uint_as_float(lo[t] << 16);
+        qx[db][4 * (2 * a) + 2 * t + 1] = __uint_as_float(lo[t] & 0xffff0000u);
+        qx[db][4 * (2 * a + 1) + 2 * t] = __uint_as_float(hi[t] << 16);
+        qx[db][4 * (2 * a + 1) + 2 * t + 1] = __uint_as_float(hi[t] & 0xffff0000u);
+      }
+    }
+#pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x2 w = *(const u32x2*)((const bf16*)p.q + rowoff + 32 * db + 8 * i);
-        qx[db][4 * i + 0] = __uint_as_float(w[0] << 16) * r_q;
-        qx[db][4 * i + 1] = __uint_as_float(w[0] & 0xffff0000u) * r_q;
-        qx[db][4 * i + 2] = __uint_as_float(w[1] << 16) * r_q;
-        qx[db][4 * i + 3] = __uint_as_float(w[1] & 0xffff0000u) * r_q;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dot += dq[db][4 * i + j] * qx[db][4 * i + j];
-      }
+      for (int r = 0; r < 16; ++r) dot += dq[db][r] * qx[db][r];
     dot = pair_sum(dot) * p.scale * (1.f / D);
   }
 #pragma unroll

@@ -83,8 +83,9 @@ hipError_t launch_bwd(const BwdParams& p, int head_dim, int heads_per_wg, bool q
 hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream,
                            const TimingEvents& kv_ev);
-// dK/dV kernel with the per-key state split over two warp groups (any query-heads-per-KV-head ratio).
-hipError_t launch_bwd_dkdv_split(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
+// dK/dV kernel whose two warp groups (per-key state split by role) alternate on the matrix cores
+// (any query-heads-per-KV-head ratio).
+hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
 hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream);
 
