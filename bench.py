@@ -145,9 +145,9 @@ def summarize_pmc(fetch_dir, write_dir, workload):
                        "fetch_scale": f_scale, "write_scale": w_scale},
         "kernels": kernels,
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o pmc -- python -u bench.py --steps 2 "
+            "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o pmc -- python -u bench.py --steps 2 "
             "--warmup 1 --cpu-seconds 0 --no-kernel-events --copy-probe",
-            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o pmc -- python -u bench.py --steps 2 "
+            "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o pmc -- python -u bench.py --steps 2 "
             "--warmup 1 --cpu-seconds 0 --no-kernel-events --copy-probe",
             "python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
         ],
