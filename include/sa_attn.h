@@ -57,7 +57,7 @@ typedef enum {
   SA_OK = 0,
   SA_ERR_NULL = 1,        /* a required pointer is NULL */
   SA_ERR_SHAPE = 2,       /* a size <= 0, Hq % Hkv != 0, window < -1, a non-finite scale or eps,
-                             eps < 0, or T*Hq*128*2 >= 2^31 (per-batch 32-bit addressing) */
+                             eps < 0, or (T+256)*Hq*128*2 >= 2^31 (per-batch 32-bit addressing) */
   SA_ERR_UNSUPPORTED = 3, /* head_dim not in {64, 128} */
   SA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
   SA_ERR_WORKSPACE = 5,   /* workspace NULL, not 256-byte aligned, or smaller than the *_workspace_bytes() size */

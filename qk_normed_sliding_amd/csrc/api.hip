@@ -63,8 +63,8 @@ sa_status check_shape(int B, int T, int Hq, int Hkv, int head_dim, int window, f
   if (elems > 9.0e18) return SA_ERR_SHAPE;
   if ((double)B * Hq * ((T + 127) / 128) > 2.0e9) return SA_ERR_SHAPE;
   // one batch's rows of q (or k, v) are addressed with 32-bit byte offsets,
-  // including the rows of the last 128-row block that lie past T
-  if (((double)T + 128.0) * Hq * 128.0 * 2.0 >= 2147483648.0) return SA_ERR_SHAPE;
+  // including the rows of the last 256-row block that lie past T
+  if (((double)T + 256.0) * Hq * 128.0 * 2.0 >= 2147483648.0) return SA_ERR_SHAPE;
   if (!valid_dim(head_dim)) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
@@ -141,12 +141,14 @@ SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* 
   p.c1 = softmax_scale * 1.4426950408889634f;
   p.eps = eps;
   const bool fixed = fixed_max_ok(qk_norm, softmax_scale, head_dim, &p.c2);
-  const int hpw = (p.G % 2 == 0) ? 2 : 1;
-  p.nsub = p.G / hpw;
-  p.nqb = (T + 127) / 128;
   p.khat = k;
   const hipStream_t s = (hipStream_t)stream;
-  if (hpw == 2 && fixed) {
+  if (fixed) {
+    // two warp groups per workgroup: two query heads of a KV group, or (odd G)
+    // two interleaved halves of 256 rows of one head
+    p.pair_rows = p.G % 2 != 0;
+    p.nsub = p.pair_rows ? p.G : p.G / 2;
+    p.nqb = p.pair_rows ? (T + 255) / 256 : (T + 127) / 128;
     // prologue: normed k rows and transposed v rows, so the attention kernel copies tiles
     p.Tp = (T + 63) / 64 * 64;
     p.nwg = persistent_wgs();
@@ -157,6 +159,10 @@ SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* 
     if (sa::launch_kv_prep(kp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
     return sa::launch_fwd_pp(p, head_dim, s, tl_events[SA_KERNEL_FWD]) == hipSuccess ? SA_OK : SA_ERR_HIP;
   }
+  // online-softmax kernel (logits without the QK-norm bound)
+  const int hpw = (p.G % 2 == 0) ? 2 : 1;
+  p.nsub = p.G / hpw;
+  p.nqb = (T + 127) / 128;
   return sa::launch_fwd(p, head_dim, hpw, qk_norm != 0, fixed, s, tl_events[SA_KERNEL_FWD]) == hipSuccess
              ? SA_OK
              : SA_ERR_HIP;
@@ -206,28 +212,23 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
   p.scale = softmax_scale;
   p.c1 = softmax_scale * 1.4426950408889634f;
   p.eps = eps;
-  const int hpw = (p.G % 2 == 0) ? 2 : 1;
-  p.nsub = p.G / hpw;
-  p.nqb = (T + 127) / 128;
+  // dQ: two warp groups per workgroup, on two query heads of a KV group or
+  // (odd G) on two interleaved halves of 256 rows of one head
+  p.pair_rows = p.G % 2 != 0;
+  p.nsub = p.pair_rows ? p.G : p.G / 2;
+  p.nqb = p.pair_rows ? (T + 255) / 256 : (T + 127) / 128;
   p.nkb = (T + 127) / 128;
   const hipStream_t s = (hipStream_t)stream;
   p.khat = k;
-  if (hpw == 2) {
-    // two-warp-group dQ kernel over k_hat tiles copied straight into LDS
-    if (qk_norm) {
-      void* khat = (char*)workspace + round256(rows * head_dim * 2) + round256(rows * sizeof(float));
-      sa::NormParams np{k, khat, nullptr, (int64_t)B * T * Hkv, eps};
-      if (sa::launch_qknorm(np, head_dim, s) != hipSuccess) return SA_ERR_HIP;
-      p.khat = khat;
-    }
-    if (sa::launch_bwd_dq_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DQ]) != hipSuccess) return SA_ERR_HIP;
-    return sa::launch_bwd_dkdv_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess ? SA_OK
-                                                                                                : SA_ERR_HIP;
+  if (qk_norm) {
+    // normed k rows, copied straight into LDS as tiles by the dQ kernel
+    void* khat = (char*)workspace + round256(rows * head_dim * 2) + round256(rows * sizeof(float));
+    sa::NormParams np{k, khat, nullptr, (int64_t)B * T * Hkv, eps};
+    if (sa::launch_qknorm(np, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+    p.khat = khat;
   }
-  return sa::launch_bwd(p, head_dim, hpw, qk_norm != 0, s, tl_events[SA_KERNEL_BWD_DQ],
-                        tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess
-             ? SA_OK
-             : SA_ERR_HIP;
+  if (sa::launch_bwd_dq_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DQ]) != hipSuccess) return SA_ERR_HIP;
+  return sa::launch_bwd_dkdv_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
 SA_API sa_status sa_set_timing_events(int kernel, void* start, void* stop) {

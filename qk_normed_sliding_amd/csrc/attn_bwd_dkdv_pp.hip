@@ -1,6 +1,5 @@
 // dK/dV kernel of the backward ([post] QK-norm and SSSL passages; [guide]
-// 8.2.1; same gradients as the dK/dV kernel in attn_bwd.hip), organised like
-// the forward as two warp groups that take turns on the matrix cores. One
+// 8.2.1), organised like the forward as two warp groups that take turns on the matrix cores. One
 // workgroup owns 128 keys of one KV head (32 per wave of a group) and walks
 // the query tiles (64 rows of one query head of the group) whose rows see
 // them; the per-key state is split by role:

@@ -1,9 +1,10 @@
-// dQ kernel of the backward for an even number of query heads per KV head,
-// organised like attn_fwd_pp.hip: two warp groups (one query head each, 32
-// query rows per wave) alternate M-phases and V-phases between workgroup
-// barriers, and the key and value tiles arrive as plain buffer-to-LDS copies
-// (k_hat from a norm prologue, v as stored). Same gradient as the dQ kernel
-// in attn_bwd.hip ([post] QK-norm and SSSL passages; [guide] 8.2.1):
+// dQ kernel of the backward, organised like attn_fwd_pp.hip: two warp groups
+// (32 query rows per wave; the groups take two query heads of a KV group, or
+// with an odd ratio alternate 32-row slices of 256 rows of one head)
+// alternate M-phases and V-phases between workgroup barriers, and the key and
+// value tiles arrive as plain buffer-to-LDS copies (k_hat from a norm
+// prologue, v as stored). The gradient of [post] QK-norm and SSSL passages,
+// [guide] 8.2.1:
 //   S = K_hat q_hat^T, dP = V dO^T        (one query row per lane)
 //   P = exp(S - LSE), dS = P (dP - Delta)  (V-phase)
 //   dq_hat^T += K_hat^T dS^T                (next M-phase; K_hat read K-major
@@ -57,8 +58,11 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   rem /= p.nsub;
   const int g = rem % p.Hkv;
   const int b = rem / p.Hkv;
-  const int head = g * p.G + sub * 2 + grp;
-  const int r0 = qb * BM + rw * 32;
+  // rows of the block: the two groups take two query heads (same 128 rows),
+  // or alternate 32-row slices of 256 rows of one head
+  const int BMI = p.pair_rows ? 2 * BM : BM;
+  const int head = g * p.G + (p.pair_rows ? sub : sub * 2 + grp);
+  const int r0 = qb * BMI + (p.pair_rows ? 64 * rw + 32 * grp : 32 * rw);
   const int T = p.T;
   const int W = p.window;
   const uint32_t Wm = W < 0 ? 0x7fffffffu : (uint32_t)W;
@@ -86,8 +90,8 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   float r_q = 1.f, delta = 0.f, lse2 = 0.f;
 
   // ---- key tiles that intersect the band of this block's rows
-  const int row_lo = qb * BM;
-  const int row_hi = min(T, row_lo + BM) - 1;
+  const int row_lo = qb * BMI;
+  const int row_hi = min(T, row_lo + BMI) - 1;
   const int key_lo = (W < 0) ? 0 : max(0, row_lo - W);
   const int n_lo = key_lo / BN;
   const int ntile = row_hi / BN - n_lo + 1;

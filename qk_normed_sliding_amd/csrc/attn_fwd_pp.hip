@@ -1,13 +1,15 @@
 // Forward of QK-normed, grouped-query, sliding-window causal attention for
-// the main shape class: an even number of query heads per KV head, bounded
-// logits (fixed row maximum), head_dim 64 or 128. Same computation as
+// bounded logits (fixed row maximum), head_dim 64 or 128. Same computation as
 // attn_fwd.hip ([post] QK-norm and SSSL passages; [guide] 8.2.1), organised
 // for gfx950 as a persistent kernel of two warp groups that take turns on
 // the matrix cores:
 //
 //   - A work item is one 128-row query block of 2 query heads sharing a KV
 //     head; waves 0-3 (group 0) own the first head's rows, waves 4-7 (group
-//     1) the second's, 32 rows per wave, q_hat normed in registers. One
+//     1) the second's, 32 rows per wave, q_hat normed in registers. With an
+//     odd number of query heads per KV head (MHA among them) an item is 256
+//     rows of one head instead, wave rw of group g taking rows 64rw + 32g ..
+//     +31, so that both groups again span the same keys. One
 //     workgroup runs per compute unit and takes the items of a fixed
 //     heavy-first "snake" order (round k: item k*G + w, or k*G + G-1-w on
 //     odd rounds), which balances the causal triangle as well as a dynamic
@@ -83,6 +85,11 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   const int kvstride = p.Hkv * D;
 
   // ---- the workgroup's items (heavy query blocks first, snake order)
+  // rows of an item, and this wave's first row in it: the two groups take
+  // two query heads (same 128 rows), or alternate 32-row slices of 256 rows
+  // of one head
+  const int BMI = p.pair_rows ? 2 * BM : BM;
+  const int wrow = p.pair_rows ? 64 * rw + 32 * grp : 32 * rw;
   const int per_qb = p.B * p.Hkv * p.nsub;
   const int n_items = p.nqb * per_qb;
   const int G = gridDim.x;
@@ -104,9 +111,9 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
     rem /= p.nsub;
     it.g = rem % p.Hkv;
     it.b = rem / p.Hkv;
-    it.head = it.g * p.G + sub * 2 + grp;
-    const int row_lo = it.qb * BM;
-    const int row_hi = min(T, row_lo + BM) - 1;
+    it.head = it.g * p.G + (p.pair_rows ? sub : sub * 2 + grp);
+    const int row_lo = it.qb * BMI;
+    const int row_hi = min(T, row_lo + BMI) - 1;
     const int key_lo = (W < 0) ? 0 : max(0, row_lo - W);
     it.n_lo = key_lo / BN;
     it.ntile = row_hi / BN - it.n_lo + 1;
@@ -204,7 +211,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   };
   auto q_prefetch = [&](const Item& it) {
     const u32x4 rq = q_rsrc(it);
-    const int r0 = it.qb * BM + rw * 32;
+    const int r0 = it.qb * BMI + wrow;
 #pragma unroll
     for (int m = 0; m < 32 / QRPI; ++m) {
       const int r = QRPI * m + lane / CPR;
@@ -387,7 +394,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   {
     const Item it = item(0);
     const auto rq = make_rsrc((const bf16*)p.q + ((long)it.b * T * p.Hq + it.head) * D, (uint32_t)T * qstride * 2);
-    const uint32_t off = (uint32_t)((it.qb * BM + rw * 32 + l32) * qstride + 8 * half) * 2;
+    const uint32_t off = (uint32_t)((it.qb * BMI + wrow + l32) * qstride + 8 * half) * 2;
     u32x4 x[KST];
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) x[kk] = bload16(rq, off + 32 * kk);
@@ -412,8 +419,8 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   int st = 0;
   for (int k = 0; k < nk; ++k) {
     const Item it = item(k);
-    const int r0 = it.qb * BM + rw * 32;  // first query row of this wave
-    const int row_hi = min(T, it.qb * BM + BM) - 1;
+    const int r0 = it.qb * BMI + wrow;  // first query row of this wave
+    const int row_hi = min(T, it.qb * BMI + BMI) - 1;
     // tiles of the item that hold keys visible to some row of this wave
     const int ta = r0 < T ? (W < 0 ? 0 : max(0, r0 - W) / BN) - it.n_lo : 1;
     const int tb = r0 < T ? min(r0 + 31, row_hi) / BN - it.n_lo : 0;

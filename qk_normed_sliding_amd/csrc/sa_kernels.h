@@ -19,8 +19,10 @@ struct FwdParams {
   float c1;              // softmax_scale * log2(e): logits in the base-2 domain
   float c2;              // fixed row maximum (base 2) when the logits are bounded
   float eps;
-  int nqb;               // number of 128-row query blocks
+  int nqb;               // number of query blocks (128 rows; 256 with pair_rows)
   int nsub;              // workgroups per (batch, KV head, query block) = G / heads-per-workgroup
+  int pair_rows;         // two-group kernels: 0 = the two warp groups take the same 128 rows of two
+                         // query heads; 1 = they take alternate 32-row slices of 256 rows of one head (odd G)
   int Tp;                // T rounded up to a multiple of 64 (key axis of vt)
   int nwg;               // workgroups of a persistent launch (one per compute unit)
 };
@@ -52,8 +54,9 @@ struct BwdParams {
   float scale;
   float c1;       // scale * log2(e)
   float eps;
-  int nqb;        // number of 128-row query blocks (dQ kernel)
+  int nqb;        // number of query blocks (dQ kernel; 128 rows, 256 with pair_rows)
   int nsub;       // dQ workgroups per (batch, KV head, query block)
+  int pair_rows;  // as in FwdParams
   int nkb;        // number of 128-key blocks (dK/dV kernel)
   int nwg;        // workgroups of a persistent launch (one per compute unit)
 };
@@ -75,14 +78,10 @@ struct TimingEvents {
 // Launchers return the first HIP error seen (hipGetLastError() after the launches).
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, bool fixed_max,
                       hipStream_t stream, const TimingEvents& ev);
-// Two-warp-group forward for an even query-heads-per-KV-head ratio with bounded logits.
+// Two-warp-group forward with bounded logits (any query-heads-per-KV-head ratio; p.pair_rows for odd ones).
 hipError_t launch_fwd_pp(const FwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
-hipError_t launch_bwd(const BwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, hipStream_t stream,
-                      const TimingEvents& dq_ev, const TimingEvents& kv_ev);
-// Two-warp-group dQ kernel for an even query-heads-per-KV-head ratio (reads p.khat).
+// Two-warp-group dQ kernel (reads p.khat; p.pair_rows for an odd query-heads-per-KV-head ratio).
 hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
-hipError_t launch_bwd_dkdv(const BwdParams& p, int head_dim, bool qk_norm, hipStream_t stream,
-                           const TimingEvents& kv_ev);
 // dK/dV kernel whose two warp groups (per-key state split by role) alternate on the matrix cores
 // (any query-heads-per-KV-head ratio).
 hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);

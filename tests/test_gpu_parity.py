@@ -39,8 +39,15 @@ CASES = [
     # B, T, Hq, Hkv, D, W, qk_norm, scale (None = 1/sqrt(D))
     (2, 300, 4, 2, 128, -1, True, None),
     (2, 300, 4, 2, 128, 100, True, None),
-    (1, 513, 6, 3, 128, 256, True, None),     # G = 3: one head per workgroup
+    (1, 513, 6, 3, 128, 256, True, None),     # G = 2, ragged tail
+    (1, 513, 6, 2, 128, 256, True, None),     # G = 3: odd ratio, 256-row items of one head
+    (1, 100, 3, 1, 64, 40, True, None),       # G = 3, one item shorter than its first 128 rows
     (1, 257, 2, 2, 64, 64, True, None),       # MHA, D = 64
+    (2, 600, 6, 6, 128, -1, True, None),      # MHA, D = 128 (the pages' head layout), full causal
+    (1, 777, 6, 6, 128, 300, True, None),     # MHA, sliding window, ragged tail
+    (1, 129, 1, 1, 128, -1, True, None),      # MHA, the second group's rows past T
+    (1, 1, 1, 1, 64, -1, True, None),         # MHA, single position
+    (1, 300, 2, 2, 128, -1, False, None),     # MHA without QK-norm
     (1, 130, 4, 1, 64, 0, True, None),        # window 0: self only
     (1, 1, 2, 1, 128, -1, True, None),        # single position
     (1, 2, 2, 1, 64, -1, True, None),
@@ -70,13 +77,17 @@ def test_small_forward_backward(sa, case):
     compare_backward(dq, dk, dv, q, k, v, do, W, scale, qk_norm)
 
 
-@pytest.mark.parametrize("W", [-1, 0, 1, 63, 64, 127, 128, 129, 1000, 1024, 2046])
-def test_band_mask_bit_exact(sa, W):
+MASK_CASES = [(W, 2, 1) for W in (-1, 0, 1, 63, 64, 127, 128, 129, 1000, 1024, 2046)] + \
+             [(W, 1, 1) for W in (-1, 0, 63, 128, 255, 256, 1024)]  # MHA: 256-row items
+
+
+@pytest.mark.parametrize("W,Hq,Hkv", MASK_CASES, ids=[f"W{c[0]}Hq{c[1]}Hkv{c[2]}" for c in MASK_CASES])
+def test_band_mask_bit_exact(sa, W, Hq, Hkv):
     """Probe: q rows along e0 and k rows along e1 give all-zero logits, so every
     visible key gets the same weight. Batch b carries one-hot values on keys
     128b .. 128b+127 (channel = key mod 128), so O[b, i, h, c] > 0 exactly when
     key 128b + c is visible to query i. exp(LSE_i) counts the visible keys."""
-    B, T, Hq, Hkv, D = 16, 2048, 2, 1, 128
+    B, T, D = 16, 2048, 128
     q = torch.zeros(B, T, Hq, D, dtype=torch.bfloat16)
     k = torch.zeros(B, T, Hkv, D, dtype=torch.bfloat16)
     q[..., 0] = 1.0
@@ -219,6 +230,8 @@ PERSIST_CASES = [
     (4, 50, 4, 2, 128, -1, 2),      # single-tile items back to back
     (2, 333, 12, 2, 64, 40, 4),     # G = 6: three head pairs per KV head
     (2, 260, 4, 2, 64, 0, 3),
+    (2, 700, 6, 6, 128, 256, 3),    # MHA: 256-row items of one head
+    (3, 390, 3, 1, 64, -1, 2),      # G = 3
 ]
 
 
