@@ -52,6 +52,7 @@ class Workload:
     scaled_row_frac: float = 0.0  # fraction of head rows multiplied by scaled_row_factor
     scaled_row_factor: float = 1.0
     eps: float = EPS
+    chunked: bool = False  # draw each tensor one batch row at a time (same generator, in order)
     notes: str = field(default="", compare=False)
 
     @property
@@ -71,6 +72,10 @@ WORKLOADS = {
                 (1024, 1024, 1024, -1, 1024, 1024, 1024, -1), True),
     5: Workload(5, "sssl8_long_fwdbwd_B4_T8192_Hq6_Hkv3_D128_rows10pct_x8", 4, 8192, 6, 3, 128,
                 (4096, 4096, 4096, -1, 4096, 4096, 4096, -1), True, 0.10, 8.0),
+    # the pages' own model shape: multi-head attention (n_kv_head = n_head = 6,
+    # head_dim 128) at device batch 128, sequence 2048, SSSL pattern
+    6: Workload(6, "sssl8_mha_fwdbwd_B128_T2048_Hq6_Hkv6_D128", 128, 2048, 6, 6, 128,
+                (1024, 1024, 1024, -1, 1024, 1024, 1024, -1), True, chunked=True),
 }
 
 
@@ -78,9 +83,15 @@ def seed_for(cfg: int, layer: int, t: int) -> int:
     return SEED_BASE + 1000 * cfg + 10 * layer + t
 
 
-def _randn_bf16(shape, seed: int) -> torch.Tensor:
+def _randn_bf16(shape, seed: int, chunked: bool = False) -> torch.Tensor:
     g = torch.Generator().manual_seed(seed)
-    return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    if not chunked:
+        return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    # one leading index at a time from the same generator: no full-size fp32 temporary
+    out = torch.empty(shape, dtype=torch.bfloat16)
+    for i in range(shape[0]):
+        out[i] = torch.randn(shape[1:], generator=g, dtype=torch.float32)
+    return out
 
 
 def _row_mask(shape_rows, frac: float, seed: int) -> torch.Tensor:
@@ -88,12 +99,12 @@ def _row_mask(shape_rows, frac: float, seed: int) -> torch.Tensor:
     return torch.rand(shape_rows, generator=g, dtype=torch.float32) < frac
 
 
-def random_qkvdo(B, T, Hq, Hkv, D, seed_q, seed_k, seed_v, seed_do, with_do=True):
+def random_qkvdo(B, T, Hq, Hkv, D, seed_q, seed_k, seed_v, seed_do, with_do=True, chunked=False):
     """bf16 CPU tensors q [B,T,Hq,D], k/v [B,T,Hkv,D], dO [B,T,Hq,D] (or None)."""
-    q = _randn_bf16((B, T, Hq, D), seed_q)
-    k = _randn_bf16((B, T, Hkv, D), seed_k)
-    v = _randn_bf16((B, T, Hkv, D), seed_v)
-    do = _randn_bf16((B, T, Hq, D), seed_do) if with_do else None
+    q = _randn_bf16((B, T, Hq, D), seed_q, chunked)
+    k = _randn_bf16((B, T, Hkv, D), seed_k, chunked)
+    v = _randn_bf16((B, T, Hkv, D), seed_v, chunked)
+    do = _randn_bf16((B, T, Hq, D), seed_do, chunked) if with_do else None
     return q, k, v, do
 
 
@@ -106,7 +117,8 @@ def layer_inputs(w: Workload, layer: int, qk_rows_only: bool = False):
     q and k only (a variant used beside the literal reading).
     """
     s = [seed_for(w.cfg, layer, t) for t in range(8)]
-    q, k, v, do = random_qkvdo(w.B, w.T, w.Hq, w.Hkv, w.D, s[0], s[1], s[2], s[3], with_do=w.backward)
+    q, k, v, do = random_qkvdo(w.B, w.T, w.Hq, w.Hkv, w.D, s[0], s[1], s[2], s[3], with_do=w.backward,
+                               chunked=w.chunked)
     if w.scaled_row_frac > 0:
         f = w.scaled_row_factor
         tensors = [q, k] if qk_rows_only else [q, k, v, do]

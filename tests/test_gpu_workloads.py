@@ -90,3 +90,15 @@ def test_long_context_qk_rows_only(sa):
     q, k, v, do = synth.layer_inputs(w, 6, qk_rows_only=True)
     out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[6], w.scale, eps=w.eps)
     _check_slices(w, 6, q, k, v, do, out, [(2, 2)])
+
+
+@pytest.mark.parametrize("layer", [0, 3])
+def test_mha_model_shape_workload(sa, layer):
+    """The pages' own model shape (MHA, n_head = n_kv_head = 6, device batch
+    128): one sliding and one full-causal layer at full size, each slice
+    (batch row, head) compared with the oracle."""
+    w = synth.WORKLOADS[6]
+    log(f"[workload 6] {w.name} layer {layer}")
+    q, k, v, do = synth.layer_inputs(w, layer)
+    out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[layer], w.scale, eps=w.eps)
+    _check_slices(w, layer, q, k, v, do, out, [(0, 0), (w.B - 1, w.Hkv - 1), (61 + layer, 2 + layer % 3)])
