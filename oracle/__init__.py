@@ -15,5 +15,9 @@ from .attention import (  # noqa: F401
     qknorm,
     rms_norm,
     rms_norm_backward,
+    rope_angles,
+    rope_rotate,
+    rope_rotate_back,
+    rope_tables,
     sssl_windows,
 )

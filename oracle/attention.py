@@ -17,6 +17,8 @@ fusion and no rounding:
      W = -1 (full causal)
   5. softmax over the band, O_i = sum_j P_ij v_j, LSE_i = log sum_j exp(S_ij)
   6. backward of 1-5 with respect to the raw q, k, v
+  optional: the rotary position embedding of q and k rows (tables of cos and
+  sin given per position), applied before step 1
 
 Sources (cited by page title and section):
   [post]   The social post that walks through autoresearch's train.py
@@ -39,7 +41,13 @@ Readings where the pages are silent (each one is listed in the design notes):
   - GQA map: contiguous groups, h -> floor(h / G);
   - no attention-logit softcap, no dropout, no document mask;
   - LSE in natural log; gradients are with respect to the raw (un-normed)
-    q and k.
+    q and k;
+  - rotary embedding ([guide] 8.2.1 lists precomputed rotary tables and no
+    formula): dimension i < D/2 pairs with i + D/2 and both turn by the angle
+    theta[t, i] of the row's position t, taken from caller-given cos/sin
+    tables; the default tables use theta[t, i] = t * 10000^(-2i/D). The
+    rotation is applied to q and k before their norm (it preserves each
+    row's length, so the two commute).
 
 Every helper below is a module attribute so a test can replace one with a
 planted mistake and show that the pins catch it.
@@ -121,6 +129,49 @@ def rms_norm_backward(x_hat: torch.Tensor, r: torch.Tensor, dx_hat: torch.Tensor
     return r * (dx_hat - x_hat * (dx_hat * x_hat).sum(dim=-1, keepdim=True) / D)
 
 
+# ---------------------------------------------------------------- rotary embedding
+
+def rope_angles(T: int, D: int, base: float = 10000.0) -> torch.Tensor:
+    """[T, D/2] float64 angles theta[t, i] = t * base^(-2i/D).
+
+    [guide] 8.2.1 (rotary embeddings, precomputed tables); the frequency
+    ladder is the reading listed in the module docstring.
+    """
+    t = torch.arange(T, dtype=F64).view(T, 1)
+    i = torch.arange(D // 2, dtype=F64).view(1, D // 2)
+    return t * torch.pow(torch.tensor(base, dtype=F64), -2.0 * i / D)
+
+
+def rope_tables(T: int, D: int, base: float = 10000.0):
+    """(cos, sin) [T, D/2] float64 of rope_angles."""
+    a = rope_angles(T, D, base)
+    return torch.cos(a), torch.sin(a)
+
+
+def rope_rotate(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor) -> torch.Tensor:
+    """Rotary embedding of x [B, T, H, D]: row (b, t, h) turns each pair
+    (x_i, x_{i+D/2}) by the angle of table row t:
+      y_i = x_i cos - x_{i+D/2} sin,   y_{i+D/2} = x_i sin + x_{i+D/2} cos.
+    cos and sin have at least T rows of D/2 entries.
+    """
+    x = x.to(F64)
+    T, D = x.shape[1], x.shape[-1]
+    c = cos[:T].to(F64).view(1, T, 1, D // 2)
+    s = sin[:T].to(F64).view(1, T, 1, D // 2)
+    x1, x2 = x[..., : D // 2], x[..., D // 2:]
+    return torch.cat([x1 * c - x2 * s, x1 * s + x2 * c], dim=-1)
+
+
+def rope_rotate_back(y: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor) -> torch.Tensor:
+    """Transpose (inverse) of rope_rotate: the gradient map of the rotation."""
+    y = y.to(F64)
+    T, D = y.shape[1], y.shape[-1]
+    c = cos[:T].to(F64).view(1, T, 1, D // 2)
+    s = sin[:T].to(F64).view(1, T, 1, D // 2)
+    y1, y2 = y[..., : D // 2], y[..., D // 2:]
+    return torch.cat([y1 * c + y2 * s, -y1 * s + y2 * c], dim=-1)
+
+
 # ---------------------------------------------------------------- heads
 
 def kv_head(h: int, Hq: int, Hkv: int) -> int:
@@ -141,7 +192,10 @@ def _check_shapes(q, k, v):
     return B, T, Hq, Hkv, D
 
 
-def _normed(q, k, qk_norm, eps):
+def _normed(q, k, qk_norm, eps, rope=None):
+    if rope is not None:
+        q = rope_rotate(q, *rope)
+        k = rope_rotate(k, *rope)
     if qk_norm:
         q_hat, r_q = rms_norm(q, eps)
         k_hat, r_k = rms_norm(k, eps)
@@ -165,10 +219,10 @@ def _probs_one_head(q_hat_bh, k_hat_bg, mask, scale):
 
 # ---------------------------------------------------------------- forward
 
-def attention_probs(q, k, window, scale, qk_norm=True, eps=1e-6):
+def attention_probs(q, k, window, scale, qk_norm=True, eps=1e-6, rope=None):
     """Softmax probabilities P [B, Hq, T, T] (zero outside the band)."""
     B, T, Hq, Hkv, D = _check_shapes(q, k, k)
-    q_hat, _, k_hat, _ = _normed(q, k, qk_norm, eps)
+    q_hat, _, k_hat, _ = _normed(q, k, qk_norm, eps, rope)
     mask = band_mask(T, window)
     P = torch.zeros(B, Hq, T, T, dtype=F64)
     for b in range(B):
@@ -178,13 +232,14 @@ def attention_probs(q, k, window, scale, qk_norm=True, eps=1e-6):
     return P
 
 
-def attn_forward(q, k, v, window, scale, qk_norm=True, eps=1e-6):
+def attn_forward(q, k, v, window, scale, qk_norm=True, eps=1e-6, rope=None):
     """Forward of the layer: returns (o [B,T,Hq,D], lse [B,Hq,T]) in float64.
 
-    q [B,T,Hq,D], k and v [B,T,Hkv,D] (any float dtype; upcast exactly).
+    q [B,T,Hq,D], k and v [B,T,Hkv,D] (any float dtype; upcast exactly);
+    rope = (cos, sin) tables turn q and k rows first (rope_rotate).
     """
     B, T, Hq, Hkv, D = _check_shapes(q, k, v)
-    q_hat, _, k_hat, _ = _normed(q, k, qk_norm, eps)
+    q_hat, _, k_hat, _ = _normed(q, k, qk_norm, eps, rope)
     v = v.to(F64)
     mask = band_mask(T, window)
     o = torch.zeros(B, T, Hq, D, dtype=F64)
@@ -199,7 +254,7 @@ def attn_forward(q, k, v, window, scale, qk_norm=True, eps=1e-6):
 
 # ---------------------------------------------------------------- backward
 
-def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6):
+def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6, rope=None):
     """Gradients (dq, dk, dv) of <O, dO> with respect to the raw q, k, v (float64).
 
     Per (b, h) with g its KV head:
@@ -209,10 +264,11 @@ def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6):
       dS      = P * (dP - Delta)
       dq_hat  = scale * dS K_hat_g
       dk_hat_g += scale * dS^T Q_hat
-    then the RMS-norm backward maps dq_hat, dk_hat to dq, dk.
+    then the RMS-norm backward maps dq_hat, dk_hat to the gradients of the
+    rotated rows, and (with rope) the transposed rotation to dq, dk.
     """
     B, T, Hq, Hkv, D = _check_shapes(q, k, v)
-    q_hat, r_q, k_hat, r_k = _normed(q, k, qk_norm, eps)
+    q_hat, r_q, k_hat, r_k = _normed(q, k, qk_norm, eps, rope)
     v = v.to(F64)
     do = do.to(F64)
     mask = band_mask(T, window)
@@ -235,6 +291,9 @@ def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6):
         dk = rms_norm_backward(k_hat, r_k, dk_hat)
     else:
         dq, dk = dq_hat, dk_hat
+    if rope is not None:
+        dq = rope_rotate_back(dq, *rope)
+        dk = rope_rotate_back(dk, *rope)
     return dq, dk, dv
 
 

@@ -325,6 +325,121 @@ def test_delta_identity():
     assert torch.allclose(oracle.attn_backward_delta(o, do), (P * dP).sum(-1), atol=1e-13)
 
 
+# ------------------------------------------------------------------ rotary embedding
+
+def _lib_rope(x, theta):
+    """Rotary embedding by complex multiplication (torch.polar): the pair
+    (x_i, x_{i+D/2}) as the complex number x_i + 1j x_{i+D/2}, times e^{1j theta[t, i]}."""
+    T, D = x.shape[1], x.shape[-1]
+    z = torch.complex(x[..., : D // 2].contiguous(), x[..., D // 2:].contiguous())
+    w = torch.polar(torch.ones_like(theta[:T]), theta[:T]).view(1, T, 1, D // 2)
+    y = z * w
+    return torch.cat([y.real, y.imag], dim=-1)
+
+
+def test_rope_angles_geometric_ladder():
+    """theta[t, i] = t * base^(-2i/D): row 1 is torch.logspace from 1 down to
+    base^(-(D-2)/D), and every row t is t times row 1."""
+    for D, base in ((16, 10000.0), (128, 10000.0), (8, 500.0)):
+        th = oracle.rope_angles(7, D, base)
+        ladder = torch.logspace(0.0, -(D - 2) / D, D // 2, base=base, dtype=F64)
+        assert torch.allclose(th[1], ladder, rtol=1e-14, atol=0)
+        assert torch.equal(th[0], torch.zeros(D // 2, dtype=F64))
+        assert torch.allclose(th, torch.arange(7, dtype=F64).view(7, 1) * ladder, rtol=1e-14, atol=0)
+
+
+def test_rope_rotation_is_complex_multiplication():
+    x = _rand((2, 9, 3, 16), 80)
+    theta = oracle.rope_angles(12, 16)
+    cos, sin = oracle.rope_tables(12, 16)
+    assert torch.allclose(oracle.rope_rotate(x, cos, sin), _lib_rope(x, theta), atol=1e-14)
+
+
+def test_rope_preserves_norm_and_inverts():
+    x = _rand((1, 11, 2, 32), 81, scale=3.0)
+    cos, sin = oracle.rope_tables(11, 32)
+    y = oracle.rope_rotate(x, cos, sin)
+    assert torch.allclose(y.norm(dim=-1), x.norm(dim=-1), rtol=1e-14)
+    assert torch.allclose(oracle.rope_rotate_back(y, cos, sin), x, atol=1e-14)
+    assert torch.equal(y[:, 0], x[:, 0])  # position 0 turns by zero
+
+
+def test_rope_scores_depend_on_offset_only():
+    """<R_m q, R_n k> = <R_{m+s} q, R_{n+s} k>: the logit sees only m - n."""
+    D, T = 16, 40
+    cos, sin = oracle.rope_tables(T, D)
+    q1, k1 = _rand((D,), 82), _rand((D,), 83)
+    q = torch.zeros(1, T, 1, D, dtype=F64)
+    k = torch.zeros(1, T, 1, D, dtype=F64)
+    q[0, :, 0] = q1
+    k[0, :, 0] = k1
+    qr, kr = oracle.rope_rotate(q, cos, sin)[0, :, 0], oracle.rope_rotate(k, cos, sin)[0, :, 0]
+    for m, n, sft in ((5, 2, 7), (3, 3, 30), (10, 0, 19), (0, 9, 11)):
+        assert abs(float(qr[m] @ kr[n]) - float(qr[m + sft] @ kr[n + sft])) < 1e-12
+    assert abs(float(qr[4] @ kr[1]) - float(qr[3] @ kr[1])) > 1e-3  # and it does see the offset
+
+
+def test_rope_commutes_with_the_weightless_norm():
+    x = _rand((2, 13, 3, 16), 84, scale=2.0)
+    cos, sin = oracle.rope_tables(13, 16)
+    a = oracle.rms_norm(oracle.rope_rotate(x, cos, sin), 1e-6)[0]
+    b = oracle.rope_rotate(oracle.rms_norm(x, 1e-6)[0], cos, sin)
+    assert torch.allclose(a, b, atol=1e-14)
+
+
+ROPE_CASES = [
+    # B, T, Hq, Hkv, D, W, qk_norm
+    (2, 21, 6, 3, 16, -1, True),
+    (1, 21, 4, 4, 8, 5, True),
+    (1, 21, 4, 2, 16, 0, True),
+    (1, 21, 4, 2, 8, 7, False),
+]
+
+
+def _rope_err(case, seed=90, scale=0.4):
+    B, T, Hq, Hkv, D, W, qk_norm = case
+    q, k, v, do = (_rand((B, T, Hq, D), seed), _rand((B, T, Hkv, D), seed + 1),
+                   _rand((B, T, Hkv, D), seed + 2), _rand((B, T, Hq, D), seed + 3))
+    theta = oracle.rope_angles(T + 5, D)  # longer table than T: rows 0 .. T-1 are used
+    rope = (torch.cos(theta), torch.sin(theta))
+    o, lse = oracle.attn_forward(q, k, v, W, scale, qk_norm=qk_norm, rope=rope)
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    o_ref, lse_ref = _lib_forward(_lib_rope(qa, theta), _lib_rope(ka, theta), va, W, scale, qk_norm=qk_norm)
+    gq, gk, gv = torch.autograd.grad(o_ref, (qa, ka, va), do)
+    dq, dk, dv = oracle.attn_backward(q, k, v, do, W, scale, qk_norm=qk_norm, rope=rope)
+    return max(float((o - o_ref).abs().max()), float((lse - lse_ref).abs().max()),
+               float((dq - gq).abs().max()), float((dk - gk).abs().max()), float((dv - gv).abs().max()))
+
+
+@pytest.mark.parametrize("case", ROPE_CASES)
+def test_rope_attention_matches_library_forward_and_autograd(case):
+    assert _rope_err(case) < 1e-11
+
+
+def test_rope_backward_central_finite_differences():
+    B, T, Hq, Hkv, D, W, scale, h = 1, 6, 2, 1, 8, 3, 0.35, 1e-6
+    q, k, v, do = (_rand((B, T, Hq, D), 95), _rand((B, T, Hkv, D), 96), _rand((B, T, Hkv, D), 97),
+                   _rand((B, T, Hq, D), 98))
+    rope = oracle.rope_tables(T, D, base=30.0)  # fast-turning table: large angles at small T
+    grads = oracle.attn_backward(q, k, v, do, W, scale, rope=rope)
+
+    def loss():
+        return float((oracle.attn_forward(q, k, v, W, scale, rope=rope)[0] * do).sum())
+
+    for idx, (x, g) in enumerate(zip((q, k), grads[:2])):
+        fd = torch.zeros_like(x)
+        flat, fdf = x.view(-1), fd.view(-1)
+        for e in range(flat.numel()):
+            old = float(flat[e])
+            flat[e] = old + h
+            lp = loss()
+            flat[e] = old - h
+            lm = loss()
+            flat[e] = old
+            fdf[e] = (lp - lm) / (2 * h)
+        assert float((fd - g).norm() / g.norm()) < 1e-6, idx
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 def _all_pins_pass():
@@ -339,6 +454,8 @@ def _all_pins_pass():
                 return False
     x = _rand((2, 3, 8), 3)
     if not torch.allclose(OA.rms_norm(x, 0.1)[0], F.rms_norm(x, (8,), eps=0.1), atol=1e-14):
+        return False
+    if _rope_err(ROPE_CASES[0]) > 1e-11 or _rope_err(ROPE_CASES[1]) > 1e-11:
         return False
     return True
 
@@ -370,6 +487,19 @@ def _mut_rms_norm_backward(x_hat, r, dx_hat):
     return r * dx_hat  # projection term dropped
 
 
+def _mut_rope_rotate(x, cos, sin):
+    x = x.to(F64)
+    T, D = x.shape[1], x.shape[-1]
+    c = cos[:T].to(F64).view(1, T, 1, D // 2)
+    s = sin[:T].to(F64).view(1, T, 1, D // 2)
+    x1, x2 = x[..., : D // 2], x[..., D // 2:]
+    return torch.cat([x1 * c + x2 * s, -x1 * s + x2 * c], dim=-1)  # turns the other way
+
+
+def _mut_rope_rotate_back(y, cos, sin):
+    return OA.rope_rotate(y, cos, sin)  # the rotation instead of its transpose
+
+
 def _mut_probs(q_hat_bh, k_hat_bg, mask, scale):
     return OA.__dict__["_real_probs"](q_hat_bh, k_hat_bg, mask, scale * scale)  # scale applied twice
 
@@ -380,6 +510,8 @@ def _mut_probs(q_hat_bh, k_hat_bg, mask, scale):
     ("rms_norm", _mut_rms_norm),
     ("rms_norm_backward", _mut_rms_norm_backward),
     ("_probs_one_head", _mut_probs),
+    ("rope_rotate", _mut_rope_rotate),
+    ("rope_rotate_back", _mut_rope_rotate_back),
 ])
 def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
     monkeypatch.setitem(OA.__dict__, "_real_probs", OA._probs_one_head)
