@@ -118,8 +118,8 @@ size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
  *   Two kernels, no atomics: a dQ kernel per query block (it also writes the
  *   normed q rows and Delta into the workspace) and a dK/dV kernel per key
  *   block; the GQA sums over the query heads of a group happen inside the
- *   dK/dV kernel. With an even number of query heads per KV head a norm
- *   pass first writes the normed k rows into the workspace for the dQ kernel.
+ *   dK/dV kernel. With qk_norm a norm pass first writes the normed k rows
+ *   into the workspace for both kernels.
  *   q, k, v, o, lse, dout : inputs (o and lse as written by sa_attn_fwd).
  *   dq, dk, dv            : bf16 outputs, fully overwritten.
  *   workspace             : device buffer of at least
@@ -135,6 +135,43 @@ sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes,
                       int B, int T, int Hq, int Hkv, int head_dim, int window,
                       float softmax_scale, int qk_norm, float eps, void* stream);
+
+/*
+ * sa_attn_fwd_rope / sa_attn_bwd_rope - sa_attn_fwd / sa_attn_bwd with the
+ * rotary position embedding of q and k fused into the kernels.
+ *   [guide] 8.2.1 lists rotary embeddings built from precomputed tables and
+ *   gives no formula; the standard rotary embedding is taken. Every q and k
+ *   head row at position t turns each pair of dimensions (i, i + D/2),
+ *   i < D/2, by the angle whose cosine and sine the tables hold:
+ *     c = rope_cos[t * rope_stride + i], s = rope_sin[t * rope_stride + i],
+ *     y_i = x_i c - x_{i+D/2} s,   y_{i+D/2} = x_i s + x_{i+D/2} c,
+ *   and the RMS norm follows (the turn keeps each row's length, so the order
+ *   does not change the result). Outputs and lse are those of sa_attn_fwd on
+ *   the turned rows; the gradients are with respect to the raw (unturned,
+ *   un-normed) q and k. The usual tables hold cos and sin of
+ *   t * 10000^(-2i/D).
+ *   rope_cos, rope_sin : fp32 DEVICE tables, read only, 16-byte aligned, at
+ *                        least T rows of head_dim/2 entries at a row stride
+ *                        of rope_stride floats (rope_stride >= head_dim/2, a
+ *                        multiple of 4). The backward must get the same tables
+ *                        as the forward.
+ *   Other arguments, workspaces and outputs as for sa_attn_fwd / sa_attn_bwd.
+ *   Additional errors: SA_ERR_NULL for a NULL table, SA_ERR_SHAPE for a bad
+ *   stride, SA_ERR_ALIGN for a misaligned table, SA_ERR_UNSUPPORTED when
+ *   qk_norm == 0, or (forward) when |softmax_scale| * head_dim is too large
+ *   for the kernels' fixed row maximum.
+ */
+sa_status sa_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           int B, int T, int Hq, int Hkv, int head_dim, int window,
+                           float softmax_scale, int qk_norm, float eps,
+                           const float* rope_cos, const float* rope_sin, int rope_stride, void* stream);
+sa_status sa_attn_bwd_rope(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes,
+                           int B, int T, int Hq, int Hkv, int head_dim, int window,
+                           float softmax_scale, int qk_norm, float eps,
+                           const float* rope_cos, const float* rope_sin, int rope_stride, void* stream);
 
 /* Kernels that sa_set_timing_events can bracket. */
 enum { SA_KERNEL_FWD = 0, SA_KERNEL_BWD_DQ = 1, SA_KERNEL_BWD_DKDV = 2 };

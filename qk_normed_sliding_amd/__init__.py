@@ -11,7 +11,8 @@ Entry points (same names as the C ABI):
   sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None, workspace=None)
   sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim)
   sa_attn_bwd(q, k, v, o, lse, dout, window=-1, ..., dq=None, dk=None, dv=None, workspace=None)
-Helpers: attention(...) (autograd), sssl_windows(n_layer, T, pattern).
+  sa_attn_fwd_rope(q, k, v, rope_cos, rope_sin, ...), sa_attn_bwd_rope(..., rope_cos, rope_sin, ...)
+Helpers: attention(...) (autograd), sssl_windows(n_layer, T, pattern), rope_tables(T, D).
 """
 
 from __future__ import annotations
@@ -26,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa_attn.so")
 
 SA_OK = 0
-ABI_VERSION = 2
+ABI_VERSION = 3
 SA_KERNEL_FWD = 0
 SA_KERNEL_BWD_DQ = 1
 SA_KERNEL_BWD_DKDV = 2
@@ -62,6 +63,12 @@ def _load():
     lib.sa_attn_bwd.restype = i32
     lib.sa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                 i32, i32, i32, i32, i32, i32, f32, i32, f32, vp]
+    lib.sa_attn_fwd_rope.restype = i32
+    lib.sa_attn_fwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, f32, i32, f32,
+                                     vp, vp, i32, vp]
+    lib.sa_attn_bwd_rope.restype = i32
+    lib.sa_attn_bwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                     i32, i32, i32, i32, i32, i32, f32, i32, f32, vp, vp, i32, vp]
     lib.sa_set_timing_events.restype = i32
     lib.sa_set_timing_events.argtypes = [i32, vp, vp]
     lib.sa_set_max_workgroups.restype = i32
@@ -144,9 +151,24 @@ def sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim):
     return int(_lib.sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim))
 
 
+def _rope_args(rope_cos, rope_sin, T, D, device):
+    for t, n in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != device or t.dim() != 2:
+            raise SAError(f"{n}: fp32 [rows, >= D/2] tensor on {device} expected")
+        if t.shape[0] < T or t.shape[1] < D // 2 or t.stride(1) != 1:
+            raise SAError(f"{n}: at least T={T} rows of D/2={D // 2} unit-stride entries expected")
+    if rope_cos.stride(0) != rope_sin.stride(0):
+        raise SAError("rope_cos and rope_sin must share a row stride")
+    return _ptr(rope_cos), _ptr(rope_sin), int(rope_cos.stride(0))
+
+
 def sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None,
-                workspace=None, stream=None):
-    """Forward of one layer. q [B,T,Hq,D], k/v [B,T,Hkv,D] bf16. Returns (o, lse)."""
+                workspace=None, stream=None, rope=None):
+    """Forward of one layer. q [B,T,Hq,D], k/v [B,T,Hkv,D] bf16. Returns (o, lse).
+    rope = (cos, sin) rotary tables run sa_attn_fwd_rope instead."""
+    if rope is not None:
+        return sa_attn_fwd_rope(q, k, v, rope[0], rope[1], window, softmax_scale, qk_norm, eps, o, lse,
+                                workspace, stream)
     B, T, Hq, Hkv, D = _dims(q, k)
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16, (B, T, Hkv, D))
@@ -168,13 +190,41 @@ def sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, 
     return o, lse
 
 
+def sa_attn_fwd_rope(q, k, v, rope_cos, rope_sin, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None,
+                     lse=None, workspace=None, stream=None):
+    """Forward with the rotary embedding of q and k fused (fp32 cos/sin tables [>= T, >= D/2])."""
+    B, T, Hq, Hkv, D = _dims(q, k)
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, T, Hkv, D))
+    _need(v, "v", torch.bfloat16, (B, T, Hkv, D))
+    rc, rs, stride = _rope_args(rope_cos, rope_sin, T, D, q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    if workspace is None:
+        workspace = torch.empty(sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check("sa_attn_fwd_rope", _lib.sa_attn_fwd_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+        B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D), int(bool(qk_norm)), float(eps),
+        rc, rs, stride, _stream(q.device, stream)))
+    return o, lse
+
+
 def sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim):
     return int(_lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim))
 
 
 def sa_attn_bwd(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6,
-                dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Backward of one layer. Returns (dq, dk, dv) with respect to the raw q, k, v."""
+                dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None):
+    """Backward of one layer. Returns (dq, dk, dv) with respect to the raw q, k, v.
+    rope = (cos, sin) rotary tables run sa_attn_bwd_rope instead."""
+    if rope is not None:
+        return sa_attn_bwd_rope(q, k, v, o, lse, dout, rope[0], rope[1], window, softmax_scale, qk_norm, eps,
+                                dq, dk, dv, workspace, stream)
     B, T, Hq, Hkv, D = _dims(q, k)
     for t, n, shp in ((q, "q", None), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D)),
                       (o, "o", q.shape), (dout, "dout", q.shape)):
@@ -197,6 +247,31 @@ def sa_attn_bwd(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=Tr
     return dq, dk, dv
 
 
+def sa_attn_bwd_rope(q, k, v, o, lse, dout, rope_cos, rope_sin, window=-1, softmax_scale=None, qk_norm=True,
+                     eps=1e-6, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward with the rotary embedding fused; the same tables as the forward."""
+    B, T, Hq, Hkv, D = _dims(q, k)
+    for t, n, shp in ((q, "q", None), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D)),
+                      (o, "o", q.shape), (dout, "dout", q.shape)):
+        _need(t, n, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    rc, rs, stride = _rope_args(rope_cos, rope_sin, T, D, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, q.shape)
+    _need(dk, "dk", torch.bfloat16, k.shape)
+    _need(dv, "dv", torch.bfloat16, v.shape)
+    if workspace is None:
+        workspace = torch.empty(sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check("sa_attn_bwd_rope", _lib.sa_attn_bwd_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), workspace.numel(), B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D),
+        int(bool(qk_norm)), float(eps), rc, rs, stride, _stream(q.device, stream)))
+    return dq, dk, dv
+
+
 def sa_set_timing_events(kernel, start_event, stop_event):
     """Benchmarking hook: record raw hipEvent_t handles (ints, or None to clear)
     around the main kernel of later calls from this thread."""
@@ -215,23 +290,35 @@ def sa_set_max_workgroups(n):
 
 class _Attention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, window, softmax_scale, qk_norm, eps):
+    def forward(ctx, q, k, v, window, softmax_scale, qk_norm, eps, rope):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, lse = sa_attn_fwd(q, k, v, window, softmax_scale, qk_norm, eps)
+        o, lse = sa_attn_fwd(q, k, v, window, softmax_scale, qk_norm, eps, rope=rope)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.args = (window, softmax_scale, qk_norm, eps)
+        ctx.rope = rope
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = sa_attn_bwd(q, k, v, o, lse, do.contiguous(), *ctx.args)
-        return dq, dk, dv, None, None, None, None
+        dq, dk, dv = sa_attn_bwd(q, k, v, o, lse, do.contiguous(), *ctx.args, rope=ctx.rope)
+        return dq, dk, dv, None, None, None, None, None
 
 
-def attention(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6):
-    """Differentiable layer: o = attention(q, k, v); gradients via sa_attn_bwd."""
-    return _Attention.apply(q, k, v, window, softmax_scale, qk_norm, eps)
+def attention(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, rope=None):
+    """Differentiable layer: o = attention(q, k, v); gradients via sa_attn_bwd.
+    rope = (cos, sin) fp32 device tables (see rope_tables) turns q and k first."""
+    return _Attention.apply(q, k, v, window, softmax_scale, qk_norm, eps, rope)
+
+
+def rope_tables(n_pos: int, head_dim: int, base: float = 10000.0, device=None):
+    """Rotary tables (cos, sin), fp32 [n_pos, head_dim/2], of the angles
+    t * base^(-2i/head_dim) ([guide] 8.2.1: the tables are precomputed once,
+    for more positions than a sequence holds)."""
+    t = torch.arange(n_pos, dtype=torch.float64, device=device).view(n_pos, 1)
+    i = torch.arange(head_dim // 2, dtype=torch.float64, device=device).view(1, head_dim // 2)
+    a = t * torch.pow(torch.tensor(base, dtype=torch.float64, device=device), -2.0 * i / head_dim)
+    return torch.cos(a).float().contiguous(), torch.sin(a).float().contiguous()
 
 
 def sssl_windows(n_layer: int, seq_len: int, pattern: str = "SSSL"):

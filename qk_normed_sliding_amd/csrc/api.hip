@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 // Benchmarking hook: events recorded around the main kernel of later calls
 // made from this host thread (see sa_set_timing_events).
@@ -79,6 +79,19 @@ bool fixed_max_ok(int qk_norm, float scale, int head_dim, float* c2) {
   return qk_norm != 0 && bound <= 32.f;
 }
 
+// Validates optional rotary tables: both or neither pointer, rows of at least
+// head_dim/2 floats at a 16-byte-aligned stride, and only with the QK-norm.
+sa_status check_rope(const float* cos, const float* sin, int stride, int head_dim, int qk_norm, sa::Rope* out) {
+  *out = sa::Rope{nullptr, nullptr, 0};
+  if (cos == nullptr && sin == nullptr) return SA_OK;
+  if (cos == nullptr || sin == nullptr) return SA_ERR_NULL;
+  if (!qk_norm) return SA_ERR_UNSUPPORTED;
+  if (stride < head_dim / 2 || stride % 4 != 0) return SA_ERR_SHAPE;
+  if (!aligned16(cos) || !aligned16(sin)) return SA_ERR_ALIGN;
+  *out = sa::Rope{cos, sin, stride};
+  return SA_OK;
+}
+
 }  // namespace
 
 SA_API int sa_abi_version(void) { return kAbiVersion; }
@@ -115,11 +128,15 @@ SA_API size_t sa_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int hea
   return round256((size_t)B * T * Hkv * head_dim * 2) + round256((size_t)B * Hkv * head_dim * Tp * 2);
 }
 
-SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
-                             size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
-                             float softmax_scale, int qk_norm, float eps, void* stream) {
+static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                          float softmax_scale, int qk_norm, float eps, const float* rope_cos, const float* rope_sin,
+                          int rope_stride, void* stream) {
   const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
   if (st != SA_OK) return st;
+  sa::Rope rope;
+  const sa_status sr = check_rope(rope_cos, rope_sin, rope_stride, head_dim, qk_norm, &rope);
+  if (sr != SA_OK) return sr;
   if (!q || !k || !v || !o || !lse) return SA_ERR_NULL;
   if (qk_norm && (workspace == nullptr || workspace_bytes < sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim) ||
                   ((uintptr_t)workspace & 255u) != 0))
@@ -155,11 +172,13 @@ SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* 
     if (p.nwg <= 0) return SA_ERR_HIP;
     p.khat = workspace;
     p.vt = (char*)workspace + round256((size_t)B * T * Hkv * head_dim * 2);
-    sa::KvPrepParams kp{k, v, (void*)p.khat, (void*)p.vt, B, T, Hkv, p.Tp, eps};
+    p.rope = rope;
+    sa::KvPrepParams kp{k, v, (void*)p.khat, (void*)p.vt, B, T, Hkv, p.Tp, eps, rope};
     if (sa::launch_kv_prep(kp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
     return sa::launch_fwd_pp(p, head_dim, s, tl_events[SA_KERNEL_FWD]) == hipSuccess ? SA_OK : SA_ERR_HIP;
   }
-  // online-softmax kernel (logits without the QK-norm bound)
+  // online-softmax kernel (logits without the QK-norm bound); no rotary tables there
+  if (rope.cos != nullptr) return SA_ERR_UNSUPPORTED;
   const int hpw = (p.G % 2 == 0) ? 2 : 1;
   p.nsub = p.G / hpw;
   p.nqb = (T + 127) / 128;
@@ -176,12 +195,15 @@ SA_API size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int hea
          round256((size_t)B * T * Hkv * head_dim * 2);
 }
 
-SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                             const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                             size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
-                             float softmax_scale, int qk_norm, float eps, void* stream) {
+static sa_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          int B, int T, int Hq, int Hkv, int head_dim, int window, float softmax_scale, int qk_norm,
+                          float eps, const float* rope_cos, const float* rope_sin, int rope_stride, void* stream) {
   const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
   if (st != SA_OK) return st;
+  sa::Rope rope;
+  const sa_status sr = check_rope(rope_cos, rope_sin, rope_stride, head_dim, qk_norm, &rope);
+  if (sr != SA_OK) return sr;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SA_ERR_NULL;
   const size_t need = sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim);
   if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
@@ -223,12 +245,47 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
   if (qk_norm) {
     // normed k rows, copied straight into LDS as tiles by the dQ kernel
     void* khat = (char*)workspace + round256(rows * head_dim * 2) + round256(rows * sizeof(float));
-    sa::NormParams np{k, khat, nullptr, (int64_t)B * T * Hkv, eps};
+    sa::NormParams np{k, khat, nullptr, (int64_t)B * T * Hkv, eps, rope, Hkv, T};
     if (sa::launch_qknorm(np, head_dim, s) != hipSuccess) return SA_ERR_HIP;
     p.khat = khat;
   }
+  p.rope = rope;
   if (sa::launch_bwd_dq_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DQ]) != hipSuccess) return SA_ERR_HIP;
   return sa::launch_bwd_dkdv_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                             float softmax_scale, int qk_norm, float eps, void* stream) {
+  return attn_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window, softmax_scale,
+                  qk_norm, eps, nullptr, nullptr, 0, stream);
+}
+
+SA_API sa_status sa_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                                  size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                                  float softmax_scale, int qk_norm, float eps, const float* rope_cos,
+                                  const float* rope_sin, int rope_stride, void* stream) {
+  if (rope_cos == nullptr || rope_sin == nullptr) return SA_ERR_NULL;
+  return attn_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window, softmax_scale,
+                  qk_norm, eps, rope_cos, rope_sin, rope_stride, stream);
+}
+
+SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                             float softmax_scale, int qk_norm, float eps, void* stream) {
+  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window,
+                  softmax_scale, qk_norm, eps, nullptr, nullptr, 0, stream);
+}
+
+SA_API sa_status sa_attn_bwd_rope(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                  size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                                  float softmax_scale, int qk_norm, float eps, const float* rope_cos,
+                                  const float* rope_sin, int rope_stride, void* stream) {
+  if (rope_cos == nullptr || rope_sin == nullptr) return SA_ERR_NULL;
+  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window,
+                  softmax_scale, qk_norm, eps, rope_cos, rope_sin, rope_stride, stream);
 }
 
 SA_API sa_status sa_set_timing_events(int kernel, void* start, void* stop) {

@@ -119,29 +119,17 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
     }
   };
 
-  // ---- per-key fragments (B operands of S and dP): key l32, head_dim 16kk + 8half
+  // ---- per-key fragments (B operands of S and dP): key l32, head_dim 16kk +
+  // 8half. k_hat comes from the backward's norm pass (turned when rotary
+  // tables are given), the same rows the dQ kernel's S uses.
   bf16x8 kf[KST];  // group A: k_hat;  group B: v
   {
     const long first = ((long)b * T * p.Hkv + g) * D + (long)kb0 * kvstride;
     const uint32_t bytes = (uint32_t)max(0, T - kb0) * kvstride * 2;
-    const auto rk = make_rsrc((const bf16*)(grp == 0 ? p.k : p.v) + first, bytes);
+    const auto rk = make_rsrc((const bf16*)(grp == 0 ? p.khat : p.v) + first, bytes);
     const uint32_t off = (uint32_t)((32 * rw + l32) * kvstride + 8 * half) * 2;
-    float x[KST][8];
-    float ss = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk) {
-      unpack8(bload16(rk, off + 32 * kk), x[kk]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[kk][e] * x[kk][e];
-    }
-    const bool norm_here = grp == 0 && p.qhat != p.q;
-    const float r = norm_here ? fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps) : 1.f;
-#pragma unroll
-    for (int kk = 0; kk < KST; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[kk][e] *= r;
-      kf[kk] = __builtin_bit_cast(bf16x8, pack8(x[kk]));
-    }
+    for (int kk = 0; kk < KST; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, bload16(rk, off + 32 * kk));
   }
 
   // ---- LDS read addresses (bytes): row reads of rows 32qc + swap23(l32),
@@ -337,8 +325,13 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
     return;
   }
   // dk = r (dk_hat - k_hat <dk_hat, k_hat> / D), dk_hat = scale * acc; the
-  // lane pair (l, l^32) holds the whole k row, so r comes from its squares
+  // lane pair (l, l^32) holds the whole k row, so r comes from its squares.
+  // With rotary tables k_hat is the turned row (as the S MFMAs used it) and
+  // the result is turned back; head_dim d < D/2 (block db < NDB/2) pairs with
+  // d + D/2 (block db + NDB/2).
   const bool norm = p.qhat != p.q;
+  const bool rope = p.rope.cos != nullptr;
+  const long tr = (long)key * p.rope.stride + 4 * half;
   float kx[NDB][16];
   float dot = 0.f, ss = 0.f, r_k = 1.f;
   if (norm) {
@@ -352,11 +345,28 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
         kx[db][4 * i + 1] = __uint_as_float(w[0] & 0xffff0000u);
         kx[db][4 * i + 2] = __uint_as_float(w[1] << 16);
         kx[db][4 * i + 3] = __uint_as_float(w[1] & 0xffff0000u);
+      }
+    if (rope) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          ss += kx[db][4 * i + j] * kx[db][4 * i + j];
-          dot += acc[db][4 * i + j] * kx[db][4 * i + j];
+      for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 c = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
+          const f32x4 sn = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float a = kx[db][4 * i + j], bb = kx[db + NDB / 2][4 * i + j];
+            kx[db][4 * i + j] = a * c[j] - bb * sn[j];
+            kx[db + NDB / 2][4 * i + j] = a * sn[j] + bb * c[j];
+          }
         }
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        ss += kx[db][r] * kx[db][r];
+        dot += acc[db][r] * kx[db][r];
       }
     r_k = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps);
     dot = pair_sum(dot) * r_k * p.scale * (1.f / D);  // <dk_hat, k_hat> / D with k_hat = r k
@@ -364,16 +374,32 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[4];
+    for (int r = 0; r < 16; ++r) {
+      const float gh = p.scale * acc[db][r];
+      acc[db][r] = norm ? r_k * (gh - kx[db][r] * r_k * dot) : gh;
+    }
+  if (rope) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float gh = p.scale * acc[db][4 * i + j];
-        v[j] = norm ? r_k * (gh - kx[db][4 * i + j] * r_k * dot) : gh;
+    for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 c = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
+        const f32x4 sn = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = acc[db][4 * i + j], bb = acc[db + NDB / 2][4 * i + j];
+          acc[db][4 * i + j] = a * c[j] + bb * sn[j];
+          acc[db + NDB / 2][4 * i + j] = bb * c[j] - a * sn[j];
+        }
       }
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       u32x2 w;
-      w[0] = pack2(v[0], v[1]);
-      w[1] = pack2(v[2], v[3]);
+      w[0] = pack2(acc[db][4 * i], acc[db][4 * i + 1]);
+      w[1] = pack2(acc[db][4 * i + 2], acc[db][4 * i + 3]);
       *(u32x2*)((bf16*)p.dk + rowoff + 32 * db + 8 * i) = w;
     }
 }

@@ -290,6 +290,14 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
       ss = group_sum<CPR>(ss);
       dd = group_sum<CPR>(dd);
       const float rr = norm ? fast_rsqrt(ss * (1.f / D) + p.eps) : 1.f;
+      if (p.rope.cos != nullptr) {
+        // the partner chunk (other half of the row) is CPR/2 lanes away
+        float fp[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fp[e] = __shfl_xor(f[e], CPR / 2);
+        const long tr = (long)min(r0 + r, T - 1) * p.rope.stride + 8 * (cch % (CPR / 2));
+        rope8(f, fp, p.rope.cos + tr, p.rope.sin + tr, cch >= CPR / 2, false);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= rr;
       const u32x4 w = pack8(f);
@@ -363,7 +371,8 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- epilogue: dq = r (dq_hat - q_hat <dq_hat, q_hat> / D), dq_hat = scale * acc.
+  // ---- epilogue: dq = r (dq_hat - q_hat <dq_hat, q_hat> / D), dq_hat = scale * acc
+  // (with rotary tables q_hat is the turned row and the result is turned back).
   // The accumulator holds head_dim 32db + 8i + 4half + j of this lane's row;
   // q_hat (bf16, as the S MFMAs used it) comes from the operand registers,
   // which hold head_dim 16kk + 8half + e. With i = 2a + c, the element sits in
@@ -403,16 +412,34 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[4];
+    for (int r = 0; r < 16; ++r) {
+      const float gh = p.scale * dq[db][r];
+      dq[db][r] = norm ? r_q * (gh - qx[db][r] * dot) : gh;
+    }
+  if (p.rope.cos != nullptr) {
+    // head_dim d < D/2 (block db < NDB/2) pairs with d + D/2 (block db + NDB/2)
+    const long tr = (long)row * p.rope.stride + 4 * half;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float gh = p.scale * dq[db][4 * i + j];
-        v[j] = norm ? r_q * (gh - qx[db][4 * i + j] * dot) : gh;
+    for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 c = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
+        const f32x4 sn = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = dq[db][4 * i + j], bb = dq[db + NDB / 2][4 * i + j];
+          dq[db][4 * i + j] = a * c[j] + bb * sn[j];
+          dq[db + NDB / 2][4 * i + j] = bb * c[j] - a * sn[j];
+        }
       }
+  }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       u32x2 w;
-      w[0] = pack2(v[0], v[1]);
-      w[1] = pack2(v[2], v[3]);
+      w[0] = pack2(dq[db][4 * i], dq[db][4 * i + 1]);
+      w[1] = pack2(dq[db][4 * i + 2], dq[db][4 * i + 3]);
       *(u32x2*)((bf16*)p.dq + rowoff + 32 * db + 8 * i) = w;
     }
 }

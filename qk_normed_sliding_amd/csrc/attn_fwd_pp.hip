@@ -52,7 +52,7 @@ __device__ __forceinline__ void sched_ring() {
   __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
 }
 
-template <int D, int NB>
+template <int D, int NB, bool ROPE>
 __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   constexpr int BN = 64;              // keys per tile
   constexpr int BM = 128;             // query rows per item (per head)
@@ -219,7 +219,8 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
       dma16(rq, uniform((int)(qn_lds + m * 1024)), off, 0u);
     }
   };
-  auto q_norm = [&](const u32x4 (&x)[KST]) {
+  // row: the lane's query row (its rotary table row when the tables are given)
+  auto q_norm = [&](const u32x4 (&x)[KST], int row) {
     float ss = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
@@ -231,6 +232,31 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
     // q_hat carries the factor c1 = scale * log2(e), so S comes out of the
     // MFMAs already in the base-2 logit domain
     const float r = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps) * p.c1;
+    if constexpr (ROPE) {
+      // head_dim 16kk + 8half + e (kk < KST/2) pairs with the same offset in
+      // chunk kk + KST/2: both halves of a pair are in this lane
+      const long tr = (long)min(row, T - 1) * p.rope.stride + 8 * half;
+#pragma unroll
+      for (int kk = 0; kk < KST / 2; ++kk) {
+        float lo[8], hi[8], lo0[8];
+        unpack8(x[kk], lo);
+        unpack8(x[kk + KST / 2], hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo0[e] = lo[e];
+        const float* c = p.rope.cos + tr + 16 * kk;
+        const float* s = p.rope.sin + tr + 16 * kk;
+        rope8(lo, hi, c, s, false, false);
+        rope8(hi, lo0, c, s, true, false);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          lo[e] *= r;
+          hi[e] *= r;
+        }
+        qf[kk] = __builtin_bit_cast(bf16x8, pack8(lo));
+        qf[kk + KST / 2] = __builtin_bit_cast(bf16x8, pack8(hi));
+      }
+      return;
+    }
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
       float f[8];
@@ -240,12 +266,12 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
       qf[kk] = __builtin_bit_cast(bf16x8, pack8(f));
     }
   };
-  auto q_from_lds = [&]() {
+  auto q_from_lds = [&](int row) {
     u32x4 x[KST];
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk)
       x[kk] = *(SA_LDS const u32x4*)(uintptr_t)(qn_lds + (uint32_t)(l32 * D * 2 + (((2 * kk + half) ^ (l32 % CPR)) << 4)));
-    q_norm(x);
+    q_norm(x, row);
   };
 
   // The operands of an M-phase form one stream of 16-byte LDS reads, each
@@ -398,7 +424,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
     u32x4 x[KST];
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) x[kk] = bload16(rq, off + 32 * kk);
-    q_norm(x);
+    q_norm(x, it.qb * BMI + wrow + l32);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed in LDS
   __syncthreads();
@@ -441,7 +467,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
         if (tau == 0) q_prefetch(item(k + 1));
         if (tau == it.ntile - 1) {
           if (it.ntile == 1) __builtin_amdgcn_s_waitcnt(0);
-          q_from_lds();
+          q_from_lds(item(k + 1).qb * BMI + wrow + l32);
         }
       }
       if (grp == 1 || st >= 1) {
@@ -467,10 +493,18 @@ hipError_t launch_fwd_pp(const FwdParams& p, int head_dim, hipStream_t stream, c
     const hipError_t e = hipEventRecord(ev.start, stream);
     if (e != hipSuccess) return e;
   }
-  if (head_dim == 128)
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<128, NB>), grid, dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_pp_kernel<64, NB>), grid, dim3(512), 0, stream, p);
+  const bool rope = p.rope.cos != nullptr;
+  if (head_dim == 128) {
+    if (rope)
+      hipLaunchKernelGGL((attn_fwd_pp_kernel<128, NB, true>), grid, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_pp_kernel<128, NB, false>), grid, dim3(512), 0, stream, p);
+  } else {
+    if (rope)
+      hipLaunchKernelGGL((attn_fwd_pp_kernel<64, NB, true>), grid, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_pp_kernel<64, NB, false>), grid, dim3(512), 0, stream, p);
+  }
   const hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
   return e;

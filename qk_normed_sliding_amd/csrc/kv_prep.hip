@@ -2,7 +2,9 @@
 // normed once ([post] QK-norm passage; [guide] 8.2.1) and written as k_hat in
 // the layout of k, and the value rows of each (batch, KV head) are written
 // transposed, as v_t[b][g][d][t] with the key axis padded with zeros to a
-// multiple of 64. After it, the attention kernel's key and value tiles are
+// multiple of 64. With rotary tables the key rows are turned first (pairs
+// of dimensions i and i + D/2 by the angle of the row's position; the norm
+// is unchanged by the turn). After it, the attention kernel's key and value tiles are
 // plain copies that go straight from memory into LDS, and both are read
 // there with 16-byte reads (the value operand of P.V runs along keys).
 // HBM-bound: each k and v element is read once and written once.
@@ -38,6 +40,14 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
     const float rs = fast_rsqrt(group_sum<CPR>(ss) * (1.f / D) + p.eps);
+    if (p.rope.cos != nullptr) {
+      // the partner chunk (the other half of the row) is CPR/2 lanes away
+      float xp[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xp[e] = __shfl_xor(x[e], CPR / 2);
+      const long tr = (long)(in ? t : 0) * p.rope.stride + 8 * (sub % (CPR / 2));
+      rope8(x, xp, p.rope.cos + tr, p.rope.sin + tr, sub >= CPR / 2, false);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= rs;
     if (in) st16((bf16*)p.khat + off, pack8(x));

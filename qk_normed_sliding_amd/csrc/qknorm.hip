@@ -3,7 +3,9 @@
 // plus the per-row 1/sqrt(mean(x^2) + eps).
 // Sources: [post] QK-norm passage; [guide] 8.2.1 (RMSNorm via F.rms_norm).
 // HBM-bound: one 16-byte chunk per lane, D/8 lanes per row, the sum of
-// squares reduced across the row's lanes with DPP row operations.
+// squares reduced across the row's lanes with DPP row operations. With
+// rotary tables (internal use: [B, T, H] head rows) each row is also turned
+// by the angles of its position, pairs of dimensions i and i + D/2.
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -21,6 +23,14 @@ __global__ void __launch_bounds__(256) qknorm_kernel(NormParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
     const float r = fast_rsqrt(group_sum<CPR>(ss) * (1.f / D) + p.eps);
+    if (p.rope.cos != nullptr) {
+      float xp[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xp[e] = __shfl_xor(x[e], CPR / 2);
+      const long t = (row / p.H) % p.T;
+      const long tr = t * p.rope.stride + 8 * (sub % (CPR / 2));
+      rope8(x, xp, p.rope.cos + tr, p.rope.sin + tr, sub >= CPR / 2, false);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= r;
     st16((bf16*)p.y + row * D + 8 * sub, pack8(x));

@@ -137,6 +137,26 @@ __device__ __forceinline__ void unpack8(u32x4 w, float* f) {
   }
 }
 
+// Rotary embedding of 8 values x[e] of one row, dimensions i0 + e of the
+// lower half (upper = false) or i0 + D/2 + e of the upper half, given the
+// values xp[e] of the other half's partner dimensions and the table rows
+// c = cos + i0, s = sin + i0 (16-byte aligned): the pair (a, b) = (lower,
+// upper) turns to (a c - b s, a s + b c). With back = true the transposed
+// (inverse) turn: (a c + b s, -a s + b c).
+__device__ __forceinline__ void rope8(float* x, const float* xp, const float* c, const float* s, bool upper,
+                                      bool back) {
+  const f32x4 c0 = *(const f32x4*)c, c1 = *(const f32x4*)(c + 4);
+  const f32x4 s0 = *(const f32x4*)s, s1 = *(const f32x4*)(s + 4);
+  // lower: x c - xp s (back: x c + xp s); upper: x c + xp s (back: x c - xp s)
+  const float sg = (upper != back) ? 1.f : -1.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float ce = e < 4 ? c0[e] : c1[e - 4];
+    const float se = e < 4 ? s0[e] : s1[e - 4];
+    x[e] = __builtin_fmaf(x[e], ce, sg * xp[e] * se);
+  }
+}
+
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   bf16x2 r;
   r[0] = (bf16)a;

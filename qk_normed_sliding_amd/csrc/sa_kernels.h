@@ -6,6 +6,15 @@
 
 namespace sa {
 
+// Rotary embedding tables: fp32, row t (position t) at cos + t * stride and
+// sin + t * stride, head_dim / 2 entries; dimension i < D/2 pairs with
+// i + D/2. cos == nullptr: no rotation.
+struct Rope {
+  const float* cos;
+  const float* sin;
+  int stride;
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -25,6 +34,7 @@ struct FwdParams {
                          // query heads; 1 = they take alternate 32-row slices of 256 rows of one head (odd G)
   int Tp;                // T rounded up to a multiple of 64 (key axis of vt)
   int nwg;               // workgroups of a persistent launch (one per compute unit)
+  Rope rope;             // rotary tables for q (k is turned by the prologue kernel)
 };
 
 struct KvPrepParams {
@@ -34,6 +44,7 @@ struct KvPrepParams {
   void* vt;    // [B, Hkv, D, Tp]
   int B, T, Hkv, Tp;
   float eps;
+  Rope rope;   // rotary tables for k (turned before the norm)
 };
 
 struct BwdParams {
@@ -59,6 +70,7 @@ struct BwdParams {
   int pair_rows;  // as in FwdParams
   int nkb;        // number of 128-key blocks (dK/dV kernel)
   int nwg;        // workgroups of a persistent launch (one per compute unit)
+  Rope rope;      // rotary tables: q_hat is written turned, dq and dk are turned back
 };
 
 struct NormParams {
@@ -67,6 +79,8 @@ struct NormParams {
   float* rstd;
   int64_t rows;
   float eps;
+  Rope rope;   // optional: rows are [B, T, H] head rows, turned by position t = (row / H) % T
+  int H, T;
 };
 
 // Optional events recorded around a call's main kernel (benchmarking hook).

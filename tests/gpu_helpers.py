@@ -53,16 +53,23 @@ def gpu_forward(sa, q, k, v, W, scale, qk_norm=True, eps=1e-6):
     return o, lse
 
 
-def gpu_fwd_bwd(sa, q, k, v, do, W, scale, qk_norm=True, eps=1e-6):
+def gpu_fwd_bwd(sa, q, k, v, do, W, scale, qk_norm=True, eps=1e-6, rope=None):
     qd, kd, vd, dod = to_dev(q, k, v, do)
-    o, lse = sa.sa_attn_fwd(qd, kd, vd, window=W, softmax_scale=scale, qk_norm=qk_norm, eps=eps)
-    dq, dk, dv = sa.sa_attn_bwd(qd, kd, vd, o, lse, dod, window=W, softmax_scale=scale, qk_norm=qk_norm, eps=eps)
+    o, lse = sa.sa_attn_fwd(qd, kd, vd, window=W, softmax_scale=scale, qk_norm=qk_norm, eps=eps, rope=rope)
+    dq, dk, dv = sa.sa_attn_bwd(qd, kd, vd, o, lse, dod, window=W, softmax_scale=scale, qk_norm=qk_norm, eps=eps,
+                                rope=rope)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
 
-def compare_forward(o, lse, q, k, v, W, scale, qk_norm=True, eps=1e-6, o_tol=O_MAX_ABS, lse_tol=LSE_MAX_ABS):
-    o_ref, lse_ref = oracle.attn_forward(q, k, v, W, scale, qk_norm=qk_norm, eps=eps)
+def oracle_rope(rope):
+    """The GPU's fp32 rotary tables as fp64 CPU tensors for the oracle (exact widening)."""
+    return None if rope is None else tuple(t.double().cpu() for t in rope)
+
+
+def compare_forward(o, lse, q, k, v, W, scale, qk_norm=True, eps=1e-6, o_tol=O_MAX_ABS, lse_tol=LSE_MAX_ABS,
+                    rope=None):
+    o_ref, lse_ref = oracle.attn_forward(q, k, v, W, scale, qk_norm=qk_norm, eps=eps, rope=oracle_rope(rope))
     eo, el = max_abs(o.cpu(), o_ref), max_abs(lse.cpu(), lse_ref)
     log(f"  O max-abs {eo:.3e}  LSE max-abs {el:.3e}")
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
@@ -71,8 +78,9 @@ def compare_forward(o, lse, q, k, v, W, scale, qk_norm=True, eps=1e-6, o_tol=O_M
     return o_ref, lse_ref
 
 
-def compare_backward(dq, dk, dv, q, k, v, do, W, scale, qk_norm=True, eps=1e-6, tol=GRAD_REL_L2):
-    dq_r, dk_r, dv_r = oracle.attn_backward(q, k, v, do, W, scale, qk_norm=qk_norm, eps=eps)
+def compare_backward(dq, dk, dv, q, k, v, do, W, scale, qk_norm=True, eps=1e-6, tol=GRAD_REL_L2, rope=None):
+    dq_r, dk_r, dv_r = oracle.attn_backward(q, k, v, do, W, scale, qk_norm=qk_norm, eps=eps,
+                                            rope=oracle_rope(rope))
     errs = {n: rel_l2(a.cpu(), r) for n, a, r in (("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r))}
     log("  rel-L2 " + "  ".join(f"{n} {e:.3e}" for n, e in errs.items()))
     for n, a in (("dq", dq), ("dk", dk), ("dv", dv)):

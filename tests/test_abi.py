@@ -33,7 +33,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("sa_qknorm", "sa_attn_fwd", "sa_attn_fwd_workspace_bytes", "sa_attn_bwd", "sa_attn_bwd_workspace_bytes",
-              "sa_status_string", "sa_abi_version"):
+              "sa_status_string", "sa_abi_version", "sa_attn_fwd_rope", "sa_attn_bwd_rope"):
         assert n in names
 
 
@@ -104,6 +104,38 @@ def test_backward_validation_paths(sa):
     assert _bwd(lib, ws_bytes=16) == SA_ERR_WORKSPACE
     assert _bwd(lib, ws=128) == SA_ERR_WORKSPACE  # not 256-byte aligned
     assert _bwd(lib, dq=8) == SA_ERR_ALIGN
+
+
+def _fwd_rope(lib, cos=1024, sin=2048, stride=64, D=128, norm=1, scale=0.125, q=16, T=8):
+    P = ctypes.c_void_p
+    ws_bytes = lib.sa_attn_fwd_workspace_bytes(1, T, 4, 2, D)
+    return lib.sa_attn_fwd_rope(P(q), P(16), P(16), P(16), P(16), P(256), ws_bytes, 1, T, 4, 2, D, -1, scale, norm,
+                                1e-6, P(cos), P(sin), stride, None)
+
+
+def _bwd_rope(lib, cos=1024, sin=2048, stride=64, D=128, norm=1):
+    P = ctypes.c_void_p
+    need = lib.sa_attn_bwd_workspace_bytes(1, 8, 4, 2, D)
+    return lib.sa_attn_bwd_rope(P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(256), need,
+                                1, 8, 4, 2, D, -1, 0.125, norm, 1e-6, P(cos), P(sin), stride, None)
+
+
+def test_rope_validation_paths(sa):
+    lib = sa.library()
+    for call in (_fwd_rope, _bwd_rope):
+        assert call(lib, cos=0) == SA_ERR_NULL
+        assert call(lib, sin=0) == SA_ERR_NULL
+        assert call(lib, stride=60) == SA_ERR_SHAPE     # fewer than D/2 entries per row
+        assert call(lib, stride=66) == SA_ERR_SHAPE     # rows not 16-byte aligned
+        assert call(lib, D=64, stride=30) == SA_ERR_SHAPE
+        assert call(lib, cos=1028) == SA_ERR_ALIGN
+        assert call(lib, sin=8) == SA_ERR_ALIGN
+        assert call(lib, norm=0) == SA_ERR_UNSUPPORTED  # the fused turn rides on the QK-norm kernels
+        assert call(lib, D=80) == SA_ERR_UNSUPPORTED
+    # the logits of the fixed-maximum kernels must stay bounded
+    assert _fwd_rope(lib, scale=2.0) == SA_ERR_UNSUPPORTED
+    assert _fwd_rope(lib, q=0) == SA_ERR_NULL
+    assert _fwd_rope(lib, T=0) == SA_ERR_SHAPE
 
 
 def test_workspace_size(sa):

@@ -253,3 +253,55 @@ def test_persistent_workgroups_many_items(sa, case):
         sa.sa_set_max_workgroups(0)
     compare_forward(o, lse, q, k, v, W, scale)
     compare_backward(dq, dk, dv, q, k, v, do, W, scale)
+
+
+ROPE_CASES = [
+    # B, T, Hq, Hkv, D, W, table row stride (None = D/2), max workgroups (0 = one per CU)
+    (2, 300, 4, 2, 128, -1, None, 0),
+    (1, 513, 6, 3, 128, 256, 72, 0),     # G = 2, ragged tail, padded table rows
+    (1, 777, 6, 6, 128, 300, None, 0),   # MHA, 256-row items
+    (1, 260, 6, 2, 64, 100, 40, 0),      # G = 3, D = 64
+    (2, 129, 2, 1, 64, 0, None, 0),      # window 0
+    (3, 390, 4, 2, 128, 100, None, 3),   # persistent items back to back (next item's rows turned)
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=[f"B{c[0]}T{c[1]}Hq{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}s{c[6]}wg{c[7]}"
+                                                  for c in ROPE_CASES])
+def test_rope_forward_backward(sa, case):
+    """Rotary embedding fused into the kernels (sa_attn_fwd_rope /
+    sa_attn_bwd_rope) against the oracle given the same table values. The
+    tables hold more rows than T (as the trainer precomputes them for ten
+    sequence lengths) and may have padded rows."""
+    B, T, Hq, Hkv, D, W, stride, nwg = case
+    scale = D ** -0.5
+    log(f"[rope] {case}")
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=700 + T)
+    cos, sin = sa.rope_tables(10 * T, D, device="cuda")
+    if stride is not None:
+        pad_c = torch.zeros(10 * T, stride, dtype=torch.float32, device="cuda")
+        pad_s = torch.zeros_like(pad_c)
+        pad_c[:, : D // 2] = cos
+        pad_s[:, : D // 2] = sin
+        cos, sin = pad_c[:, : D // 2], pad_s[:, : D // 2]
+    rope = (cos, sin)
+    sa.sa_set_max_workgroups(nwg)
+    try:
+        o, lse, dq, dk, dv = gpu_fwd_bwd(sa, q, k, v, do, W, scale, rope=rope)
+    finally:
+        sa.sa_set_max_workgroups(0)
+    compare_forward(o, lse, q, k, v, W, scale, rope=rope)
+    compare_backward(dq, dk, dv, q, k, v, do, W, scale, rope=rope)
+
+
+def test_rope_at_position_zero_only_is_plain_attention(sa):
+    """Tables of angle zero (cos 1, sin 0) turn nothing: the fused path must
+    give the plain path's results bit for bit."""
+    B, T, Hq, Hkv, D, W = 1, 333, 4, 2, 128, 100
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=31)
+    cos = torch.ones(T, D // 2, dtype=torch.float32, device="cuda")
+    sin = torch.zeros(T, D // 2, dtype=torch.float32, device="cuda")
+    a = gpu_fwd_bwd(sa, q, k, v, do, W, D ** -0.5)
+    b = gpu_fwd_bwd(sa, q, k, v, do, W, D ** -0.5, rope=(cos, sin))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -32,7 +32,7 @@ def sa():
     return pkg
 
 
-def _check_slices(w, layer, q, k, v, do, out, slices, o_rel=0.0):
+def _check_slices(w, layer, q, k, v, do, out, slices, o_rel=0.0, rope=None):
     o, lse, dq, dk, dv = out
     W = w.windows[layer]
     G = w.Hq // w.Hkv
@@ -52,9 +52,9 @@ def _check_slices(w, layer, q, k, v, do, out, slices, o_rel=0.0):
             assert bool((diff <= bound).all())
             assert float((ls.cpu().double() - lse_ref).abs().max()) <= 2e-2
         else:
-            compare_forward(os_, ls, qs, kk, vs, W, w.scale, eps=w.eps)
+            compare_forward(os_, ls, qs, kk, vs, W, w.scale, eps=w.eps, rope=rope)
         compare_backward(dq[b:b + 1, :, hs], dk[b:b + 1, :, ks], dv[b:b + 1, :, ks], qs, kk, vs, ds, W, w.scale,
-                         eps=w.eps)
+                         eps=w.eps, rope=rope)
 
 
 @pytest.mark.parametrize("cfg", [2, 3])
@@ -102,3 +102,15 @@ def test_mha_model_shape_workload(sa, layer):
     q, k, v, do = synth.layer_inputs(w, layer)
     out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[layer], w.scale, eps=w.eps)
     _check_slices(w, layer, q, k, v, do, out, [(0, 0), (w.B - 1, w.Hkv - 1), (61 + layer, 2 + layer % 3)])
+
+
+@pytest.mark.parametrize("layer", [2, 3])
+def test_sssl_stack_with_rope(sa, layer):
+    """A sliding and a full-causal layer of the 8-layer stack with the rotary
+    embedding fused, tables precomputed for ten sequence lengths."""
+    w = synth.WORKLOADS[4]
+    log(f"[workload 4 + rope] layer {layer}")
+    q, k, v, do = synth.layer_inputs(w, layer)
+    rope = sa.rope_tables(10 * w.T, w.D, device="cuda")
+    out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[layer], w.scale, eps=w.eps, rope=rope)
+    _check_slices(w, layer, q, k, v, do, out, [(3 + layer, 1), (w.B - 1, 2)], rope=rope)
