@@ -18,7 +18,7 @@ around each of its launches inside the timed region, and a "cpu_baseline"
 object: the fp64 oracle timed on the host cores on a bounded sample of the
 same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 4]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 4] [--rope]
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (CPU only: turns two
        rocprofv3 --pmc runs of this script into profiles/traffic_<workload>.json)
 """
@@ -165,6 +165,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5, 6])
+    ap.add_argument("--rope", action="store_true",
+                    help="fuse the rotary embedding of q and k (tables for ten sequence lengths)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle sample (0 disables the CPU baseline)")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -282,15 +284,16 @@ def main():
             dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v)))
     ws = torch.empty(sa.sa_attn_bwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(sa.sa_attn_fwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device=dev)
+    rope = sa.rope_tables(10 * w.T, w.D, device=dev) if args.rope else None
     torch.cuda.synchronize()
 
     def fwd(L):
         sa.sa_attn_fwd(L["q"], L["k"], L["v"], window=L["W"], softmax_scale=w.scale, eps=w.eps, o=L["o"], lse=L["lse"],
-                       workspace=ws_f)
+                       workspace=ws_f, rope=rope)
 
     def bwd(L):
         sa.sa_attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=L["W"], softmax_scale=w.scale,
-                       eps=w.eps, dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=ws)
+                       eps=w.eps, dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=ws, rope=rope)
 
     hip = Hip()
     use_ev = not args.no_kernel_events
@@ -394,6 +397,7 @@ def main():
             "workload": w.name,
             "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
             "windows": list(w.windows), "qk_norm": True, "eps": w.eps, "softmax_scale": w.scale,
+            "rope": bool(args.rope),
             "flop_count": "band pairs x (4D fwd + 10D bwd)",
             "flop_per_step": flop_step,
             "parallelism": "single GPU",

@@ -153,8 +153,8 @@ sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o
  *   rope_cos, rope_sin : fp32 DEVICE tables, read only, 16-byte aligned, at
  *                        least T rows of head_dim/2 entries at a row stride
  *                        of rope_stride floats (rope_stride >= head_dim/2, a
- *                        multiple of 4). The backward must get the same tables
- *                        as the forward.
+ *                        multiple of 4, T * rope_stride * 4 < 2^31). The
+ *                        backward must get the same tables as the forward.
  *   Other arguments, workspaces and outputs as for sa_attn_fwd / sa_attn_bwd.
  *   Additional errors: SA_ERR_NULL for a NULL table, SA_ERR_SHAPE for a bad
  *   stride, SA_ERR_ALIGN for a misaligned table, SA_ERR_UNSUPPORTED when

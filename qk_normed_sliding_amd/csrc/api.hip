@@ -81,12 +81,14 @@ bool fixed_max_ok(int qk_norm, float scale, int head_dim, float* c2) {
 
 // Validates optional rotary tables: both or neither pointer, rows of at least
 // head_dim/2 floats at a 16-byte-aligned stride, and only with the QK-norm.
-sa_status check_rope(const float* cos, const float* sin, int stride, int head_dim, int qk_norm, sa::Rope* out) {
+sa_status check_rope(const float* cos, const float* sin, int stride, int T, int head_dim, int qk_norm,
+                     sa::Rope* out) {
   *out = sa::Rope{nullptr, nullptr, 0};
   if (cos == nullptr && sin == nullptr) return SA_OK;
   if (cos == nullptr || sin == nullptr) return SA_ERR_NULL;
   if (!qk_norm) return SA_ERR_UNSUPPORTED;
   if (stride < head_dim / 2 || stride % 4 != 0) return SA_ERR_SHAPE;
+  if ((double)T * stride * 4.0 >= 2147483648.0) return SA_ERR_SHAPE;  // 32-bit table offsets
   if (!aligned16(cos) || !aligned16(sin)) return SA_ERR_ALIGN;
   *out = sa::Rope{cos, sin, stride};
   return SA_OK;
@@ -135,7 +137,7 @@ static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, 
   const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
   if (st != SA_OK) return st;
   sa::Rope rope;
-  const sa_status sr = check_rope(rope_cos, rope_sin, rope_stride, head_dim, qk_norm, &rope);
+  const sa_status sr = check_rope(rope_cos, rope_sin, rope_stride, T, head_dim, qk_norm, &rope);
   if (sr != SA_OK) return sr;
   if (!q || !k || !v || !o || !lse) return SA_ERR_NULL;
   if (qk_norm && (workspace == nullptr || workspace_bytes < sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim) ||
@@ -202,7 +204,7 @@ static sa_status attn_bwd(const void* q, const void* k, const void* v, const voi
   const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
   if (st != SA_OK) return st;
   sa::Rope rope;
-  const sa_status sr = check_rope(rope_cos, rope_sin, rope_stride, head_dim, qk_norm, &rope);
+  const sa_status sr = check_rope(rope_cos, rope_sin, rope_stride, T, head_dim, qk_norm, &rope);
   if (sr != SA_OK) return sr;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SA_ERR_NULL;
   const size_t need = sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim);

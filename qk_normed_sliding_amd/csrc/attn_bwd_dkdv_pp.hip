@@ -332,6 +332,17 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   const bool norm = p.qhat != p.q;
   const bool rope = p.rope.cos != nullptr;
   const long tr = (long)key * p.rope.stride + 4 * half;
+  // table entries first: their loads are in flight with the k rows'
+  f32x4 tc[NDB / 2][4], ts[NDB / 2][4];
+  if (rope) {
+#pragma unroll
+    for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tc[db][i] = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
+        ts[db][i] = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+      }
+  }
   float kx[NDB][16];
   float dot = 0.f, ss = 0.f, r_k = 1.f;
   if (norm) {
@@ -351,8 +362,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
       for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4 c = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
-          const f32x4 sn = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+          const f32x4 c = tc[db][i], sn = ts[db][i];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float a = kx[db][4 * i + j], bb = kx[db + NDB / 2][4 * i + j];
@@ -383,8 +393,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
     for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 c = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
-        const f32x4 sn = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+        const f32x4 c = tc[db][i], sn = ts[db][i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float a = acc[db][4 * i + j], bb = acc[db + NDB / 2][4 * i + j];

@@ -273,6 +273,22 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
       xd[m] = bload16(rd, off);
       xo[m] = bload16(ro, off);
     }
+    // rotary table entries of the lane's rows and dimensions, in flight with the rows
+    const bool rope = p.rope.cos != nullptr;
+    f32x4 tab[QM][4];  // cos (2 x 4), sin (2 x 4)
+    if (rope) {
+      const auto rc = make_rsrc(p.rope.cos, 0xffffffffu);
+      const auto rs = make_rsrc(p.rope.sin, 0xffffffffu);
+#pragma unroll
+      for (int m = 0; m < QM; ++m) {
+        const uint32_t off =
+            (uint32_t)(min(r0 + QRPI * m + crow, T - 1) * p.rope.stride + 8 * (cch % (CPR / 2))) * 4;
+        tab[m][0] = __builtin_bit_cast(f32x4, bload16(rc, off));
+        tab[m][1] = __builtin_bit_cast(f32x4, bload16(rc, off + 16));
+        tab[m][2] = __builtin_bit_cast(f32x4, bload16(rs, off));
+        tab[m][3] = __builtin_bit_cast(f32x4, bload16(rs, off + 16));
+      }
+    }
     bf16* qh = (bf16*)p.qhat + first;
 #pragma unroll
     for (int m = 0; m < QM; ++m) {
@@ -290,13 +306,16 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
       ss = group_sum<CPR>(ss);
       dd = group_sum<CPR>(dd);
       const float rr = norm ? fast_rsqrt(ss * (1.f / D) + p.eps) : 1.f;
-      if (p.rope.cos != nullptr) {
-        // the partner chunk (other half of the row) is CPR/2 lanes away
+      if (rope) {
+        // the partner chunk (other half of the row) is CPR/2 lanes away:
+        // lower half x c - x' s, upper half x c + x' s
         float fp[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) fp[e] = __shfl_xor(f[e], CPR / 2);
-        const long tr = (long)min(r0 + r, T - 1) * p.rope.stride + 8 * (cch % (CPR / 2));
-        rope8(f, fp, p.rope.cos + tr, p.rope.sin + tr, cch >= CPR / 2, false);
+        const float sg = cch >= CPR / 2 ? 1.f : -1.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          f[e] = __builtin_fmaf(f[e], tab[m][e / 4][e % 4], sg * fp[e] * tab[m][2 + e / 4][e % 4]);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= rr;
@@ -383,6 +402,20 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   // for c = 1, in both lane halves.
   if (!wave_active || row >= T) return;
   const long rowoff = ((long)b * T + row) * qstride + (long)head * D + 4 * half;
+  // rotary table entries of the row, loaded first (head_dim d < D/2 in block
+  // db < NDB/2 pairs with d + D/2 in block db + NDB/2)
+  const bool rope = p.rope.cos != nullptr;
+  f32x4 tc[NDB / 2][4], ts[NDB / 2][4];
+  if (rope) {
+    const long tr = (long)row * p.rope.stride + 4 * half;
+#pragma unroll
+    for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tc[db][i] = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
+        ts[db][i] = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+      }
+  }
   float qx[NDB][16];
   float dot = 0.f;
   if (norm) {
@@ -416,15 +449,12 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
       const float gh = p.scale * dq[db][r];
       dq[db][r] = norm ? r_q * (gh - qx[db][r] * dot) : gh;
     }
-  if (p.rope.cos != nullptr) {
-    // head_dim d < D/2 (block db < NDB/2) pairs with d + D/2 (block db + NDB/2)
-    const long tr = (long)row * p.rope.stride + 4 * half;
+  if (rope) {
 #pragma unroll
     for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 c = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
-        const f32x4 sn = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+        const f32x4 c = tc[db][i], sn = ts[db][i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float a = dq[db][4 * i + j], bb = dq[db + NDB / 2][4 * i + j];
