@@ -21,3 +21,4 @@ from .attention import (  # noqa: F401
     rope_tables,
     sssl_windows,
 )
+from .muon import POLAR_EXPRESS_COEFFS, polar_express, polar_step  # noqa: F401,E402

@@ -305,3 +305,20 @@ def test_rope_at_position_zero_only_is_plain_attention(sa):
     b = gpu_fwd_bwd(sa, q, k, v, do, W, D ** -0.5, rope=(cos, sin))
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_backward_is_deterministic(sa):
+    """No atomics anywhere in the backward: the GQA sums over query heads
+    happen in registers of the dK/dV kernel, and every dQ row is written by
+    one wave. Two calls on the same inputs give identical bits (the
+    deterministic-dQ mode the trainer would otherwise ask for)."""
+    B, T, Hq, Hkv, D, W = 2, 700, 6, 2, 128, 256
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=41)
+    a = gpu_fwd_bwd(sa, q, k, v, do, W, D ** -0.5)
+    sa.sa_set_max_workgroups(5)  # a different persistent grid must not change the result either
+    try:
+        b = gpu_fwd_bwd(sa, q, k, v, do, W, D ** -0.5)
+    finally:
+        sa.sa_set_max_workgroups(0)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
