@@ -173,6 +173,33 @@ sa_status sa_attn_bwd_rope(const void* q, const void* k, const void* v, const vo
                            float softmax_scale, int qk_norm, float eps,
                            const float* rope_cos, const float* rope_sin, int rope_stride, void* stream);
 
+/*
+ * sa_polar_express - Muon's orthogonalisation of a stack of bf16 matrices
+ * ("autoresearch Administrator & Developer Guide", section 8.2.3): per matrix
+ *   X = G / (||G||_F + eps), then for the first `steps` of the five printed
+ *   coefficient triples (a, b, c):
+ *     A = X X^T (or X^T X for a tall matrix: the smaller square),
+ *     B = b A + c A A,  X <- a X + B X (or a X + X B),
+ *   out = X. (The guide does not show the initial scaling; dividing by the
+ *   Frobenius norm bounds every singular value by 1, the range the
+ *   coefficients are made for.)
+ *   g, out    : bf16 [batch, rows, cols], contiguous, 16-byte aligned; out
+ *               fully overwritten (must not overlap g).
+ *   rows, cols: multiples of 128 (SA_ERR_UNSUPPORTED otherwise); one matrix
+ *               below 2^31 bytes; batch <= 65535.
+ *   steps     : 1..5 (5 in the trainer); eps >= 0 (the trainer's guard is tiny).
+ *   workspace : at least sa_polar_express_workspace_bytes(batch, rows, cols)
+ *               bytes, 256-byte aligned (two copies of X on its wide side,
+ *               A and B, the norm's partial sums); contents unspecified.
+ *   Arithmetic: bf16 MFMA operands with fp32 accumulation; X, A and B are
+ *   stored as bf16 between the products, as a bf16 optimizer step keeps them.
+ *   The result depends only on its own matrix: matrices of a stack are
+ *   independent.
+ */
+size_t sa_polar_express_workspace_bytes(int batch, int rows, int cols);
+sa_status sa_polar_express(const void* g, void* out, void* workspace, size_t workspace_bytes,
+                           int batch, int rows, int cols, int steps, float eps, void* stream);
+
 /* Kernels that sa_set_timing_events can bracket. */
 enum { SA_KERNEL_FWD = 0, SA_KERNEL_BWD_DQ = 1, SA_KERNEL_BWD_DKDV = 2 };
 

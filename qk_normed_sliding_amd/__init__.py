@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim)
   sa_attn_bwd(q, k, v, o, lse, dout, window=-1, ..., dq=None, dk=None, dv=None, workspace=None)
   sa_attn_fwd_rope(q, k, v, rope_cos, rope_sin, ...), sa_attn_bwd_rope(..., rope_cos, rope_sin, ...)
+  sa_polar_express_workspace_bytes(batch, rows, cols), sa_polar_express(g, out=None, steps=5, eps=1e-7)
 Helpers: attention(...) (autograd), sssl_windows(n_layer, T, pattern), rope_tables(T, D).
 """
 
@@ -69,6 +70,10 @@ def _load():
     lib.sa_attn_bwd_rope.restype = i32
     lib.sa_attn_bwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                      i32, i32, i32, i32, i32, i32, f32, i32, f32, vp, vp, i32, vp]
+    lib.sa_polar_express_workspace_bytes.restype = sz
+    lib.sa_polar_express_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.sa_polar_express.restype = i32
+    lib.sa_polar_express.argtypes = [vp, vp, vp, sz, i32, i32, i32, i32, f32, vp]
     lib.sa_set_timing_events.restype = i32
     lib.sa_set_timing_events.argtypes = [i32, vp, vp]
     lib.sa_set_max_workgroups.restype = i32
@@ -270,6 +275,32 @@ def sa_attn_bwd_rope(q, k, v, o, lse, dout, rope_cos, rope_sin, window=-1, softm
         _ptr(workspace), workspace.numel(), B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D),
         int(bool(qk_norm)), float(eps), rc, rs, stride, _stream(q.device, stream)))
     return dq, dk, dv
+
+
+def sa_polar_express_workspace_bytes(batch, rows, cols):
+    return int(_lib.sa_polar_express_workspace_bytes(batch, rows, cols))
+
+
+def sa_polar_express(g, out=None, steps=5, eps=1e-7, workspace=None, stream=None):
+    """Muon's polar-express orthogonalisation of bf16 g [batch, rows, cols] (or [rows, cols])."""
+    squeeze = g.dim() == 2
+    g3 = g.unsqueeze(0) if squeeze else g
+    if g3.dim() != 3:
+        raise SAError("g: [batch, rows, cols] or [rows, cols] expected")
+    _need(g3, "g", torch.bfloat16)
+    batch, rows, cols = g3.shape
+    if out is None:
+        out = torch.empty_like(g3)
+    out3 = out.unsqueeze(0) if out.dim() == 2 else out
+    _need(out3, "out", torch.bfloat16, g3.shape)
+    if workspace is None:
+        workspace = torch.empty(max(1, sa_polar_express_workspace_bytes(batch, rows, cols)), dtype=torch.uint8,
+                                device=g.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check("sa_polar_express", _lib.sa_polar_express(
+        _ptr(g3), _ptr(out3), _ptr(workspace), workspace.numel(), batch, rows, cols, int(steps), float(eps),
+        _stream(g.device, stream)))
+    return out3.squeeze(0) if squeeze else out3
 
 
 def sa_set_timing_events(kernel, start_event, stop_event):

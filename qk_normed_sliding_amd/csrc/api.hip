@@ -290,6 +290,86 @@ SA_API sa_status sa_attn_bwd_rope(const void* q, const void* k, const void* v, c
                   softmax_scale, qk_norm, eps, rope_cos, rope_sin, rope_stride, stream);
 }
 
+// ---------------------------------------------------------------- polar express
+
+namespace {
+
+// [guide] 8.2.3, the printed coefficients (a, b, c) of the five steps, in order.
+constexpr float kPolarCoeffs[5][3] = {
+    {8.156554524902461f, -22.48329292557795f, 15.878769915207462f},
+    {4.042929935166739f, -2.808917465908714f, 0.5000178451051316f},
+    {3.8916678022926607f, -2.772484153217685f, 0.5060648178503393f},
+    {3.285753657755655f, -2.3681294933425376f, 0.46449024233003106f},
+    {2.3465413258596377f, -1.7097828382687081f, 0.42323551169305323f},
+};
+
+sa_status check_polar(int batch, int rows, int cols, int steps, float eps) {
+  if (batch <= 0 || rows <= 0 || cols <= 0) return SA_ERR_SHAPE;
+  if (rows % 128 != 0 || cols % 128 != 0) return SA_ERR_UNSUPPORTED;
+  if ((double)rows * cols * 2.0 >= 2147483648.0 || (double)batch * rows * cols > 9.0e18) return SA_ERR_SHAPE;
+  if (batch > 65535) return SA_ERR_SHAPE;
+  if (steps < 1 || steps > 5) return SA_ERR_SHAPE;
+  if (!isfinite(eps) || eps < 0.f) return SA_ERR_SHAPE;
+  return SA_OK;
+}
+
+}  // namespace
+
+SA_API size_t sa_polar_express_workspace_bytes(int batch, int rows, int cols) {
+  if (check_polar(batch, rows, cols, 5, 0.f) != SA_OK) return 0;
+  const size_t m = (size_t)(rows < cols ? rows : cols), n = (size_t)(rows < cols ? cols : rows);
+  // X (two buffers, wide side [m][n]), A and B ([m][m]), partial sums of the norm
+  return 2 * round256((size_t)batch * m * n * 2) + 2 * round256((size_t)batch * m * m * 2) +
+         round256((size_t)batch * sa::kFroChunks * 4);
+}
+
+SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, size_t workspace_bytes, int batch,
+                                  int rows, int cols, int steps, float eps, void* stream) {
+  const sa_status st = check_polar(batch, rows, cols, steps, eps);
+  if (st != SA_OK) return st;
+  if (!g || !out) return SA_ERR_NULL;
+  if (!aligned16(g) || !aligned16(out)) return SA_ERR_ALIGN;
+  const size_t need = sa_polar_express_workspace_bytes(batch, rows, cols);
+  if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return SA_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  const bool tall = rows > cols;
+  const int m = tall ? cols : rows, n = tall ? rows : cols;
+  char* ws = (char*)workspace;
+  void* x0 = ws;
+  void* x1 = ws + round256((size_t)batch * m * n * 2);
+  void* A = (char*)x1 + round256((size_t)batch * m * n * 2);
+  void* Bm = (char*)A + round256((size_t)batch * m * m * 2);
+  float* part = (float*)((char*)Bm + round256((size_t)batch * m * m * 2));
+  // wide view of the input: the transpose of a tall matrix
+  const void* src = g;
+  if (tall) {
+    if (sa::launch_transpose(g, x0, batch, rows, cols, s) != hipSuccess) return SA_ERR_HIP;
+    src = x0;
+  }
+  if (sa::launch_fro_scale(src, x0, part, batch, (long)m * n, eps, s) != hipSuccess) return SA_ERR_HIP;
+  void* cur = x0;
+  void* nxt = x1;
+  for (int k = 0; k < steps; ++k) {
+    const float a = kPolarCoeffs[k][0], b = kPolarCoeffs[k][1], c = kPolarCoeffs[k][2];
+    // A = X X^T
+    sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f};
+    if (sa::launch_gemm(pg, false, batch, s) != hipSuccess) return SA_ERR_HIP;
+    // B = c A A + b A  (A is symmetric: A A = A A^T)
+    sa::GemmParams pb{A, A, A, Bm, m, m, m, c, b};
+    if (sa::launch_gemm(pb, false, batch, s) != hipSuccess) return SA_ERR_HIP;
+    // X <- B X + a X, straight into the output on the last step of a wide matrix
+    void* dst = (k == steps - 1 && !tall) ? out : nxt;
+    sa::GemmParams px{Bm, cur, cur, dst, m, n, m, 1.f, a};
+    if (sa::launch_gemm(px, true, batch, s) != hipSuccess) return SA_ERR_HIP;
+    void* t = cur;
+    cur = nxt;
+    nxt = t;
+  }
+  if (tall && sa::launch_transpose(cur, out, batch, m, n, s) != hipSuccess) return SA_ERR_HIP;
+  return SA_OK;
+}
+
 SA_API sa_status sa_set_timing_events(int kernel, void* start, void* stop) {
   if (kernel != SA_KERNEL_FWD && kernel != SA_KERNEL_BWD_DQ && kernel != SA_KERNEL_BWD_DKDV) return SA_ERR_SHAPE;
   if ((start == nullptr) != (stop == nullptr)) return SA_ERR_NULL;

@@ -83,6 +83,19 @@ struct NormParams {
   int H, T;
 };
 
+// Batched bf16 GEMM of the polar-express iteration: per matrix b,
+// C[b] = alpha A[b] op(B[b]) + beta C0[b], A [M][K], op(B) = B^T with B
+// [N][K] or B with B [K][N]; C, C0 [M][N]; M, N multiples of 128, K of 64.
+struct GemmParams {
+  const void* a;
+  const void* b;
+  const void* c0;  // nullptr: beta ignored
+  void* c;
+  int M, N, K;
+  float alpha, beta;
+};
+constexpr int kFroChunks = 64;  // partial sums per matrix of the Frobenius norm
+
 // Optional events recorded around a call's main kernel (benchmarking hook).
 struct TimingEvents {
   hipEvent_t start = nullptr;
@@ -100,6 +113,12 @@ hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream
 // (any query-heads-per-KV-head ratio).
 hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
 hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream);
+// Polar-express pieces: GEMM (b_kn: B given as [K][N]), X / ||X||_F per matrix
+// (part: batch * kFroChunks floats), and per-matrix transpose [R][C] -> [C][R].
+hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream);
+hipError_t launch_fro_scale(const void* x, void* y, float* part, int batch, long per_matrix, float eps,
+                            hipStream_t stream);
+hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, hipStream_t stream);
 hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace sa

@@ -33,7 +33,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("sa_qknorm", "sa_attn_fwd", "sa_attn_fwd_workspace_bytes", "sa_attn_bwd", "sa_attn_bwd_workspace_bytes",
-              "sa_status_string", "sa_abi_version", "sa_attn_fwd_rope", "sa_attn_bwd_rope"):
+              "sa_status_string", "sa_abi_version", "sa_attn_fwd_rope", "sa_attn_bwd_rope",
+              "sa_polar_express", "sa_polar_express_workspace_bytes"):
         assert n in names
 
 
@@ -195,3 +196,33 @@ def test_binding_rejects_cpu_tensors(sa):
     k = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         sa.sa_attn_fwd(q, k, k)
+
+
+def test_polar_express_validation_paths(sa):
+    lib = sa.library()
+    P = ctypes.c_void_p
+    r256 = lambda x: (x + 255) // 256 * 256
+    # two X buffers on the wide side, A and B, 64 partial sums per matrix
+    assert lib.sa_polar_express_workspace_bytes(8, 768, 3072) == 2 * r256(8 * 768 * 3072 * 2) + 2 * r256(
+        8 * 768 * 768 * 2) + r256(8 * 64 * 4)
+    assert lib.sa_polar_express_workspace_bytes(8, 3072, 768) == lib.sa_polar_express_workspace_bytes(8, 768, 3072)
+    assert lib.sa_polar_express_workspace_bytes(1, 100, 128) == 0
+
+    def call(g=16, out=32, ws=256, ws_bytes=None, batch=2, rows=256, cols=384, steps=5, eps=1e-7):
+        need = lib.sa_polar_express_workspace_bytes(batch, rows, cols)
+        return lib.sa_polar_express(P(g), P(out), P(ws), need if ws_bytes is None else ws_bytes, batch, rows, cols,
+                                    steps, eps, None)
+
+    assert call(g=0) == SA_ERR_NULL
+    assert call(out=0) == SA_ERR_NULL
+    assert call(g=8) == SA_ERR_ALIGN
+    assert call(rows=200) == SA_ERR_UNSUPPORTED
+    assert call(cols=64) == SA_ERR_UNSUPPORTED
+    assert call(batch=0) == SA_ERR_SHAPE
+    assert call(steps=0) == SA_ERR_SHAPE
+    assert call(steps=6) == SA_ERR_SHAPE
+    assert call(eps=-1.0) == SA_ERR_SHAPE
+    assert call(rows=32768, cols=32768) == SA_ERR_SHAPE
+    assert call(ws=0) == SA_ERR_WORKSPACE
+    assert call(ws_bytes=100) == SA_ERR_WORKSPACE
+    assert call(ws=128) == SA_ERR_WORKSPACE
