@@ -167,6 +167,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5, 6])
     ap.add_argument("--rope", action="store_true",
                     help="fuse the rotary embedding of q and k (tables for ten sequence lengths)")
+    ap.add_argument("--polar", action="store_true",
+                    help="time Muon's polar-express orthogonalisation of the trainer's weight groups instead "
+                         "of the attention step (its own JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle sample (0 disables the CPU baseline)")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -250,8 +253,93 @@ def cpu_baseline(w, budget_s):
     }
 
 
+# The trainer's Muon groups at n_embd 768, 8 layers, multi-head attention (the
+# pages' default n_kv_head = n_head): per layer the q, k, v and output
+# projections (768 x 768) and the MLP's two matrices ([out, in] = 3072 x 768
+# and 768 x 3072), stacked by shape.
+POLAR_GROUPS = ((32, 768, 768), (8, 3072, 768), (8, 768, 3072))
+
+
+def polar_flops(batch, rows, cols, steps=5):
+    """MFMA FLOP of the iteration: per step A = X X^T (2 m^2 n), A A (2 m^3), B X (2 m^2 n), m <= n."""
+    m, n = min(rows, cols), max(rows, cols)
+    return float(batch) * steps * (4.0 * m * m * n + 2.0 * m ** 3)
+
+
+def bench_polar(args):
+    import torch
+
+    import qk_normed_sliding_amd as sa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(4242)
+    groups = []
+    for batch, rows, cols in POLAR_GROUPS:
+        g = torch.randn((batch, rows, cols), generator=gen, dtype=torch.float32).to(torch.bfloat16).to(dev)
+        ws = torch.empty(sa.sa_polar_express_workspace_bytes(batch, rows, cols), dtype=torch.uint8, device=dev)
+        groups.append((g, torch.empty_like(g), ws))
+    flop = sum(polar_flops(*x) for x in POLAR_GROUPS)
+
+    def step():
+        for g, out, ws in groups:
+            sa.sa_polar_express(g, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    tflops = flop / (ms * 1e-3) / 1e12
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+
+        torch.set_num_threads(max(1, os.cpu_count() or 1))
+        done = spent = 0.0
+        samples = 0
+        while spent < args.cpu_seconds:
+            batch, rows, cols = POLAR_GROUPS[samples % len(POLAR_GROUPS)]
+            g = groups[samples % len(POLAR_GROUPS)][0][0:1].cpu()
+            t = time.perf_counter()
+            oracle.polar_express(g)
+            spent += time.perf_counter() - t
+            done += polar_flops(1, rows, cols)
+            samples += 1
+        cpu = {"value": done / spent / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(), "kind": "oracle",
+               "sample": f"{samples} single matrices cycling through the three groups (fp64 iteration), "
+                         f"{spent:.1f} s"}
+
+    out = {
+        "metric": "Muon polar-express TFLOP/s (5 steps, the trainer's weight groups at n_embd 768)",
+        "value": tflops, "unit": "TFLOP/s", "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 gradients of the weight shapes)",
+        "config": {"workload": "muon_polar_express_n768_8layers_mha", "groups": [list(x) for x in POLAR_GROUPS],
+                   "flop_count": "per matrix 5 x (4 m^2 n + 2 m^3), m <= n", "flop_per_step": flop,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (with the norm and transpose passes)",
+                     "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.polar and args.gpus == 1:
+        bench_polar(args)
+        return
     if args.summarize_pmc:
         import synth
 
