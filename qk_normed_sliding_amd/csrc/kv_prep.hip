@@ -17,7 +17,10 @@ template <int D>
 __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepParams p) {
   constexpr int CPR = D / 8;       // 16-byte chunks per row
   constexpr int RPP = 256 / CPR;   // rows per pass of the workgroup
-  constexpr int VP = D + 8;        // LDS pitch of the staged value tile (elements)
+  // LDS pitch of the staged value tile: D + 2 elements is an odd number of
+  // 4-byte words, so the 2-byte column reads of the transposed write (keys
+  // 8c + 2j, c = 0..7, at one column) fall on distinct banks
+  constexpr int VP = D + 2;
   __shared__ __attribute__((aligned(16))) bf16 vs[64 * VP];
 
   const int t0 = blockIdx.x * 64;
@@ -51,7 +54,9 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= rs;
     if (in) st16((bf16*)p.khat + off, pack8(x));
-    *(u32x4*)(vs + r * VP + 8 * sub) = vw;  // rows past T stay zero
+    uint32_t* vrow = (uint32_t*)(vs + r * VP + 8 * sub);  // 4-byte aligned at this pitch
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vrow[e] = vw[e];  // rows past T stay zero
   }
   __syncthreads();
 
