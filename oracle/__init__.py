@@ -20,5 +20,9 @@ from .attention import (  # noqa: F401
     rope_rotate_back,
     rope_tables,
     sssl_windows,
+    ve_backward,
+    ve_gate,
+    ve_layers,
+    ve_mix,
 )
 from .muon import POLAR_EXPRESS_COEFFS, polar_express, polar_step  # noqa: F401,E402

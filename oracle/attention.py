@@ -19,6 +19,8 @@ fusion and no rounding:
   6. backward of 1-5 with respect to the raw q, k, v
   optional: the rotary position embedding of q and k rows (tables of cos and
   sin given per position), applied before step 1
+  optional: the value-embedding gate of the value rows (below), applied to v
+  before step 5
 
 Sources (cited by page title and section):
   [post]   The social post that walks through autoresearch's train.py
@@ -172,6 +174,43 @@ def rope_rotate_back(y: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor) -> t
     return torch.cat([y1 * c + y2 * s, -y1 * s + y2 * c], dim=-1)
 
 
+# ---------------------------------------------------------------- value embeddings
+
+def ve_layers(n_layer: int) -> list:
+    """Layers that carry value embeddings: alternating, the last always included
+    ([guide] 8.2.1)."""
+    return [i for i in range(n_layer) if (n_layer - 1 - i) % 2 == 0]
+
+
+def ve_gate(x32: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """gate [B, T, Hkv] = 2 sigmoid(x[..., :32] W^T): [guide] 8.2.1, the value-embedding
+    gate (a bias-free linear map of the first 32 channels to one value per KV head)."""
+    z = x32.to(F64) @ w.to(F64).transpose(0, 1)
+    return 2.0 * torch.sigmoid(z)
+
+
+def ve_mix(v: torch.Tensor, x32: torch.Tensor, w: torch.Tensor, ids: torch.Tensor, table: torch.Tensor):
+    """v + gate[..., None] * ve with ve = table[ids] viewed [B, T, Hkv, D] ([guide] 8.2.1)."""
+    B, T, Hkv, D = v.shape
+    ve = table.to(F64)[ids.long()].view(B, T, Hkv, D)
+    return v.to(F64) + ve_gate(x32, w).unsqueeze(-1) * ve
+
+
+def ve_backward(dv_mixed, x32, w, ids, table):
+    """Gradients of the mix, given dL/dv' for v' = v + g ve, g = 2 sigmoid(z), z = x32 W^T:
+    dv = dv', dve = g dv', dg = <dv', ve> over D, dz = dg g (1 - g/2),
+    dW = sum_{b,t} dz^T x32, dx32 = dz W. Returns (dve [B,T,Hkv,D], dW [Hkv,32], dx32 [B,T,32])."""
+    B, T, Hkv, D = dv_mixed.shape
+    dvm = dv_mixed.to(F64)
+    ve = table.to(F64)[ids.long()].view(B, T, Hkv, D)
+    g = ve_gate(x32, w)
+    dve = g.unsqueeze(-1) * dvm
+    dz = (dvm * ve).sum(-1) * g * (1.0 - g / 2.0)
+    dw = torch.einsum("bth,btc->hc", dz, x32.to(F64))
+    dx32 = dz @ w.to(F64)
+    return dve, dw, dx32
+
+
 # ---------------------------------------------------------------- heads
 
 def kv_head(h: int, Hq: int, Hkv: int) -> int:
@@ -232,15 +271,16 @@ def attention_probs(q, k, window, scale, qk_norm=True, eps=1e-6, rope=None):
     return P
 
 
-def attn_forward(q, k, v, window, scale, qk_norm=True, eps=1e-6, rope=None):
+def attn_forward(q, k, v, window, scale, qk_norm=True, eps=1e-6, rope=None, ve=None):
     """Forward of the layer: returns (o [B,T,Hq,D], lse [B,Hq,T]) in float64.
 
     q [B,T,Hq,D], k and v [B,T,Hkv,D] (any float dtype; upcast exactly);
-    rope = (cos, sin) tables turn q and k rows first (rope_rotate).
+    rope = (cos, sin) tables turn q and k rows first (rope_rotate);
+    ve = (x32, w, ids, table) mixes value embeddings into v first (ve_mix).
     """
     B, T, Hq, Hkv, D = _check_shapes(q, k, v)
     q_hat, _, k_hat, _ = _normed(q, k, qk_norm, eps, rope)
-    v = v.to(F64)
+    v = v.to(F64) if ve is None else ve_mix(v, *ve)
     mask = band_mask(T, window)
     o = torch.zeros(B, T, Hq, D, dtype=F64)
     lse = torch.zeros(B, Hq, T, dtype=F64)
@@ -254,7 +294,7 @@ def attn_forward(q, k, v, window, scale, qk_norm=True, eps=1e-6, rope=None):
 
 # ---------------------------------------------------------------- backward
 
-def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6, rope=None):
+def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6, rope=None, ve=None):
     """Gradients (dq, dk, dv) of <O, dO> with respect to the raw q, k, v (float64).
 
     Per (b, h) with g its KV head:
@@ -266,10 +306,12 @@ def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6, rope=None)
       dk_hat_g += scale * dS^T Q_hat
     then the RMS-norm backward maps dq_hat, dk_hat to the gradients of the
     rotated rows, and (with rope) the transposed rotation to dq, dk.
+    With ve = (x32, w, ids, table) the value rows are the mixed ones and the
+    result also holds (dve, dw, dx32) of ve_backward: (dq, dk, dv, dve, dw, dx32).
     """
     B, T, Hq, Hkv, D = _check_shapes(q, k, v)
     q_hat, r_q, k_hat, r_k = _normed(q, k, qk_norm, eps, rope)
-    v = v.to(F64)
+    v = v.to(F64) if ve is None else ve_mix(v, *ve)
     do = do.to(F64)
     mask = band_mask(T, window)
     dq_hat = torch.zeros(B, T, Hq, D, dtype=F64)
@@ -294,6 +336,8 @@ def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6, rope=None)
     if rope is not None:
         dq = rope_rotate_back(dq, *rope)
         dk = rope_rotate_back(dk, *rope)
+    if ve is not None:
+        return (dq, dk, dv) + ve_backward(dv, *ve)
     return dq, dk, dv
 
 

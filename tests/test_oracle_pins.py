@@ -440,6 +440,88 @@ def test_rope_backward_central_finite_differences():
         assert float((fd - g).norm() / g.norm()) < 1e-6, idx
 
 
+# ------------------------------------------------------------------ value embeddings
+
+def test_ve_layers_match_the_printed_map():
+    rows = [int(ln) for ln in open(os.path.join(GOLDEN, "ve_layers_depth8.txt")) if ln.strip() and ln[0] != "#"]
+    assert oracle.ve_layers(8) == rows
+    for n in (1, 2, 5, 12):
+        layers = oracle.ve_layers(n)
+        assert layers[-1] == n - 1 and all(b - a == 2 for a, b in zip(layers, layers[1:]))
+
+
+def test_ve_zero_gate_weights_give_the_identity_pathway():
+    """Zero gate weights: 2 sigmoid(0) = 1, so v' = v + ve (the trainer's initial state)."""
+    B, T, Hkv, D, V = 2, 5, 3, 8, 11
+    v, x32, table = _rand((B, T, Hkv, D), 1), _rand((B, T, 32), 2), _rand((V, Hkv * D), 3)
+    ids = torch.randint(0, V, (B, T), generator=torch.Generator().manual_seed(4))
+    w = torch.zeros(Hkv, 32, dtype=F64)
+    assert torch.equal(oracle.ve_gate(x32, w), torch.ones(B, T, Hkv, dtype=F64))
+    assert torch.allclose(oracle.ve_mix(v, x32, w, ids, table), v + table[ids].view(B, T, Hkv, D), atol=0)
+
+
+VE_CASES = [
+    # B, T, Hq, Hkv, D, W, V
+    (2, 17, 6, 3, 16, -1, 13),
+    (1, 17, 4, 4, 8, 5, 7),
+]
+
+
+def _ve_inputs(case, seed):
+    B, T, Hq, Hkv, D, W, V = case
+    q, k, v, do = (_rand((B, T, Hq, D), seed), _rand((B, T, Hkv, D), seed + 1),
+                   _rand((B, T, Hkv, D), seed + 2), _rand((B, T, Hq, D), seed + 3))
+    x32, w, table = _rand((B, T, 32), seed + 4), _rand((Hkv, 32), seed + 5, 0.2), _rand((V, Hkv * D), seed + 6)
+    ids = torch.randint(0, V, (B, T), generator=torch.Generator().manual_seed(seed + 7))
+    return q, k, v, do, x32, w, ids, table
+
+
+def _ve_err(case, seed=120, scale=0.4):
+    B, T, Hq, Hkv, D, W, V = case
+    q, k, v, do, x32, w, ids, table = _ve_inputs(case, seed)
+    o, lse = oracle.attn_forward(q, k, v, W, scale, ve=(x32, w, ids, table))
+    leaves = [t.clone().requires_grad_(True) for t in (q, k, v, x32, w, table)]
+    qa, ka, va, xa, wa, ta = leaves
+    gate = 2.0 * torch.sigmoid(F.linear(xa, wa))
+    vm = va + gate.unsqueeze(-1) * F.embedding(ids, ta).view(B, T, Hkv, D)
+    o_ref, lse_ref = _lib_forward(qa, ka, vm, W, scale)
+    gq, gk, gv, gx, gw, gt = torch.autograd.grad(o_ref, leaves, do)
+    dq, dk, dv, dve, dw, dx32 = oracle.attn_backward(q, k, v, do, W, scale, ve=(x32, w, ids, table))
+    # the table's gradient is the per-position dve summed into the rows the ids pick
+    dtable = torch.zeros_like(table).index_add_(0, ids.view(-1), dve.reshape(B * T, Hkv * D))
+    return max(float((o - o_ref).abs().max()), float((lse - lse_ref).abs().max()),
+               float((dq - gq).abs().max()), float((dk - gk).abs().max()), float((dv - gv).abs().max()),
+               float((dx32 - gx).abs().max()), float((dw - gw).abs().max()), float((dtable - gt).abs().max()))
+
+
+@pytest.mark.parametrize("case", VE_CASES)
+def test_ve_attention_matches_library_forward_and_autograd(case):
+    assert _ve_err(case) < 1e-11
+
+
+def test_ve_backward_central_finite_differences():
+    case = (1, 6, 2, 1, 8, 3, 5)
+    q, k, v, do, x32, w, ids, table = _ve_inputs(case, 130)
+    h, scale = 1e-6, 0.35
+    grads = oracle.attn_backward(q, k, v, do, 3, scale, ve=(x32, w, ids, table))
+
+    def loss():
+        return float((oracle.attn_forward(q, k, v, 3, scale, ve=(x32, w, ids, table))[0] * do).sum())
+
+    for x, g in ((w, grads[4]), (x32, grads[5])):
+        fd = torch.zeros_like(x)
+        flat, fdf = x.view(-1), fd.view(-1)
+        for e in range(flat.numel()):
+            old = float(flat[e])
+            flat[e] = old + h
+            lp = loss()
+            flat[e] = old - h
+            lm = loss()
+            flat[e] = old
+            fdf[e] = (lp - lm) / (2 * h)
+        assert float((fd - g).norm() / g.norm()) < 1e-6
+
+
 # ------------------------------------------------------------------ planted mistakes
 
 def _all_pins_pass():
@@ -456,6 +538,8 @@ def _all_pins_pass():
     if not torch.allclose(OA.rms_norm(x, 0.1)[0], F.rms_norm(x, (8,), eps=0.1), atol=1e-14):
         return False
     if _rope_err(ROPE_CASES[0]) > 1e-11 or _rope_err(ROPE_CASES[1]) > 1e-11:
+        return False
+    if _ve_err(VE_CASES[0]) > 1e-11:
         return False
     return True
 
@@ -500,6 +584,19 @@ def _mut_rope_rotate_back(y, cos, sin):
     return OA.rope_rotate(y, cos, sin)  # the rotation instead of its transpose
 
 
+def _mut_ve_gate(x32, w):
+    return torch.sigmoid(x32.to(F64) @ w.to(F64).transpose(0, 1))  # factor 2 dropped
+
+
+def _mut_ve_backward(dv_mixed, x32, w, ids, table):
+    B, T, Hkv, D = dv_mixed.shape
+    dvm = dv_mixed.to(F64)
+    ve = table.to(F64)[ids.long()].view(B, T, Hkv, D)
+    g = OA.ve_gate(x32, w)
+    dz = (dvm * ve).sum(-1) * g * (1.0 - g)  # slope of sigmoid taken at g instead of g/2
+    return g.unsqueeze(-1) * dvm, torch.einsum("bth,btc->hc", dz, x32.to(F64)), dz @ w.to(F64)
+
+
 def _mut_probs(q_hat_bh, k_hat_bg, mask, scale):
     return OA.__dict__["_real_probs"](q_hat_bh, k_hat_bg, mask, scale * scale)  # scale applied twice
 
@@ -512,6 +609,8 @@ def _mut_probs(q_hat_bh, k_hat_bg, mask, scale):
     ("_probs_one_head", _mut_probs),
     ("rope_rotate", _mut_rope_rotate),
     ("rope_rotate_back", _mut_rope_rotate_back),
+    ("ve_gate", _mut_ve_gate),
+    ("ve_backward", _mut_ve_backward),
 ])
 def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
     monkeypatch.setitem(OA.__dict__, "_real_probs", OA._probs_one_head)
