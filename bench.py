@@ -18,7 +18,7 @@ around each of its launches inside the timed region, and a "cpu_baseline"
 object: the fp64 oracle timed on the host cores on a bounded sample of the
 same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 4] [--rope]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 4] [--rope] [--ve]
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (CPU only: turns two
        rocprofv3 --pmc runs of this script into profiles/traffic_<workload>.json)
 """
@@ -167,6 +167,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=4, choices=[2, 3, 4, 5, 6])
     ap.add_argument("--rope", action="store_true",
                     help="fuse the rotary embedding of q and k (tables for ten sequence lengths)")
+    ap.add_argument("--ve", action="store_true",
+                    help="mix value embeddings into the layers that carry them in the trainer (1, 3, 5, 7)")
     ap.add_argument("--polar", action="store_true",
                     help="time Muon's polar-express orthogonalisation of the trainer's weight groups instead "
                          "of the attention step (its own JSON line)")
@@ -365,21 +367,35 @@ def main():
     layers = []
     for layer in range(w.n_layer):
         q, k, v, do = (x.to(dev) for x in synth.layer_inputs(w, layer))
+        ve = None
+        if args.ve and layer in sa.ve_layers(w.n_layer):
+            ve = tuple(t.to(dev) for t in synth.ve_inputs(w, layer))
         print(f"inputs of layer {layer} resident", file=sys.stderr, flush=True)
         layers.append(dict(
             W=w.windows[layer], q=q, k=k, v=v, do=do,
             o=torch.empty_like(q), lse=torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev),
-            dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v)))
+            dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), ve=ve))
     ws = torch.empty(sa.sa_attn_bwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(sa.sa_attn_fwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device=dev)
     rope = sa.rope_tables(10 * w.T, w.D, device=dev) if args.rope else None
+    ws_ve = (torch.empty(sa.sa_attn_ve_workspace_bytes(w.B, w.T, w.Hkv, w.D), dtype=torch.uint8, device=dev)
+             if args.ve else None)
     torch.cuda.synchronize()
 
     def fwd(L):
+        if L["ve"] is not None:
+            sa.sa_attn_fwd_ex(L["q"], L["k"], L["v"], window=L["W"], softmax_scale=w.scale, eps=w.eps, o=L["o"],
+                              lse=L["lse"], workspace=ws_f, rope=rope, ve=L["ve"])
+            return
         sa.sa_attn_fwd(L["q"], L["k"], L["v"], window=L["W"], softmax_scale=w.scale, eps=w.eps, o=L["o"], lse=L["lse"],
                        workspace=ws_f, rope=rope)
 
     def bwd(L):
+        if L["ve"] is not None:
+            sa.sa_attn_bwd_ex(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=L["W"], softmax_scale=w.scale,
+                              eps=w.eps, dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=ws, rope=rope, ve=L["ve"],
+                              ve_workspace=ws_ve)
+            return
         sa.sa_attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=L["W"], softmax_scale=w.scale,
                        eps=w.eps, dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=ws, rope=rope)
 
@@ -485,7 +501,7 @@ def main():
             "workload": w.name,
             "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
             "windows": list(w.windows), "qk_norm": True, "eps": w.eps, "softmax_scale": w.scale,
-            "rope": bool(args.rope),
+            "rope": bool(args.rope), "value_embeddings": bool(args.ve),
             "flop_count": "band pairs x (4D fwd + 10D bwd)",
             "flop_per_step": flop_step,
             "parallelism": "single GPU",

@@ -174,6 +174,57 @@ sa_status sa_attn_bwd_rope(const void* q, const void* k, const void* v, const vo
                            const float* rope_cos, const float* rope_sin, int rope_stride, void* stream);
 
 /*
+ * sa_attn_fwd_ex / sa_attn_bwd_ex - the forward and backward with the
+ * optional extras of the trainer's attention, each group all-or-none (NULL
+ * pointers: absent):
+ *   rotary tables : rope_cos, rope_sin, rope_stride as for sa_attn_fwd_rope;
+ *   value-embedding gate ([guide] 8.2.1: alternating layers, the last always,
+ *   mix a learned embedding of the token ids into v through a gate of the
+ *   first 32 channels of the attention's input):
+ *     g[b,t,h] = 2 sigmoid(sum_{c<32} ve_x[b,t,c] ve_w[h,c]),
+ *     v'[b,t,h,:] = v[b,t,h,:] + g[b,t,h] ve_table[ve_ids[b,t], h*D : (h+1)*D],
+ *   and attention runs on v'. (The gate's linear map has no bias: a reading.)
+ *     ve_x       : bf16 DEVICE rows [B*T] of ve_x_stride elements (>= 32, a
+ *                  multiple of 8), 16-byte aligned; the first 32 are read.
+ *     ve_w       : bf16 [Hkv, 32], 16-byte aligned.
+ *     ve_ids     : int32 [B*T]; an id outside [0, ve_vocab) reads a zero row.
+ *     ve_table   : bf16 [ve_vocab, Hkv*D], 16-byte aligned,
+ *                  ve_vocab*Hkv*D*2 < 2^31.
+ *   Backward outputs with the gate (all required then):
+ *     dv         : the gradient of the raw v (= that of v', the mix is v + ...).
+ *     dve        : bf16 [B, T, Hkv, D], the gradient of the gathered embedding
+ *                  rows per position (the table's gradient is their sum into
+ *                  the rows ve_ids picks: the caller's embedding backward).
+ *     dve_w      : fp32 [Hkv, 32], summed over all positions in a fixed order.
+ *     dve_x32    : fp32 [B, T, 32], the gradient of ve_x's first 32 channels.
+ *     ve_workspace : at least sa_attn_ve_workspace_bytes(B, T, Hkv, head_dim)
+ *                  bytes, 256-byte aligned (v', the gate, partial sums).
+ *   Both extras need qk_norm (SA_ERR_UNSUPPORTED otherwise, for the gate with
+ *   Hkv > 16, and when
+ *   |softmax_scale| * head_dim is too large for the fixed row maximum).
+ *   Other errors as for the plain calls, plus SA_ERR_NULL for a partial group,
+ *   SA_ERR_SHAPE for a bad stride or vocabulary, SA_ERR_ALIGN, SA_ERR_WORKSPACE.
+ */
+sa_status sa_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int T, int Hq, int Hkv, int head_dim, int window,
+                         float softmax_scale, int qk_norm, float eps,
+                         const float* rope_cos, const float* rope_sin, int rope_stride,
+                         const void* ve_x, int64_t ve_x_stride, const void* ve_w, const int32_t* ve_ids,
+                         const void* ve_table, int ve_vocab, void* stream);
+size_t sa_attn_ve_workspace_bytes(int B, int T, int Hkv, int head_dim);
+sa_status sa_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int T, int Hq, int Hkv, int head_dim, int window,
+                         float softmax_scale, int qk_norm, float eps,
+                         const float* rope_cos, const float* rope_sin, int rope_stride,
+                         const void* ve_x, int64_t ve_x_stride, const void* ve_w, const int32_t* ve_ids,
+                         const void* ve_table, int ve_vocab,
+                         void* dve, float* dve_w, float* dve_x32, void* ve_workspace, size_t ve_workspace_bytes,
+                         void* stream);
+
+/*
  * sa_polar_express - Muon's orthogonalisation of a stack of bf16 matrices
  * ("autoresearch Administrator & Developer Guide", section 8.2.3): per matrix
  *   X = G / (||G||_F + eps), then for the first `steps` of the five printed

@@ -12,8 +12,10 @@ Entry points (same names as the C ABI):
   sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim)
   sa_attn_bwd(q, k, v, o, lse, dout, window=-1, ..., dq=None, dk=None, dv=None, workspace=None)
   sa_attn_fwd_rope(q, k, v, rope_cos, rope_sin, ...), sa_attn_bwd_rope(..., rope_cos, rope_sin, ...)
+  sa_attn_fwd_ex / sa_attn_bwd_ex (rotary tables and value-embedding gate; also rope=..., ve=... on the plain calls)
+  sa_attn_ve_workspace_bytes(B, T, Hkv, head_dim)
   sa_polar_express_workspace_bytes(batch, rows, cols), sa_polar_express(g, out=None, steps=5, eps=1e-7)
-Helpers: attention(...) (autograd), sssl_windows(n_layer, T, pattern), rope_tables(T, D).
+Helpers: attention(...) (autograd), sssl_windows(n_layer, T, pattern), rope_tables(T, D), ve_layers(n_layer).
 """
 
 from __future__ import annotations
@@ -28,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa_attn.so")
 
 SA_OK = 0
-ABI_VERSION = 3
+ABI_VERSION = 4
 SA_KERNEL_FWD = 0
 SA_KERNEL_BWD_DQ = 1
 SA_KERNEL_BWD_DKDV = 2
@@ -70,6 +72,16 @@ def _load():
     lib.sa_attn_bwd_rope.restype = i32
     lib.sa_attn_bwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                      i32, i32, i32, i32, i32, i32, f32, i32, f32, vp, vp, i32, vp]
+    i64t = ctypes.c_int64
+    lib.sa_attn_fwd_ex.restype = i32
+    lib.sa_attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, f32, i32, f32,
+                                   vp, vp, i32, vp, i64t, vp, vp, vp, i32, vp]
+    lib.sa_attn_ve_workspace_bytes.restype = sz
+    lib.sa_attn_ve_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.sa_attn_bwd_ex.restype = i32
+    lib.sa_attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                   i32, i32, i32, i32, i32, i32, f32, i32, f32, vp, vp, i32,
+                                   vp, i64t, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.sa_polar_express_workspace_bytes.restype = sz
     lib.sa_polar_express_workspace_bytes.argtypes = [i32, i32, i32]
     lib.sa_polar_express.restype = i32
@@ -167,10 +179,88 @@ def _rope_args(rope_cos, rope_sin, T, D, device):
     return _ptr(rope_cos), _ptr(rope_sin), int(rope_cos.stride(0))
 
 
+def _ve_args(ve, B, T, Hkv, D, device):
+    """(x [B,T,C>=32] bf16, w [Hkv,32] bf16, ids [B,T] int32, table [V, Hkv*D] bf16) -> C-ABI arguments."""
+    x, w, ids, table = ve
+    _need(x, "ve x", torch.bfloat16)
+    if x.dim() != 3 or tuple(x.shape[:2]) != (B, T) or x.shape[2] < 32:
+        raise SAError(f"ve x: [B={B}, T={T}, >=32] expected")
+    _need(w, "ve w", torch.bfloat16, (Hkv, 32))
+    _need(ids, "ve ids", torch.int32, (B, T))
+    _need(table, "ve table", torch.bfloat16)
+    if table.dim() != 2 or table.shape[1] != Hkv * D:
+        raise SAError(f"ve table: [vocab, Hkv*D={Hkv * D}] expected")
+    return _ptr(x), int(x.shape[2]), _ptr(w), _ptr(ids), _ptr(table), int(table.shape[0])
+
+
+def sa_attn_fwd_ex(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None,
+                   workspace=None, stream=None, rope=None, ve=None):
+    """Forward with optional rotary tables rope=(cos, sin) and value-embedding gate ve=(x, w, ids, table)."""
+    B, T, Hq, Hkv, D = _dims(q, k)
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, T, Hkv, D))
+    _need(v, "v", torch.bfloat16, (B, T, Hkv, D))
+    rc, rs, rstride = _rope_args(rope[0], rope[1], T, D, q.device) if rope is not None else (None, None, 0)
+    vx, vxs, vw, vids, vtab, vocab = _ve_args(ve, B, T, Hkv, D, q.device) if ve is not None else (
+        None, 0, None, None, None, 0)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "o", torch.bfloat16, q.shape)
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    if workspace is None:
+        workspace = torch.empty(sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    _check("sa_attn_fwd_ex", _lib.sa_attn_fwd_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+        B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D), int(bool(qk_norm)), float(eps),
+        rc, rs, rstride, vx, vxs, vw, vids, vtab, vocab, _stream(q.device, stream)))
+    return o, lse
+
+
+def sa_attn_ve_workspace_bytes(B, T, Hkv, head_dim):
+    return int(_lib.sa_attn_ve_workspace_bytes(B, T, Hkv, head_dim))
+
+
+def sa_attn_bwd_ex(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, dq=None, dk=None,
+                   dv=None, workspace=None, stream=None, rope=None, ve=None, ve_workspace=None):
+    """Backward with the optional extras. Returns (dq, dk, dv), plus (dve, dw, dx32) with ve."""
+    B, T, Hq, Hkv, D = _dims(q, k)
+    for t, n, shp in ((q, "q", None), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D)),
+                      (o, "o", q.shape), (dout, "dout", q.shape)):
+        _need(t, n, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    rc, rs, rstride = _rope_args(rope[0], rope[1], T, D, q.device) if rope is not None else (None, None, 0)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8)
+    dve = dw = dx32 = None
+    if ve is not None:
+        vx, vxs, vw, vids, vtab, vocab = _ve_args(ve, B, T, Hkv, D, q.device)
+        dve = torch.empty_like(v)
+        dw = torch.empty((Hkv, 32), dtype=torch.float32, device=q.device)
+        dx32 = torch.empty((B, T, 32), dtype=torch.float32, device=q.device)
+        if ve_workspace is None:
+            ve_workspace = torch.empty(sa_attn_ve_workspace_bytes(B, T, Hkv, D), dtype=torch.uint8, device=q.device)
+        ve_ptrs = (vx, vxs, vw, vids, vtab, vocab, _ptr(dve), _ptr(dw), _ptr(dx32), _ptr(ve_workspace),
+                   ve_workspace.numel())
+    else:
+        ve_ptrs = (None, 0, None, None, None, 0, None, None, None, None, 0)
+    _check("sa_attn_bwd_ex", _lib.sa_attn_bwd_ex(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), workspace.numel(), B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D),
+        int(bool(qk_norm)), float(eps), rc, rs, rstride, *ve_ptrs, _stream(q.device, stream)))
+    return (dq, dk, dv) if ve is None else (dq, dk, dv, dve, dw, dx32)
+
+
 def sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None,
-                workspace=None, stream=None, rope=None):
+                workspace=None, stream=None, rope=None, ve=None):
     """Forward of one layer. q [B,T,Hq,D], k/v [B,T,Hkv,D] bf16. Returns (o, lse).
-    rope = (cos, sin) rotary tables run sa_attn_fwd_rope instead."""
+    rope = (cos, sin) rotary tables and/or ve = (x, w, ids, table) value embeddings use the fused entry points."""
+    if ve is not None:
+        return sa_attn_fwd_ex(q, k, v, window, softmax_scale, qk_norm, eps, o, lse, workspace, stream, rope, ve)
     if rope is not None:
         return sa_attn_fwd_rope(q, k, v, rope[0], rope[1], window, softmax_scale, qk_norm, eps, o, lse,
                                 workspace, stream)
@@ -224,9 +314,12 @@ def sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim):
 
 
 def sa_attn_bwd(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6,
-                dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None):
-    """Backward of one layer. Returns (dq, dk, dv) with respect to the raw q, k, v.
-    rope = (cos, sin) rotary tables run sa_attn_bwd_rope instead."""
+                dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None, ve=None):
+    """Backward of one layer. Returns (dq, dk, dv) with respect to the raw q, k, v
+    (with ve also (dve, dw, dx32)); rope/ve as for sa_attn_fwd."""
+    if ve is not None:
+        return sa_attn_bwd_ex(q, k, v, o, lse, dout, window, softmax_scale, qk_norm, eps, dq, dk, dv, workspace,
+                              stream, rope, ve)
     if rope is not None:
         return sa_attn_bwd_rope(q, k, v, o, lse, dout, rope[0], rope[1], window, softmax_scale, qk_norm, eps,
                                 dq, dk, dv, workspace, stream)
@@ -340,6 +433,11 @@ def attention(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, ro
     """Differentiable layer: o = attention(q, k, v); gradients via sa_attn_bwd.
     rope = (cos, sin) fp32 device tables (see rope_tables) turns q and k first."""
     return _Attention.apply(q, k, v, window, softmax_scale, qk_norm, eps, rope)
+
+
+def ve_layers(n_layer: int):
+    """Layers that carry value embeddings: alternating, the last always ([guide] 8.2.1)."""
+    return [i for i in range(n_layer) if (n_layer - 1 - i) % 2 == 0]
 
 
 def rope_tables(n_pos: int, head_dim: int, base: float = 10000.0, device=None):

@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 // Benchmarking hook: events recorded around the main kernel of later calls
 // made from this host thread (see sa_set_timing_events).
@@ -94,9 +94,39 @@ sa_status check_rope(const float* cos, const float* sin, int stride, int T, int 
   return SA_OK;
 }
 
+// Validates optional value-embedding inputs: all four or none; x rows of
+// x_stride >= 32 elements (a multiple of 8), 16-byte aligned x, w and table,
+// 4-byte aligned ids; the table addressed with 32-bit offsets; only on the
+// QK-norm kernels (the forward's key/value prologue mixes the rows).
+sa_status check_ve(const void* x, int64_t x_stride, const void* w, const int32_t* ids, const void* table, int vocab,
+                   int Hkv, int head_dim, int qk_norm, sa::VeParams* out, uint32_t* table_bytes) {
+  *out = sa::VeParams{nullptr, 0, nullptr, nullptr, nullptr};
+  *table_bytes = 0;
+  const int given = (x != nullptr) + (w != nullptr) + (ids != nullptr) + (table != nullptr);
+  if (given == 0) return SA_OK;
+  if (given != 4) return SA_ERR_NULL;
+  if (!qk_norm) return SA_ERR_UNSUPPORTED;
+  if (vocab <= 0 || x_stride < 32 || x_stride % 8 != 0) return SA_ERR_SHAPE;
+  if (Hkv > sa::kVeMaxHeads) return SA_ERR_UNSUPPORTED;
+  if ((double)vocab * Hkv * head_dim * 2.0 >= 2147483648.0) return SA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(table) || !aligned4(ids)) return SA_ERR_ALIGN;
+  *out = sa::VeParams{x, (long)x_stride, w, ids, table};
+  *table_bytes = (uint32_t)((size_t)vocab * Hkv * head_dim * 2);
+  return SA_OK;
+}
+
+size_t ve_blocks(int B, int T) { return ((size_t)B * T + sa::kVeRows - 1) / sa::kVeRows; }
+
 }  // namespace
 
 SA_API int sa_abi_version(void) { return kAbiVersion; }
+
+SA_API size_t sa_attn_ve_workspace_bytes(int B, int T, int Hkv, int head_dim) {
+  if (check_shape(B, T, Hkv, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
+  const size_t rh = (size_t)B * T * Hkv;
+  // v' (bf16), gate and dz (fp32 per row and head), per-block partial sums of dw
+  return round256(rh * head_dim * 2) + 2 * round256(rh * 4) + round256(ve_blocks(B, T) * Hkv * 32 * 4);
+}
 
 SA_API const char* sa_status_string(int status) {
   switch (status) {
@@ -133,12 +163,17 @@ SA_API size_t sa_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int hea
 static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
                           size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
                           float softmax_scale, int qk_norm, float eps, const float* rope_cos, const float* rope_sin,
-                          int rope_stride, void* stream) {
+                          int rope_stride, const void* ve_x, int64_t ve_x_stride, const void* ve_w,
+                          const int32_t* ve_ids, const void* ve_table, int ve_vocab, void* stream) {
   const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
   if (st != SA_OK) return st;
   sa::Rope rope;
   const sa_status sr = check_rope(rope_cos, rope_sin, rope_stride, T, head_dim, qk_norm, &rope);
   if (sr != SA_OK) return sr;
+  sa::VeParams ve;
+  uint32_t ve_bytes = 0;
+  const sa_status sv = check_ve(ve_x, ve_x_stride, ve_w, ve_ids, ve_table, ve_vocab, Hkv, head_dim, qk_norm, &ve, &ve_bytes);
+  if (sv != SA_OK) return sv;
   if (!q || !k || !v || !o || !lse) return SA_ERR_NULL;
   if (qk_norm && (workspace == nullptr || workspace_bytes < sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim) ||
                   ((uintptr_t)workspace & 255u) != 0))
@@ -175,12 +210,12 @@ static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, 
     p.khat = workspace;
     p.vt = (char*)workspace + round256((size_t)B * T * Hkv * head_dim * 2);
     p.rope = rope;
-    sa::KvPrepParams kp{k, v, (void*)p.khat, (void*)p.vt, B, T, Hkv, p.Tp, eps, rope};
+    sa::KvPrepParams kp{k, v, (void*)p.khat, (void*)p.vt, B, T, Hkv, p.Tp, eps, rope, ve, ve_bytes};
     if (sa::launch_kv_prep(kp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
     return sa::launch_fwd_pp(p, head_dim, s, tl_events[SA_KERNEL_FWD]) == hipSuccess ? SA_OK : SA_ERR_HIP;
   }
-  // online-softmax kernel (logits without the QK-norm bound); no rotary tables there
-  if (rope.cos != nullptr) return SA_ERR_UNSUPPORTED;
+  // online-softmax kernel (logits without the QK-norm bound); no rotary tables or value embeddings there
+  if (rope.cos != nullptr || ve.x != nullptr) return SA_ERR_UNSUPPORTED;
   const int hpw = (p.G % 2 == 0) ? 2 : 1;
   p.nsub = p.G / hpw;
   p.nqb = (T + 127) / 128;
@@ -200,13 +235,27 @@ SA_API size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int hea
 static sa_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                           const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                           int B, int T, int Hq, int Hkv, int head_dim, int window, float softmax_scale, int qk_norm,
-                          float eps, const float* rope_cos, const float* rope_sin, int rope_stride, void* stream) {
+                          float eps, const float* rope_cos, const float* rope_sin, int rope_stride, const void* ve_x,
+                          int64_t ve_x_stride, const void* ve_w, const int32_t* ve_ids, const void* ve_table,
+                          int ve_vocab, void* dve, float* dve_w, float* dve_x32, void* ve_workspace,
+                          size_t ve_workspace_bytes, void* stream) {
   const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
   if (st != SA_OK) return st;
   sa::Rope rope;
   const sa_status sr = check_rope(rope_cos, rope_sin, rope_stride, T, head_dim, qk_norm, &rope);
   if (sr != SA_OK) return sr;
+  sa::VeParams ve;
+  uint32_t ve_bytes = 0;
+  const sa_status sv = check_ve(ve_x, ve_x_stride, ve_w, ve_ids, ve_table, ve_vocab, Hkv, head_dim, qk_norm, &ve, &ve_bytes);
+  if (sv != SA_OK) return sv;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SA_ERR_NULL;
+  if (ve.x != nullptr) {
+    if (!dve || !dve_w || !dve_x32) return SA_ERR_NULL;
+    if (!aligned16(dve) || !aligned4(dve_w) || !aligned4(dve_x32)) return SA_ERR_ALIGN;
+    if (ve_workspace == nullptr || ve_workspace_bytes < sa_attn_ve_workspace_bytes(B, T, Hkv, head_dim) ||
+        ((uintptr_t)ve_workspace & 255u) != 0)
+      return SA_ERR_WORKSPACE;
+  }
   const size_t need = sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim);
   if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
     return SA_ERR_WORKSPACE;
@@ -252,15 +301,34 @@ static sa_status attn_bwd(const void* q, const void* k, const void* v, const voi
     p.khat = khat;
   }
   p.rope = rope;
+  // value embeddings: the attention kernels run on v' = v + g ve, written once
+  const long nrows = (long)B * T;
+  const size_t rh = (size_t)nrows * Hkv;
+  char* vw = (char*)ve_workspace;
+  void* v_mixed = vw;
+  float* gate = (float*)(vw + round256(rh * head_dim * 2));
+  float* dz = (float*)((char*)gate + round256(rh * 4));
+  float* part = (float*)((char*)dz + round256(rh * 4));
+  if (ve.x != nullptr) {
+    sa::VePrepParams vp{ve, v, v_mixed, gate, nrows, Hkv, ve_bytes};
+    if (sa::launch_ve_prep(vp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+    p.v = v_mixed;
+  }
   if (sa::launch_bwd_dq_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DQ]) != hipSuccess) return SA_ERR_HIP;
-  return sa::launch_bwd_dkdv_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DKDV]) == hipSuccess ? SA_OK : SA_ERR_HIP;
+  if (sa::launch_bwd_dkdv_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DKDV]) != hipSuccess) return SA_ERR_HIP;
+  if (ve.x != nullptr) {
+    // dv holds dL/dv' (also the raw v's gradient); the gate's and embedding's gradients from it
+    sa::VeBwdParams bp{ve, dv, gate, dve, dz, dve_x32, part, dve_w, nrows, Hkv, ve_bytes};
+    if (sa::launch_ve_bwd(bp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+  }
+  return SA_OK;
 }
 
 SA_API sa_status sa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
                              size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
                              float softmax_scale, int qk_norm, float eps, void* stream) {
   return attn_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window, softmax_scale,
-                  qk_norm, eps, nullptr, nullptr, 0, stream);
+                  qk_norm, eps, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, 0, stream);
 }
 
 SA_API sa_status sa_attn_fwd_rope(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
@@ -269,7 +337,18 @@ SA_API sa_status sa_attn_fwd_rope(const void* q, const void* k, const void* v, v
                                   const float* rope_sin, int rope_stride, void* stream) {
   if (rope_cos == nullptr || rope_sin == nullptr) return SA_ERR_NULL;
   return attn_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window, softmax_scale,
-                  qk_norm, eps, rope_cos, rope_sin, rope_stride, stream);
+                  qk_norm, eps, rope_cos, rope_sin, rope_stride, nullptr, 0, nullptr, nullptr, nullptr, 0, stream);
+}
+
+SA_API sa_status sa_attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                                size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                                float softmax_scale, int qk_norm, float eps, const float* rope_cos,
+                                const float* rope_sin, int rope_stride, const void* ve_x, int64_t ve_x_stride,
+                                const void* ve_w, const int32_t* ve_ids, const void* ve_table, int ve_vocab,
+                                void* stream) {
+  return attn_fwd(q, k, v, o, lse, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window, softmax_scale,
+                  qk_norm, eps, rope_cos, rope_sin, rope_stride, ve_x, ve_x_stride, ve_w, ve_ids, ve_table, ve_vocab,
+                  stream);
 }
 
 SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -277,7 +356,8 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
                              float softmax_scale, int qk_norm, float eps, void* stream) {
   return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window,
-                  softmax_scale, qk_norm, eps, nullptr, nullptr, 0, stream);
+                  softmax_scale, qk_norm, eps, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, 0, nullptr,
+                  nullptr, nullptr, nullptr, 0, stream);
 }
 
 SA_API sa_status sa_attn_bwd_rope(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -287,7 +367,21 @@ SA_API sa_status sa_attn_bwd_rope(const void* q, const void* k, const void* v, c
                                   const float* rope_sin, int rope_stride, void* stream) {
   if (rope_cos == nullptr || rope_sin == nullptr) return SA_ERR_NULL;
   return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window,
-                  softmax_scale, qk_norm, eps, rope_cos, rope_sin, rope_stride, stream);
+                  softmax_scale, qk_norm, eps, rope_cos, rope_sin, rope_stride, nullptr, 0, nullptr, nullptr, nullptr,
+                  0, nullptr, nullptr, nullptr, nullptr, 0, stream);
+}
+
+SA_API sa_status sa_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                                float softmax_scale, int qk_norm, float eps, const float* rope_cos,
+                                const float* rope_sin, int rope_stride, const void* ve_x, int64_t ve_x_stride,
+                                const void* ve_w, const int32_t* ve_ids, const void* ve_table, int ve_vocab,
+                                void* dve, float* dve_w, float* dve_x32, void* ve_workspace,
+                                size_t ve_workspace_bytes, void* stream) {
+  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window,
+                  softmax_scale, qk_norm, eps, rope_cos, rope_sin, rope_stride, ve_x, ve_x_stride, ve_w, ve_ids,
+                  ve_table, ve_vocab, dve, dve_w, dve_x32, ve_workspace, ve_workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- polar express

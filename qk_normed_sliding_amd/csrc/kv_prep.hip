@@ -2,7 +2,8 @@
 // normed once ([post] QK-norm passage; [guide] 8.2.1) and written as k_hat in
 // the layout of k, and the value rows of each (batch, KV head) are written
 // transposed, as v_t[b][g][d][t] with the key axis padded with zeros to a
-// multiple of 64. With rotary tables the key rows are turned first (pairs
+// multiple of 64. With value embeddings the value rows are mixed first
+// (v + gate * embedding, ve_common.h). With rotary tables the key rows are turned first (pairs
 // of dimensions i and i + D/2 by the angle of the row's position; the norm
 // is unchanged by the turn). After it, the attention kernel's key and value tiles are
 // plain copies that go straight from memory into LDS, and both are read
@@ -10,6 +11,7 @@
 // HBM-bound: each k and v element is read once and written once.
 #include "sa_common.h"
 #include "sa_kernels.h"
+#include "ve_common.h"
 
 namespace sa {
 
@@ -27,6 +29,8 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepParams p) {
   const int bg = blockIdx.y;  // b * Hkv + g
   const int b = bg / p.Hkv, g = bg % p.Hkv;
   const int sub = threadIdx.x % CPR;
+  const bool ve_on = p.ve.x != nullptr;
+  const auto rt = make_rsrc(p.ve.table, p.ve_table_bytes);
 
   for (int r = threadIdx.x / CPR; r < 64; r += RPP) {
     const int t = t0 + r;
@@ -36,6 +40,17 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepParams p) {
     if (in) {
       kw = ld16((const bf16*)p.k + off);
       vw = ld16((const bf16*)p.v + off);
+      if (ve_on) {
+        // value-embedding gate: v + 2 sigmoid(x[:32] . w[g]) table[id][g]
+        const long row = (long)b * p.T + t;
+        const float gt = ve_gate_of(p.ve, row, g);
+        float vv[8], ee[8];
+        unpack8(vw, vv);
+        unpack8(ve_chunk(p.ve, rt, p.ve_table_bytes, row, p.Hkv, D, g, sub), ee);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vv[e] = __builtin_fmaf(gt, ee[e], vv[e]);
+        vw = pack8(vv);
+      }
     }
     float x[8];
     unpack8(kw, x);

@@ -15,6 +15,43 @@ struct Rope {
   int stride;
 };
 
+// Value-embedding gate inputs (x == nullptr: none): x bf16 rows of x_stride
+// elements (the first 32 read), w bf16 [Hkv][32], ids int32 [B*T], table
+// bf16 [vocab][Hkv*D] (read through a buffer of table_bytes: ids past it read zeros).
+struct VeParams {
+  const void* x;
+  long x_stride;
+  const void* w;
+  const int32_t* ids;
+  const void* table;
+};
+constexpr int kVeRows = 64;  // rows per block of the gate backward's partial sums
+constexpr int kVeMaxHeads = 16;  // KV heads the value-embedding gate supports
+
+struct VePrepParams {
+  VeParams ve;
+  const void* v;
+  void* v_mixed;   // bf16 [rows, Hkv, D]
+  float* gate;     // fp32 [rows, Hkv]
+  long rows;       // B * T
+  int Hkv;
+  uint32_t table_bytes;
+};
+
+struct VeBwdParams {
+  VeParams ve;
+  const void* dv;      // dL/dv' (bf16 [rows, Hkv, D])
+  const float* gate;   // as written by ve_prep
+  void* dve;           // bf16 [rows, Hkv, D]
+  float* dz;           // fp32 [rows, Hkv] (workspace)
+  float* dx32;         // fp32 [rows, 32]
+  float* part;         // fp32 [ceil(rows / kVeRows), Hkv, 32] (workspace)
+  float* dw;           // fp32 [Hkv, 32]
+  long rows;
+  int Hkv;
+  uint32_t table_bytes;
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -45,6 +82,8 @@ struct KvPrepParams {
   int B, T, Hkv, Tp;
   float eps;
   Rope rope;   // rotary tables for k (turned before the norm)
+  VeParams ve; // value-embedding gate mixed into v (ve.x == nullptr: none)
+  uint32_t ve_table_bytes;
 };
 
 struct BwdParams {
@@ -119,6 +158,9 @@ hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t st
 hipError_t launch_fro_scale(const void* x, void* y, float* part, int batch, long per_matrix, float eps,
                             hipStream_t stream);
 hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, hipStream_t stream);
+// Value-embedding gate: v' and g for the backward; then dve, dx32 and dw from dL/dv'.
+hipError_t launch_ve_prep(const VePrepParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_ve_bwd(const VeBwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace sa

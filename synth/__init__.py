@@ -130,6 +130,23 @@ def layer_inputs(w: Workload, layer: int, qk_rows_only: bool = False):
     return q, k, v, do
 
 
+VE_VOCAB = 8192  # the trainer's VOCAB_SIZE (the guide's constants table)
+VE_CHANNELS = 768  # n_embd: the rows the gate reads the first 32 channels of
+
+
+def ve_inputs(w: Workload, layer: int):
+    """Seeded value-embedding inputs of one layer: x [B, T, 768] bf16 (the
+    attention's input rows), gate weights [Hkv, 32] bf16 ~ N(0, 0.2^2) (zero at
+    the trainer's start; a spread here so the gate varies), token ids [B, T]
+    int32 uniform over the vocabulary, embedding table [8192, Hkv*D] bf16."""
+    s = [seed_for(w.cfg, layer, t) for t in range(8, 12)]
+    x = _randn_bf16((w.B, w.T, VE_CHANNELS), s[0], w.chunked)
+    gw = (0.2 * torch.randn((w.Hkv, 32), generator=torch.Generator().manual_seed(s[1]))).to(torch.bfloat16)
+    ids = torch.randint(0, VE_VOCAB, (w.B, w.T), generator=torch.Generator().manual_seed(s[2]), dtype=torch.int32)
+    table = _randn_bf16((VE_VOCAB, w.Hkv * w.D), s[3])
+    return x, gw, ids, table
+
+
 def small_case(B, T, Hq, Hkv, D, seed=7, with_do=True, dtype=torch.bfloat16):
     """Small seeded case for parity tests at sizes the oracle finishes in seconds."""
     q, k, v, do = random_qkvdo(B, T, Hq, Hkv, D, seed, seed + 1, seed + 2, seed + 3, with_do)

@@ -78,9 +78,10 @@ def compare_forward(o, lse, q, k, v, W, scale, qk_norm=True, eps=1e-6, o_tol=O_M
     return o_ref, lse_ref
 
 
-def compare_backward(dq, dk, dv, q, k, v, do, W, scale, qk_norm=True, eps=1e-6, tol=GRAD_REL_L2, rope=None):
+def compare_backward(dq, dk, dv, q, k, v, do, W, scale, qk_norm=True, eps=1e-6, tol=GRAD_REL_L2, rope=None,
+                     ve=None):
     dq_r, dk_r, dv_r = oracle.attn_backward(q, k, v, do, W, scale, qk_norm=qk_norm, eps=eps,
-                                            rope=oracle_rope(rope))
+                                            rope=oracle_rope(rope), ve=ve)[:3]
     errs = {n: rel_l2(a.cpu(), r) for n, a, r in (("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r))}
     log("  rel-L2 " + "  ".join(f"{n} {e:.3e}" for n, e in errs.items()))
     for n, a in (("dq", dq), ("dk", dk), ("dv", dv)):

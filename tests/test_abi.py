@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("sa_qknorm", "sa_attn_fwd", "sa_attn_fwd_workspace_bytes", "sa_attn_bwd", "sa_attn_bwd_workspace_bytes",
               "sa_status_string", "sa_abi_version", "sa_attn_fwd_rope", "sa_attn_bwd_rope",
-              "sa_polar_express", "sa_polar_express_workspace_bytes"):
+              "sa_polar_express", "sa_polar_express_workspace_bytes", "sa_attn_fwd_ex", "sa_attn_bwd_ex",
+              "sa_attn_ve_workspace_bytes"):
         assert n in names
 
 
@@ -226,3 +227,41 @@ def test_polar_express_validation_paths(sa):
     assert call(ws=0) == SA_ERR_WORKSPACE
     assert call(ws_bytes=100) == SA_ERR_WORKSPACE
     assert call(ws=128) == SA_ERR_WORKSPACE
+
+
+def test_value_embedding_validation_paths(sa):
+    lib = sa.library()
+    P = ctypes.c_void_p
+    B, T, Hq, Hkv, D = 1, 8, 4, 2, 64
+    r256 = lambda x: (x + 255) // 256 * 256
+    rh = B * T * Hkv
+    assert lib.sa_attn_ve_workspace_bytes(B, T, Hkv, D) == r256(rh * D * 2) + 2 * r256(rh * 4) + r256(1 * Hkv * 32 * 4)
+
+    def fwd(x=4096, xs=768, w=8192, ids=12288, tab=16384, vocab=100, norm=1):
+        ws = lib.sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D)
+        return lib.sa_attn_fwd_ex(P(16), P(16), P(16), P(16), P(16), P(256), ws, B, T, Hq, Hkv, D, -1, 0.125, norm,
+                                  1e-6, None, None, 0, P(x), xs, P(w), P(ids), P(tab), vocab, None)
+
+    def bwd(dve=20480, dw=24576, dx=28672, vws=32768, vws_bytes=None, ids=12288):
+        ws = lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D)
+        need = lib.sa_attn_ve_workspace_bytes(B, T, Hkv, D) if vws_bytes is None else vws_bytes
+        return lib.sa_attn_bwd_ex(P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(256), ws,
+                                  B, T, Hq, Hkv, D, -1, 0.125, 1, 1e-6, None, None, 0,
+                                  P(4096), 768, P(8192), P(ids), P(16384), 100,
+                                  P(dve), P(dw), P(dx), P(vws), need, None)
+
+    assert fwd(ids=0) == SA_ERR_NULL            # a partial group
+    assert fwd(tab=0) == SA_ERR_NULL
+    assert fwd(xs=16) == SA_ERR_SHAPE           # fewer than 32 channels
+    assert fwd(xs=100) == SA_ERR_SHAPE          # rows not 16-byte aligned
+    assert fwd(vocab=0) == SA_ERR_SHAPE
+    assert fwd(vocab=1 << 24) == SA_ERR_SHAPE   # table past 32-bit offsets
+    assert fwd(x=4100) == SA_ERR_ALIGN
+    assert fwd(ids=12290) == SA_ERR_ALIGN
+    assert fwd(norm=0) == SA_ERR_UNSUPPORTED
+    assert bwd(dve=0) == SA_ERR_NULL
+    assert bwd(dw=0) == SA_ERR_NULL
+    assert bwd(dve=20488) == SA_ERR_ALIGN
+    assert bwd(vws=0) == SA_ERR_WORKSPACE
+    assert bwd(vws_bytes=64) == SA_ERR_WORKSPACE
+    assert bwd(vws=32768 + 128) == SA_ERR_WORKSPACE

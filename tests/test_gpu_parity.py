@@ -322,3 +322,90 @@ def test_backward_is_deterministic(sa):
         sa.sa_set_max_workgroups(0)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+
+VE_CASES = [
+    # B, T, Hq, Hkv, D, W, vocab, rope
+    (2, 300, 4, 2, 128, -1, 97, False),
+    (1, 513, 6, 3, 128, 256, 500, True),     # with the rotary tables as well
+    (1, 400, 6, 6, 64, 100, 64, False),      # MHA, D = 64
+    (2, 129, 3, 1, 128, 0, 31, False),       # G = 3, window 0
+]
+
+
+def _check_o_mixed(o, lse, o_r, lse_r):
+    """The mixed rows v' = v + g ve reach |v'| ~ 8 (g up to 2, two N(0,1) terms),
+    and a row that sees few keys returns v' itself through two bf16 roundings
+    (v' staged for the matrix cores, O stored), each up to 2^-8 relative: O is
+    held to |diff| <= 2e-2 + 2^-7 |O_ref| elementwise, as for the workload whose
+    rows are scaled by 8; LSE to the plain bound."""
+    diff = (o.cpu().double() - o_r).abs()
+    el = max_abs(lse.cpu(), lse_r)
+    log(f"  O max-abs {float(diff.max()):.3e} (mixed bound)  LSE max-abs {el:.3e}")
+    assert bool((diff <= O_MAX_ABS + 2.0 ** -7 * o_r.abs()).all())
+    assert el <= LSE_MAX_ABS
+
+
+def _ve_case_inputs(B, T, Hkv, D, V, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((B, T, 768), generator=g).to(torch.bfloat16)
+    w = (0.3 * torch.randn((Hkv, 32), generator=g)).to(torch.bfloat16)
+    ids = torch.randint(0, V, (B, T), generator=g, dtype=torch.int32)
+    table = torch.randn((V, Hkv * D), generator=g).to(torch.bfloat16)
+    return x, w, ids, table
+
+
+@pytest.mark.parametrize("case", VE_CASES, ids=[f"B{c[0]}T{c[1]}Hq{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}V{c[6]}r{int(c[7])}"
+                                                for c in VE_CASES])
+def test_value_embedding_forward_backward(sa, case):
+    """v' = v + 2 sigmoid(x[:32] w^T) table[ids], fused into the key/value
+    prologue (forward) and the backward's value passes, against the oracle:
+    outputs, the attention gradients, and dve, dw, dx32 (rel-L2 5e-2)."""
+    B, T, Hq, Hkv, D, W, V, use_rope = case
+    scale = D ** -0.5
+    log(f"[ve] {case}")
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=900 + T)
+    x, w, ids, table = _ve_case_inputs(B, T, Hkv, D, V, 910 + T)
+    rope = sa.rope_tables(T, D, device="cuda") if use_rope else None
+    ve_dev = tuple(t.cuda() for t in (x, w, ids, table))
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = sa.sa_attn_fwd(qd, kd, vd, window=W, softmax_scale=scale, rope=rope, ve=ve_dev)
+    dq, dk, dv, dve, dw, dx32 = sa.sa_attn_bwd(qd, kd, vd, o, lse, dod, window=W, softmax_scale=scale, rope=rope,
+                                               ve=ve_dev)
+    torch.cuda.synchronize()
+    ve_ref = (x[..., :32], w, ids, table)
+    rope_ref = None if rope is None else tuple(t.double().cpu() for t in rope)
+    o_r, lse_r = oracle.attn_forward(q, k, v, W, scale, rope=rope_ref, ve=ve_ref)
+    _check_o_mixed(o, lse, o_r, lse_r)
+    ref = oracle.attn_backward(q, k, v, do, W, scale, rope=rope_ref, ve=ve_ref)
+    names = ("dq", "dk", "dv", "dve", "dw", "dx32")
+    errs = {}
+    for n, a, r in zip(names, (dq, dk, dv, dve, dw, dx32), ref):
+        assert torch.isfinite(a.float()).all(), n
+        if float(r.norm()) <= 1e-9 * r.numel() ** 0.5:
+            errs[n] = max_abs(a.cpu(), r)
+            assert errs[n] <= 1e-1, n
+        else:
+            errs[n] = rel_l2(a.cpu(), r)
+            assert errs[n] <= 5e-2, (n, errs[n])
+    log("  " + "  ".join(f"{n} {e:.3e}" for n, e in errs.items()))
+
+
+def test_value_embedding_ids_outside_the_table_read_zero_rows(sa):
+    """An id outside [0, vocab) contributes a zero embedding row: same result
+    as the oracle with that id pointing at an appended zero row."""
+    B, T, Hq, Hkv, D, W, V = 1, 200, 4, 2, 128, 64, 50
+    q, k, v, do = synth.small_case(B, T, Hq, Hkv, D, seed=77)
+    x, w, ids, table = _ve_case_inputs(B, T, Hkv, D, V, 78)
+    ids[0, 5] = V + 3
+    ids[0, 9] = -2
+    ids[0, 150] = 1 << 30
+    o, lse = sa.sa_attn_fwd(*(t.cuda() for t in (q, k, v)), window=W, softmax_scale=D ** -0.5,
+                            ve=tuple(t.cuda() for t in (x, w, ids, table)))
+    torch.cuda.synchronize()
+    ids_ref = ids.clone()
+    ids_ref[(ids < 0) | (ids >= V)] = V
+    table_ref = torch.cat([table, torch.zeros(1, Hkv * D, dtype=table.dtype)])
+    o_r, lse_r = oracle.attn_forward(q, k, v, W, D ** -0.5, ve=(x[..., :32], w, ids_ref, table_ref))
+    _check_o_mixed(o, lse, o_r, lse_r)
