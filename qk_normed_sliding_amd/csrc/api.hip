@@ -402,9 +402,39 @@ sa_status check_polar(int batch, int rows, int cols, int steps, float eps) {
   if (rows % 128 != 0 || cols % 128 != 0) return SA_ERR_UNSUPPORTED;
   if ((double)rows * cols * 2.0 >= 2147483648.0 || (double)batch * rows * cols > 9.0e18) return SA_ERR_SHAPE;
   if (batch > 65535) return SA_ERR_SHAPE;
+  // one-dimensional GEMM grids: batch x tiles x (at most 8 K splits) x 256 threads below 2^31
+  if ((long)batch * (rows / 128) * (cols / 128) >= (1L << 20)) return SA_ERR_SHAPE;
   if (steps < 1 || steps > 5) return SA_ERR_SHAPE;
   if (!isfinite(eps) || eps < 0.f) return SA_ERR_SHAPE;
   return SA_OK;
+}
+
+// K splits of a GEMM with `jobs` workgroups (computed tiles x batch): the
+// fewest equal ranges (multiples of 64, at least 256 long) that give 512
+// workgroups, enough to fill the compute units twice over.
+int polar_splits(long jobs, int K) {
+  int best = 1;
+  for (int sp : {1, 2, 3, 4, 6, 8}) {
+    if (K % (64 * sp) != 0 || K / sp < 256) continue;
+    best = sp;
+    if (jobs * sp >= 512) break;
+  }
+  return best;
+}
+
+// The two symmetric products of a step on [m][n] matrices: A = X X^T (K = n)
+// and A A (K = m), both with upper tiles only; their splits and the floats
+// of split partials they need.
+struct PolarPlan {
+  int s_xx, s_aa;
+  size_t part_floats;
+};
+PolarPlan polar_plan(int batch, int m, int n) {
+  const long jobs = (long)sa::gemm_tiles(m, m, 1) * batch;
+  PolarPlan pl{polar_splits(jobs, n), polar_splits(jobs, m), 0};
+  const int smax = pl.s_xx > pl.s_aa ? pl.s_xx : pl.s_aa;
+  pl.part_floats = smax > 1 ? (size_t)jobs * smax * 128 * 128 : 0;
+  return pl;
 }
 
 }  // namespace
@@ -412,9 +442,11 @@ sa_status check_polar(int batch, int rows, int cols, int steps, float eps) {
 SA_API size_t sa_polar_express_workspace_bytes(int batch, int rows, int cols) {
   if (check_polar(batch, rows, cols, 5, 0.f) != SA_OK) return 0;
   const size_t m = (size_t)(rows < cols ? rows : cols), n = (size_t)(rows < cols ? cols : rows);
-  // X (two buffers, wide side [m][n]), A and B ([m][m]), partial sums of the norm
+  const PolarPlan pl = polar_plan(batch, (int)m, (int)n);
+  // X (two buffers, wide side [m][n]), A and B ([m][m]), partial sums of the
+  // norm, split-K partial tiles
   return 2 * round256((size_t)batch * m * n * 2) + 2 * round256((size_t)batch * m * m * 2) +
-         round256((size_t)batch * sa::kFroChunks * 4);
+         round256((size_t)batch * sa::kFroChunks * 4) + round256(pl.part_floats * 4);
 }
 
 SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, size_t workspace_bytes, int batch,
@@ -435,6 +467,8 @@ SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, siz
   void* A = (char*)x1 + round256((size_t)batch * m * n * 2);
   void* Bm = (char*)A + round256((size_t)batch * m * m * 2);
   float* part = (float*)((char*)Bm + round256((size_t)batch * m * m * 2));
+  const PolarPlan pl = polar_plan(batch, m, n);
+  float* kpart = (float*)((char*)part + round256((size_t)batch * sa::kFroChunks * 4));
   // wide view of the input: the transpose of a tall matrix
   const void* src = g;
   if (tall) {
@@ -446,11 +480,11 @@ SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, siz
   void* nxt = x1;
   for (int k = 0; k < steps; ++k) {
     const float a = kPolarCoeffs[k][0], b = kPolarCoeffs[k][1], c = kPolarCoeffs[k][2];
-    // A = X X^T
-    sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f};
+    // A = X X^T (symmetric: upper tiles only)
+    sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f, 1, pl.s_xx, kpart};
     if (sa::launch_gemm(pg, false, batch, s) != hipSuccess) return SA_ERR_HIP;
-    // B = c A A + b A  (A is symmetric: A A = A A^T)
-    sa::GemmParams pb{A, A, A, Bm, m, m, m, c, b};
+    // B = c A A + b A  (A is symmetric: A A = A A^T, and so is B)
+    sa::GemmParams pb{A, A, A, Bm, m, m, m, c, b, 1, pl.s_aa, kpart};
     if (sa::launch_gemm(pb, false, batch, s) != hipSuccess) return SA_ERR_HIP;
     // X <- B X + a X, straight into the output on the last step of a wide matrix
     void* dst = (k == steps - 1 && !tall) ? out : nxt;

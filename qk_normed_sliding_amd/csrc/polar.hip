@@ -14,10 +14,42 @@
 // XOR-swizzled so that the operand reads are bank-conflict free. The MFMA
 // takes the N-side operand first, so each lane's accumulators hold one row of
 // C (16 columns) and the epilogue stores 8 bytes per (lane, register quad).
+// A symmetric product (X X^T, and A A with A symmetric) computes only the
+// tiles on and above the diagonal and stores each off-diagonal tile mirrored
+// as well. A product with few tiles and a long K splits K into equal ranges:
+// each workgroup writes its fp32 partial tile and a second kernel adds the
+// partials in a fixed order, applies alpha and beta and stores C (mirrored
+// too when symmetric).
 #include "sa_common.h"
 #include "sa_kernels.h"
 
 namespace sa {
+
+// Tile (tm, tn) of computed tile t: row-major over all tiles, or over the
+// tiles with tm <= tn of a symmetric product.
+__device__ __forceinline__ void tile_of(int t, int tiles_n, int sym, int& tm, int& tn) {
+  if (sym) {
+    tm = 0;
+    while (t >= tiles_n - tm) {
+      t -= tiles_n - tm;
+      ++tm;
+    }
+    tn = tm + t;
+  } else {
+    tm = t / tiles_n;
+    tn = t % tiles_n;
+  }
+}
+
+// Work item of the workgroup with linear id L out of n, dealt round-robin to
+// 8 XCDs: XCD x = L % 8 runs items [start(x), start(x + 1)) in order.
+__device__ __forceinline__ int xcd_item(int L, int n) {
+  constexpr int kXcds = 8;
+  const int x = L % kXcds, slot = L / kXcds;
+  const int per = n / kXcds, rem = n % kXcds;
+  const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return start + slot;
+}
 
 template <bool BN>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
@@ -32,9 +64,20 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   const int l32 = lane & 31;
   const int wm = w >> 1, wn = w & 1;  // this wave's 64 x 64 quarter of the tile
   const int tiles_n = p.N / TN;
-  const int m0 = (blockIdx.x / tiles_n) * TM;
-  const int n0 = (blockIdx.x % tiles_n) * TN;
-  const long bz = blockIdx.y;
+  const int splits = p.splits > 1 ? p.splits : 1;
+  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
+  // work item w = (matrix, tile, split) in that order goes to the XCD that
+  // runs a contiguous range of items, so the tiles of a matrix, which share
+  // its row and column panels, meet in one L2.
+  const int per_mat = gemm_tiles(p.M, p.N, p.sym) * splits;
+  const int w_item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+  const int tile = (w_item % per_mat) / splits, sp = w_item % splits;
+  int tm, tn;
+  tile_of(tile, tiles_n, p.sym, tm, tn);
+  const int m0 = tm * TM;
+  const int n0 = tn * TN;
+  const long bz = w_item / per_mat;
+  const int kbeg = sp * (p.K / splits);  // this workgroup's range of K
 
   const bf16* A = (const bf16*)p.a + bz * p.M * p.K;
   const bf16* B = (const bf16*)p.b + bz * p.N * p.K;
@@ -57,7 +100,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     }
   }
   auto issue = [&](int ks, int st) {
-    const int k0 = ks * TK;
+    const int k0 = kbeg + ks * TK;
     const uint32_t la = lds_addr(&As[st][0]);
     const uint32_t lb = lds_addr(&Bs[st][0]);
 #pragma unroll
@@ -102,7 +145,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
-  const int nk = p.K / TK;
+  const int nk = p.K / splits / TK;
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -133,8 +176,26 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  // epilogue: C = alpha acc + beta C0 (bf16)
+  if (splits > 1) {  // fp32 partial tile, row-major 128 x 128
+    float* dst = p.part + (((long)bz * splits + sp) * gemm_tiles(p.M, p.N, p.sym) + tile) * (TM * TN);
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 32 * (2 * wm + y) + l32, c = 32 * (2 * wn + x) + 8 * i + 4 * half;
+          *(f32x4*)(dst + r * TN + c) = f32x4{acc[x][y][4 * i], acc[x][y][4 * i + 1], acc[x][y][4 * i + 2],
+                                             acc[x][y][4 * i + 3]};
+        }
+    return;
+  }
+
+  // epilogue: C = alpha acc + beta C0 (bf16); an off-diagonal tile of a
+  // symmetric product also goes to its mirror position, where 32 lanes
+  // store 32 consecutive elements of a row per instruction
   const long cbase = bz * p.M * p.N;
+  const bool mirror = p.sym && tm != tn;
 #pragma unroll
   for (int y = 0; y < 2; ++y) {
     const long row = m0 + 32 * (2 * wm + y) + l32;
@@ -157,8 +218,74 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
         o[0] = pack2(v[0], v[1]);
         o[1] = pack2(v[2], v[3]);
         *(u32x2*)((bf16*)p.c + off) = o;
+        if (mirror) {
+          const long col = n0 + 32 * (2 * wn + x) + 8 * i + 4 * half;
+          unsigned short* mc = (unsigned short*)p.c + cbase + col * p.M + row;
+          mc[0] = (unsigned short)(o[0] & 0xffffu);
+          mc[p.M] = (unsigned short)(o[0] >> 16);
+          mc[2L * p.M] = (unsigned short)(o[1] & 0xffffu);
+          mc[3L * p.M] = (unsigned short)(o[1] >> 16);
+        }
       }
   }
+}
+
+// Split-K reduction: the 64 x 64 quarter blockIdx.x % 4 of computed tile
+// blockIdx.x / 4 of matrix blockIdx.y. Thread (r, q) adds the partials of
+// row r, columns 16q .. 16q + 15 in split order, applies alpha and beta and
+// stores 32 bytes; the mirror goes through an LDS transpose.
+__global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
+  __shared__ unsigned short t[64][72];
+  const int tile = blockIdx.x / 4, qr = (blockIdx.x / 2) & 1, qc = blockIdx.x & 1;
+  int tm, tn;
+  tile_of(tile, p.N / 128, p.sym, tm, tn);
+  const long bz = blockIdx.y;
+  const int ntile = gemm_tiles(p.M, p.N, p.sym);
+  const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const int lr = 64 * qr + r, lc = 64 * qc + 16 * q;  // within the 128 x 128 tile
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float* src = p.part + (((long)bz * p.splits + s) * ntile + tile) * (128 * 128) + lr * 128 + lc;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x4 x = *(const f32x4*)(src + 4 * e4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * e4 + e] += x[e];
+    }
+  }
+  const long row = tm * 128 + lr, col = tn * 128 + lc;
+  const long off = bz * p.M * p.N + row * p.N + col;
+  float c0[16];
+  if (p.c0 != nullptr) {
+    unpack8(ld16((const bf16*)p.c0 + off), c0);
+    unpack8(ld16((const bf16*)p.c0 + off + 8), c0 + 8);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = p.alpha * v[e] + (p.c0 != nullptr ? p.beta * c0[e] : 0.f);
+  const u32x4 w0 = pack8(v), w1 = pack8(v + 8);
+  st16((bf16*)p.c + off, w0);
+  st16((bf16*)p.c + off + 8, w1);
+  if (!(p.sym && tm != tn)) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    t[r][16 * q + 2 * e] = (unsigned short)(w0[e] & 0xffffu);
+    t[r][16 * q + 2 * e + 1] = (unsigned short)(w0[e] >> 16);
+    t[r][16 * q + 8 + 2 * e] = (unsigned short)(w1[e] & 0xffffu);
+    t[r][16 * q + 8 + 2 * e + 1] = (unsigned short)(w1[e] >> 16);
+  }
+  __syncthreads();
+  // mirror: row col' = column (64qc + r) of the quarter, 16 consecutive rows 16q .. of the quarter
+  u32x4 m0v, m1v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m0v[e] = (uint32_t)t[16 * q + 2 * e][r] | ((uint32_t)t[16 * q + 2 * e + 1][r] << 16);
+    m1v[e] = (uint32_t)t[16 * q + 8 + 2 * e][r] | ((uint32_t)t[16 * q + 8 + 2 * e + 1][r] << 16);
+  }
+  const long moff = bz * p.M * p.N + (long)(tn * 128 + 64 * qc + r) * p.M + tm * 128 + 64 * qr + 16 * q;
+  st16((bf16*)p.c + moff, m0v);
+  st16((bf16*)p.c + moff + 8, m1v);
 }
 
 // Sum of squares of chunk blockIdx.x of matrix blockIdx.y (elements
@@ -218,11 +345,16 @@ __global__ void __launch_bounds__(256) transpose_kernel(const bf16* in, bf16* ou
 }
 
 hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.M / 128) * (p.N / 128)), (unsigned)batch);
+  const int splits = p.splits > 1 ? p.splits : 1;
+  const int ntile = gemm_tiles(p.M, p.N, p.sym);
+  const dim3 grid((unsigned)(ntile * splits * batch));
   if (b_kn)
     hipLaunchKernelGGL((gemm_kernel<true>), grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((gemm_kernel<false>), grid, dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(ntile * 4), (unsigned)batch), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

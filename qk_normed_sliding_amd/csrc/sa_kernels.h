@@ -132,7 +132,15 @@ struct GemmParams {
   void* c;
   int M, N, K;
   float alpha, beta;
+  int sym;         // C is symmetric (M == N): only tiles on or above the diagonal are computed, each stored mirrored too
+  int splits;      // K in this many equal ranges (0 or 1: none); fp32 partial tiles in part, summed by a second kernel
+  float* part;     // batch * splits * (computed tiles) * 128 * 128 floats
 };
+// Tiles of C that a GEMM computes (all, or those on and above the diagonal).
+__host__ __device__ inline int gemm_tiles(int M, int N, int sym) {
+  const int tm = M / 128, tn = N / 128;
+  return sym ? tm * (tm + 1) / 2 : tm * tn;
+}
 constexpr int kFroChunks = 64;  // partial sums per matrix of the Frobenius norm
 
 // Optional events recorded around a call's main kernel (benchmarking hook).

@@ -203,11 +203,21 @@ def test_polar_express_validation_paths(sa):
     lib = sa.library()
     P = ctypes.c_void_p
     r256 = lambda x: (x + 255) // 256 * 256
-    # two X buffers on the wide side, A and B, 64 partial sums per matrix
+    # two X buffers on the wide side, A and B, 64 partial sums per matrix, and
+    # split-K partial tiles: the Gram X X^T (K = 3072) of 8 matrices has 21
+    # upper tiles each, 168 workgroups, so its K is split in 4 (672 >= 512
+    # workgroups); A A (K = 768) in 3 (ranges of at least 256): 4 x 168 fp32
+    # tiles of 128 x 128
     assert lib.sa_polar_express_workspace_bytes(8, 768, 3072) == 2 * r256(8 * 768 * 3072 * 2) + 2 * r256(
-        8 * 768 * 768 * 2) + r256(8 * 64 * 4)
+        8 * 768 * 768 * 2) + r256(8 * 64 * 4) + r256(4 * 168 * 128 * 128 * 4)
+    # 32 matrices of 768 x 768: 672 workgroups per Gram, no split, no partials
+    assert lib.sa_polar_express_workspace_bytes(32, 768, 768) == 2 * r256(32 * 768 * 768 * 2) + 2 * r256(
+        32 * 768 * 768 * 2) + r256(32 * 64 * 4)
     assert lib.sa_polar_express_workspace_bytes(8, 3072, 768) == lib.sa_polar_express_workspace_bytes(8, 768, 3072)
     assert lib.sa_polar_express_workspace_bytes(1, 100, 128) == 0
+    # the GEMM grids are one-dimensional: batch x 128-tiles stays below 2^20
+    assert lib.sa_polar_express_workspace_bytes(4096, 2048, 2048) == 0
+    assert lib.sa_polar_express_workspace_bytes(4095, 2048, 2048) > 0
 
     def call(g=16, out=32, ws=256, ws_bytes=None, batch=2, rows=256, cols=384, steps=5, eps=1e-7):
         need = lib.sa_polar_express_workspace_bytes(batch, rows, cols)

@@ -56,7 +56,11 @@ def _check(sa, g, steps=5, idx=None):
     return out
 
 
-@pytest.mark.parametrize("shape", [(3, 256, 384), (2, 384, 256), (2, 256, 256), (1, 128, 640)])
+# (1, 128, 640): one tile, K split in 2; (1, 256, 1024): the Gram's K split
+# in 4 with a mirrored off-diagonal tile; (2, 512, 1536): Gram split in 6,
+# A A split in 2, both with mirrored tiles
+@pytest.mark.parametrize("shape", [(3, 256, 384), (2, 384, 256), (2, 256, 256), (1, 128, 640), (1, 256, 1024),
+                                   (2, 512, 1536)])
 def test_polar_express_small(sa, shape):
     log(f"[polar] {shape}")
     _check(sa, _grad(shape, 300 + shape[1]))
