@@ -326,21 +326,27 @@ __global__ void __launch_bounds__(256) scale_kernel(const bf16* x, bf16* y, cons
   }
 }
 
-// out[b][c][r] = in[b][r][c] for 64 x 64 tiles (R, C multiples of 64).
+// out[b][c][r] = in[b][r][c] for 64 x 64 tiles (R, C multiples of 64): 16-byte
+// loads of input rows into an LDS tile, 16-byte stores of output rows read
+// down its columns.
 __global__ void __launch_bounds__(256) transpose_kernel(const bf16* in, bf16* out, int R, int C) {
-  __shared__ unsigned short t[64][66];
+  __shared__ unsigned short t[64][72];  // rows padded to 144 bytes (16-byte aligned)
   const int tr = blockIdx.x / (C / 64), tc = blockIdx.x % (C / 64);
   const long mb = (long)blockIdx.y * R * C;
-  const unsigned short* src = (const unsigned short*)in + mb;
-  unsigned short* dst = (unsigned short*)out + mb;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int r = e / 64, c = e % 64;
-    t[r][c] = src[(long)(64 * tr + r) * C + 64 * tc + c];
+  const int r = threadIdx.x >> 3, c8 = 8 * (threadIdx.x & 7);  // rows r and r + 32, columns c8 .. c8 + 7
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 w = ld16(in + mb + (long)(64 * tr + r + 32 * h) * C + 64 * tc + c8);
+    *(u32x4*)&t[r + 32 * h][c8] = w;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int c = e / 64, r = e % 64;
-    dst[(long)(64 * tc + c) * R + 64 * tr + r] = t[r][c];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int oc = r + 32 * h;  // output row: input column 64 tc + oc; output columns c8 .. c8 + 7 = input rows
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)t[c8 + 2 * e][oc] | ((uint32_t)t[c8 + 2 * e + 1][oc] << 16);
+    st16(out + mb + (long)(64 * tc + oc) * R + 64 * tr + c8, w);
   }
 }
 
