@@ -32,25 +32,39 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepParams p) {
   const bool ve_on = p.ve.x != nullptr;
   const auto rt = make_rsrc(p.ve.table, p.ve_table_bytes);
 
-  for (int r = threadIdx.x / CPR; r < 64; r += RPP) {
+  // every row's loads first (the stores below could alias them for the
+  // compiler, which would then keep each pass's loads behind the previous
+  // pass's stores)
+  constexpr int NP = 64 / RPP;  // passes over the workgroup's 64 rows
+  u32x4 kws[NP], vws[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int t = t0 + threadIdx.x / CPR + i * RPP;
+    kws[i] = vws[i] = u32x4{0u, 0u, 0u, 0u};
+    if (t < p.T) {
+      const long off = (((long)b * p.T + t) * p.Hkv + g) * D + 8 * sub;
+      kws[i] = ld16((const bf16*)p.k + off);
+      vws[i] = ld16((const bf16*)p.v + off);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int r = threadIdx.x / CPR + i * RPP;
     const int t = t0 + r;
     const bool in = t < p.T;
     const long off = (((long)b * p.T + (in ? t : 0)) * p.Hkv + g) * D + 8 * sub;
-    u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-    if (in) {
-      kw = ld16((const bf16*)p.k + off);
-      vw = ld16((const bf16*)p.v + off);
-      if (ve_on) {
-        // value-embedding gate: v + 2 sigmoid(x[:32] . w[g]) table[id][g]
-        const long row = (long)b * p.T + t;
-        const float gt = ve_gate_of(p.ve, row, g);
-        float vv[8], ee[8];
-        unpack8(vw, vv);
-        unpack8(ve_chunk(p.ve, rt, p.ve_table_bytes, row, p.Hkv, D, g, sub), ee);
+    const u32x4 kw = kws[i];
+    u32x4 vw = vws[i];
+    if (in && ve_on) {
+      // value-embedding gate: v + 2 sigmoid(x[:32] . w[g]) table[id][g]
+      const long row = (long)b * p.T + t;
+      const float gt = ve_gate_of(p.ve, row, g);
+      float vv[8], ee[8];
+      unpack8(vw, vv);
+      unpack8(ve_chunk(p.ve, rt, p.ve_table_bytes, row, p.Hkv, D, g, sub), ee);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vv[e] = __builtin_fmaf(gt, ee[e], vv[e]);
-        vw = pack8(vv);
-      }
+      for (int e = 0; e < 8; ++e) vv[e] = __builtin_fmaf(gt, ee[e], vv[e]);
+      vw = pack8(vv);
     }
     float x[8];
     unpack8(kw, x);
