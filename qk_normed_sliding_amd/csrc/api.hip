@@ -410,12 +410,13 @@ sa_status check_polar(int batch, int rows, int cols, int steps, float eps) {
 }
 
 // K splits of a GEMM with `jobs` workgroups (computed tiles x batch): the
-// fewest equal ranges (multiples of 64, at least 256 long) that give 512
-// workgroups, enough to fill the compute units twice over.
+// fewest equal ranges (multiples of 64, at least 512 long) that give 512
+// workgroups, enough to fill the compute units twice over. Shorter ranges
+// do not pay for the partial tiles' round trip through memory.
 int polar_splits(long jobs, int K) {
   int best = 1;
   for (int sp : {1, 2, 3, 4, 6, 8}) {
-    if (K % (64 * sp) != 0 || K / sp < 256) continue;
+    if (K % (64 * sp) != 0 || K / sp < 512) continue;
     best = sp;
     if (jobs * sp >= 512) break;
   }

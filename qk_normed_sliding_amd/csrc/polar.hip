@@ -230,62 +230,53 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   }
 }
 
-// Split-K reduction: the 64 x 64 quarter blockIdx.x % 4 of computed tile
-// blockIdx.x / 4 of matrix blockIdx.y. Thread (r, q) adds the partials of
-// row r, columns 16q .. 16q + 15 in split order, applies alpha and beta and
-// stores 32 bytes; the mirror goes through an LDS transpose.
+// Split-K reduction: the 32 x 32 block blockIdx.x % 16 of computed tile
+// blockIdx.x / 16 of matrix blockIdx.y. Thread (r, q) adds the partials of
+// row r, columns 4q .. 4q + 3 in split order, applies alpha and beta and
+// stores 8 bytes; the mirror goes through an LDS transpose.
 __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
-  __shared__ unsigned short t[64][72];
-  const int tile = blockIdx.x / 4, qr = (blockIdx.x / 2) & 1, qc = blockIdx.x & 1;
+  __shared__ unsigned short t[32][34];
+  const int tile = blockIdx.x / 16, br = (blockIdx.x / 4) & 3, bc = blockIdx.x & 3;
   int tm, tn;
   tile_of(tile, p.N / 128, p.sym, tm, tn);
   const long bz = blockIdx.y;
   const int ntile = gemm_tiles(p.M, p.N, p.sym);
-  const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
-  const int lr = 64 * qr + r, lc = 64 * qc + 16 * q;  // within the 128 x 128 tile
-  float v[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = 0.f;
+  const int r = threadIdx.x >> 3, q = threadIdx.x & 7;
+  const int lr = 32 * br + r, lc = 32 * bc + 4 * q;  // within the 128 x 128 tile
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < p.splits; ++s) {
-    const float* src = p.part + (((long)bz * p.splits + s) * ntile + tile) * (128 * 128) + lr * 128 + lc;
+    const f32x4 x = *(const f32x4*)(p.part + (((long)bz * p.splits + s) * ntile + tile) * (128 * 128) + lr * 128 + lc);
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const f32x4 x = *(const f32x4*)(src + 4 * e4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * e4 + e] += x[e];
-    }
+    for (int e = 0; e < 4; ++e) v[e] += x[e];
   }
   const long row = tm * 128 + lr, col = tn * 128 + lc;
   const long off = bz * p.M * p.N + row * p.N + col;
-  float c0[16];
+  float o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = p.alpha * v[e];
   if (p.c0 != nullptr) {
-    unpack8(ld16((const bf16*)p.c0 + off), c0);
-    unpack8(ld16((const bf16*)p.c0 + off + 8), c0 + 8);
+    const u32x2 c0 = *(const u32x2*)((const bf16*)p.c0 + off);
+    o[0] += p.beta * __uint_as_float(c0[0] << 16);
+    o[1] += p.beta * __uint_as_float(c0[0] & 0xffff0000u);
+    o[2] += p.beta * __uint_as_float(c0[1] << 16);
+    o[3] += p.beta * __uint_as_float(c0[1] & 0xffff0000u);
   }
-#pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = p.alpha * v[e] + (p.c0 != nullptr ? p.beta * c0[e] : 0.f);
-  const u32x4 w0 = pack8(v), w1 = pack8(v + 8);
-  st16((bf16*)p.c + off, w0);
-  st16((bf16*)p.c + off + 8, w1);
+  u32x2 w;
+  w[0] = pack2(o[0], o[1]);
+  w[1] = pack2(o[2], o[3]);
+  *(u32x2*)((bf16*)p.c + off) = w;
   if (!(p.sym && tm != tn)) return;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    t[r][16 * q + 2 * e] = (unsigned short)(w0[e] & 0xffffu);
-    t[r][16 * q + 2 * e + 1] = (unsigned short)(w0[e] >> 16);
-    t[r][16 * q + 8 + 2 * e] = (unsigned short)(w1[e] & 0xffffu);
-    t[r][16 * q + 8 + 2 * e + 1] = (unsigned short)(w1[e] >> 16);
-  }
+  t[r][4 * q] = (unsigned short)(w[0] & 0xffffu);
+  t[r][4 * q + 1] = (unsigned short)(w[0] >> 16);
+  t[r][4 * q + 2] = (unsigned short)(w[1] & 0xffffu);
+  t[r][4 * q + 3] = (unsigned short)(w[1] >> 16);
   __syncthreads();
-  // mirror: row col' = column (64qc + r) of the quarter, 16 consecutive rows 16q .. of the quarter
-  u32x4 m0v, m1v;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    m0v[e] = (uint32_t)t[16 * q + 2 * e][r] | ((uint32_t)t[16 * q + 2 * e + 1][r] << 16);
-    m1v[e] = (uint32_t)t[16 * q + 8 + 2 * e][r] | ((uint32_t)t[16 * q + 8 + 2 * e + 1][r] << 16);
-  }
-  const long moff = bz * p.M * p.N + (long)(tn * 128 + 64 * qc + r) * p.M + tm * 128 + 64 * qr + 16 * q;
-  st16((bf16*)p.c + moff, m0v);
-  st16((bf16*)p.c + moff + 8, m1v);
+  // mirror: row (block column r) of the transposed block, its columns 4q .. 4q + 3 = block rows
+  u32x2 m;
+  m[0] = (uint32_t)t[4 * q][r] | ((uint32_t)t[4 * q + 1][r] << 16);
+  m[1] = (uint32_t)t[4 * q + 2][r] | ((uint32_t)t[4 * q + 3][r] << 16);
+  const long moff = bz * p.M * p.N + (long)(tn * 128 + 32 * bc + r) * p.M + tm * 128 + 32 * br + 4 * q;
+  *(u32x2*)((bf16*)p.c + moff) = m;
 }
 
 // Sum of squares of chunk blockIdx.x of matrix blockIdx.y (elements
@@ -360,7 +351,7 @@ hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t st
     hipLaunchKernelGGL((gemm_kernel<false>), grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(ntile * 4), (unsigned)batch), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(ntile * 16), (unsigned)batch), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

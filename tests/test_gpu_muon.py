@@ -56,11 +56,12 @@ def _check(sa, g, steps=5, idx=None):
     return out
 
 
-# (1, 128, 640): one tile, K split in 2; (1, 256, 1024): the Gram's K split
-# in 4 with a mirrored off-diagonal tile; (2, 512, 1536): Gram split in 6,
-# A A split in 2, both with mirrored tiles
-@pytest.mark.parametrize("shape", [(3, 256, 384), (2, 384, 256), (2, 256, 256), (1, 128, 640), (1, 256, 1024),
-                                   (2, 512, 1536)])
+# K is split in ranges of at least 512: (1, 128, 1024): one tile, the Gram's
+# K split in 2; (1, 256, 1024): split in 2 with a mirrored off-diagonal
+# tile; (2, 512, 1536): Gram split in 3; (1, 1024, 1024): the Gram and A A
+# both split in 2, with mirrored tiles
+@pytest.mark.parametrize("shape", [(3, 256, 384), (2, 384, 256), (2, 256, 256), (1, 128, 1024), (1, 256, 1024),
+                                   (2, 512, 1536), (1, 1024, 1024)])
 def test_polar_express_small(sa, shape):
     log(f"[polar] {shape}")
     _check(sa, _grad(shape, 300 + shape[1]))
