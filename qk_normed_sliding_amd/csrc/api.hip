@@ -410,13 +410,15 @@ sa_status check_polar(int batch, int rows, int cols, int steps, float eps) {
 }
 
 // K splits of a GEMM with `jobs` workgroups (computed tiles x batch): the
-// fewest equal ranges (multiples of 64, at least 512 long) that give 512
+// fewest equal ranges (multiples of 64, at least 1024 long) that give 512
 // workgroups, enough to fill the compute units twice over. Shorter ranges
-// do not pay for the partial tiles' round trip through memory.
+// do not pay for the partial tiles' round trip through memory (measured on
+// the trainer's groups: K = 3072 in 3 ranges beat 2 and 4; K = 768 unsplit
+// beat 3 ranges).
 int polar_splits(long jobs, int K) {
   int best = 1;
   for (int sp : {1, 2, 3, 4, 6, 8}) {
-    if (K % (64 * sp) != 0 || K / sp < 512) continue;
+    if (K % (64 * sp) != 0 || K / sp < 1024) continue;
     best = sp;
     if (jobs * sp >= 512) break;
   }

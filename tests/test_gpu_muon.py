@@ -56,12 +56,12 @@ def _check(sa, g, steps=5, idx=None):
     return out
 
 
-# K is split in ranges of at least 512: (1, 128, 1024): one tile, the Gram's
-# K split in 2; (1, 256, 1024): split in 2 with a mirrored off-diagonal
-# tile; (2, 512, 1536): Gram split in 3; (1, 1024, 1024): the Gram and A A
-# both split in 2, with mirrored tiles
-@pytest.mark.parametrize("shape", [(3, 256, 384), (2, 384, 256), (2, 256, 256), (1, 128, 1024), (1, 256, 1024),
-                                   (2, 512, 1536), (1, 1024, 1024)])
+# K is split in ranges of at least 1024: (1, 128, 2048): one tile, the
+# Gram's K split in 2; (1, 256, 2048): split in 2 with a mirrored
+# off-diagonal tile; (2, 512, 3072): Gram split in 3; (1, 2048, 2048): the
+# Gram and A A both split in 2, with mirrored tiles
+@pytest.mark.parametrize("shape", [(3, 256, 384), (2, 384, 256), (2, 256, 256), (1, 128, 2048), (1, 256, 2048),
+                                   (2, 512, 3072), (1, 2048, 2048)])
 def test_polar_express_small(sa, shape):
     log(f"[polar] {shape}")
     _check(sa, _grad(shape, 300 + shape[1]))
