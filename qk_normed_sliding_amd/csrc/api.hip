@@ -478,24 +478,25 @@ SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, siz
     if (sa::launch_transpose(g, x0, batch, rows, cols, s) != hipSuccess) return SA_ERR_HIP;
     src = x0;
   }
-  if (sa::launch_fro_scale(src, x0, part, batch, (long)m * n, eps, s) != hipSuccess) return SA_ERR_HIP;
-  void* cur = x0;
-  void* nxt = x1;
+  // ||G||_F in partial sums; the first step reads G itself and scales its products
+  if (sa::launch_fro_sumsq(src, part, batch, (long)m * n, s) != hipSuccess) return SA_ERR_HIP;
+  // step k writes bufs[k % 2]; x0 (the transposed input of a tall matrix) is read by step 0 only
+  void* bufs[2] = {x1, x0};
+  const void* cur = src;
   for (int k = 0; k < steps; ++k) {
     const float a = kPolarCoeffs[k][0], b = kPolarCoeffs[k][1], c = kPolarCoeffs[k][2];
-    // A = X X^T (symmetric: upper tiles only)
-    sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f, 1, pl.s_xx, kpart};
+    const float* nsum = k == 0 ? part : nullptr;
+    // A = X X^T (symmetric: upper tiles only); X = G / (||G|| + eps) on the first step
+    sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f, 1, pl.s_xx, kpart, nsum, 2, eps};
     if (sa::launch_gemm(pg, false, batch, s) != hipSuccess) return SA_ERR_HIP;
     // B = c A A + b A  (A is symmetric: A A = A A^T, and so is B)
     sa::GemmParams pb{A, A, A, Bm, m, m, m, c, b, 1, pl.s_aa, kpart};
     if (sa::launch_gemm(pb, false, batch, s) != hipSuccess) return SA_ERR_HIP;
     // X <- B X + a X, straight into the output on the last step of a wide matrix
-    void* dst = (k == steps - 1 && !tall) ? out : nxt;
-    sa::GemmParams px{Bm, cur, cur, dst, m, n, m, 1.f, a};
+    void* dst = (k == steps - 1 && !tall) ? out : bufs[k % 2];
+    sa::GemmParams px{Bm, cur, cur, dst, m, n, m, 1.f, a, 0, 0, nullptr, nsum, 1, eps};
     if (sa::launch_gemm(px, true, batch, s) != hipSuccess) return SA_ERR_HIP;
-    void* t = cur;
-    cur = nxt;
-    nxt = t;
+    cur = bufs[k % 2];
   }
   if (tall && sa::launch_transpose(cur, out, batch, m, n, s) != hipSuccess) return SA_ERR_HIP;
   return SA_OK;

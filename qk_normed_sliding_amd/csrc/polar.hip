@@ -1,6 +1,7 @@
 // Muon's polar-express orthogonalisation ("autoresearch Administrator &
 // Developer Guide", section 8.2.3) for stacks of bf16 matrices: the gradient
-// scaled by its Frobenius norm, then five steps
+// scaled by its Frobenius norm (the scale is folded into the first step's
+// products: X X^T takes s^2 and B X + a X takes s), then five steps
 //   A = X X^T,  B = b A + c A A,  X <- a X + B X
 // on the wide side (a tall matrix is turned into a wide one by a transpose
 // on the way in and out: the iteration commutes with transposition).
@@ -49,6 +50,23 @@ __device__ __forceinline__ int xcd_item(int L, int n) {
   const int per = n / kXcds, rem = n % kXcds;
   const int start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
   return start + slot;
+}
+
+// alpha and beta of a product, times s^npow when the operand's scaling
+// s = 1 / (||G||_F + eps) is folded in (the partial sums added in the same
+// fixed order everywhere)
+__device__ __forceinline__ void gemm_scales(const GemmParams& p, long bz, float& al, float& be) {
+  al = p.alpha;
+  be = p.beta;
+  if (p.nsum != nullptr) {
+    const float* pm = p.nsum + bz * kFroChunks;
+    float ss = 0.f;
+    for (int c = 0; c < kFroChunks; ++c) ss += pm[c];
+    const float sc = 1.f / (sqrtf(ss) + p.neps);
+    const float f = p.npow == 2 ? sc * sc : sc;
+    al *= f;
+    be *= f;
+  }
 }
 
 template <bool BN>
@@ -196,6 +214,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   // store 32 consecutive elements of a row per instruction
   const long cbase = bz * p.M * p.N;
   const bool mirror = p.sym && tm != tn;
+  float al, be;
+  gemm_scales(p, bz, al, be);
 #pragma unroll
   for (int y = 0; y < 2; ++y) {
     const long row = m0 + 32 * (2 * wm + y) + l32;
@@ -206,13 +226,13 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
         const long off = cbase + row * p.N + n0 + 32 * (2 * wn + x) + 8 * i + 4 * half;
         float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = p.alpha * acc[x][y][4 * i + j];
+        for (int j = 0; j < 4; ++j) v[j] = al * acc[x][y][4 * i + j];
         if (p.c0 != nullptr) {
           const u32x2 c0 = *(const u32x2*)((const bf16*)p.c0 + off);
-          v[0] += p.beta * __uint_as_float(c0[0] << 16);
-          v[1] += p.beta * __uint_as_float(c0[0] & 0xffff0000u);
-          v[2] += p.beta * __uint_as_float(c0[1] << 16);
-          v[3] += p.beta * __uint_as_float(c0[1] & 0xffff0000u);
+          v[0] += be * __uint_as_float(c0[0] << 16);
+          v[1] += be * __uint_as_float(c0[0] & 0xffff0000u);
+          v[2] += be * __uint_as_float(c0[1] << 16);
+          v[3] += be * __uint_as_float(c0[1] & 0xffff0000u);
         }
         u32x2 o;
         o[0] = pack2(v[0], v[1]);
@@ -251,15 +271,17 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   }
   const long row = tm * 128 + lr, col = tn * 128 + lc;
   const long off = bz * p.M * p.N + row * p.N + col;
+  float al, be;
+  gemm_scales(p, bz, al, be);
   float o[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = p.alpha * v[e];
+  for (int e = 0; e < 4; ++e) o[e] = al * v[e];
   if (p.c0 != nullptr) {
     const u32x2 c0 = *(const u32x2*)((const bf16*)p.c0 + off);
-    o[0] += p.beta * __uint_as_float(c0[0] << 16);
-    o[1] += p.beta * __uint_as_float(c0[0] & 0xffff0000u);
-    o[2] += p.beta * __uint_as_float(c0[1] << 16);
-    o[3] += p.beta * __uint_as_float(c0[1] & 0xffff0000u);
+    o[0] += be * __uint_as_float(c0[0] << 16);
+    o[1] += be * __uint_as_float(c0[0] & 0xffff0000u);
+    o[2] += be * __uint_as_float(c0[1] << 16);
+    o[3] += be * __uint_as_float(c0[1] & 0xffff0000u);
   }
   u32x2 w;
   w[0] = pack2(o[0], o[1]);
@@ -300,23 +322,6 @@ __global__ void __launch_bounds__(256) sumsq_kernel(const bf16* x, float* part, 
   if (threadIdx.x == 0) part[(long)blockIdx.y * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// y = x / (sqrt(sum of the matrix's partial sums) + eps), chunk blockIdx.x of matrix blockIdx.y.
-__global__ void __launch_bounds__(256) scale_kernel(const bf16* x, bf16* y, const float* part, long per_matrix,
-                                                    long per, float eps) {
-  const float* pm = part + (long)blockIdx.y * gridDim.x;
-  float ss = 0.f;
-  for (int c = 0; c < (int)gridDim.x; ++c) ss += pm[c];  // same order in every workgroup
-  const float sc = 1.f / (sqrtf(ss) + eps);
-  const long off = (long)blockIdx.y * per_matrix + (long)blockIdx.x * per;
-  for (long e = 8L * threadIdx.x; e < per; e += 8L * 256) {
-    float f[8];
-    unpack8(ld16(x + off + e), f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) f[k] *= sc;
-    st16(y + off + e, pack8(f));
-  }
-}
-
 // out[b][c][r] = in[b][r][c] for 64 x 64 tiles (R, C multiples of 64): 16-byte
 // loads of input rows into an LDS tile, 16-byte stores of output rows read
 // down its columns.
@@ -355,15 +360,10 @@ hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_fro_scale(const void* x, void* y, float* part, int batch, long per_matrix, float eps,
-                            hipStream_t stream) {
+hipError_t launch_fro_sumsq(const void* x, float* part, int batch, long per_matrix, hipStream_t stream) {
   const long per = per_matrix / kFroChunks;
   const dim3 grid((unsigned)kFroChunks, (unsigned)batch);
   hipLaunchKernelGGL(sumsq_kernel, grid, dim3(256), 0, stream, (const bf16*)x, part, per_matrix, per);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scale_kernel, grid, dim3(256), 0, stream, (const bf16*)x, (bf16*)y, (const float*)part,
-                     per_matrix, per, eps);
   return hipGetLastError();
 }
 

@@ -135,6 +135,10 @@ struct GemmParams {
   int sym;         // C is symmetric (M == N): only tiles on or above the diagonal are computed, each stored mirrored too
   int splits;      // K in this many equal ranges (0 or 1: none); fp32 partial tiles in part, summed by a second kernel
   float* part;     // batch * splits * (computed tiles) * 128 * 128 floats
+  const float* nsum;  // optional: per matrix kFroChunks partial sums of squares of an operand G; alpha and
+                      // beta are then multiplied by s^npow, s = 1 / (||G||_F + neps) (the operand's scaling)
+  int npow;
+  float neps;
 };
 // Tiles of C that a GEMM computes (all, or those on and above the diagonal).
 __host__ __device__ inline int gemm_tiles(int M, int N, int sym) {
@@ -160,11 +164,11 @@ hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream
 // (any query-heads-per-KV-head ratio).
 hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
 hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream);
-// Polar-express pieces: GEMM (b_kn: B given as [K][N]), X / ||X||_F per matrix
-// (part: batch * kFroChunks floats), and per-matrix transpose [R][C] -> [C][R].
+// Polar-express pieces: GEMM (b_kn: B given as [K][N]), partial sums of
+// squares for ||X||_F per matrix (part: batch * kFroChunks floats), and
+// per-matrix transpose [R][C] -> [C][R].
 hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream);
-hipError_t launch_fro_scale(const void* x, void* y, float* part, int batch, long per_matrix, float eps,
-                            hipStream_t stream);
+hipError_t launch_fro_sumsq(const void* x, float* part, int batch, long per_matrix, hipStream_t stream);
 hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, hipStream_t stream);
 // Value-embedding gate: v' and g for the backward; then dve, dx32 and dw from dL/dv'.
 hipError_t launch_ve_prep(const VePrepParams& p, int head_dim, hipStream_t stream);
