@@ -65,55 +65,71 @@ __global__ void __launch_bounds__(256) ve_bwd_rows_kernel(VeBwdParams p) {
 }
 
 // Per block of kVeRows rows: dx32[row][c] = sum_h dz[row][h] w[h][c], and the
-// block's partial dw[h][c] = sum_row dz[row][h] x[row][c]. For dw, thread
-// (j, c) sums rows j, j + 8, ... of the block for every head; the 8 row
-// groups are then added in order (fixed order: deterministic).
+// block's partial dw[h][c] = sum_row dz[row][h] x[row][c]. The block's x rows
+// (16-byte loads), dz and w are staged in LDS first. For dw, thread (j, c)
+// sums rows j, j + 8, ... of the block for every head; the 8 row groups are
+// then added in order (fixed order: deterministic).
 __global__ void __launch_bounds__(256) ve_bwd_gate_kernel(VeBwdParams p) {
+  static_assert(kVeRows == 64, "one 16-byte chunk of x per thread");
+  __shared__ float xs[kVeRows][33];
+  __shared__ float zs[kVeRows][kVeMaxHeads + 1];
+  __shared__ float wsh[kVeMaxHeads][32];
   __shared__ float acc[8][kVeMaxHeads][32];
+  const int tid = threadIdx.x;
   const long r0 = (long)blockIdx.x * kVeRows;
   const int nr = (int)min((long)kVeRows, p.rows - r0);
-  const bf16* wg = (const bf16*)p.ve.w;
-  for (int e = threadIdx.x; e < nr * 32; e += 256) {
-    const long row = r0 + e / 32;
-    const int c = e % 32;
-    float s = 0.f;
-    for (int h = 0; h < p.Hkv; ++h) s = __builtin_fmaf(p.dz[row * p.Hkv + h], (float)wg[h * 32 + c], s);
-    p.dx32[row * 32 + c] = s;
+  const int H = p.Hkv;
+  {
+    const int r = tid >> 2, ch = tid & 3;
+    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (r < nr) unpack8(ld16((const bf16*)p.ve.x + (r0 + r) * p.ve.x_stride + 8 * ch), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xs[r][8 * ch + e] = f[e];
   }
-  const int c = threadIdx.x % 32, j = threadIdx.x / 32;
-  const bf16* xb = (const bf16*)p.ve.x;
-  for (int h = 0; h < p.Hkv; ++h) {
+  for (int e = tid; e < nr * H; e += 256) zs[e / H][e % H] = p.dz[r0 * H + e];
+  for (int e = tid; e < H * 32; e += 256) wsh[e / 32][e % 32] = (float)((const bf16*)p.ve.w)[e];
+  __syncthreads();
+  for (int e = tid; e < nr * 32; e += 256) {
+    const int r = e / 32, c = e % 32;
+    float s = 0.f;
+    for (int h = 0; h < H; ++h) s = __builtin_fmaf(zs[r][h], wsh[h][c], s);
+    p.dx32[(r0 + r) * 32 + c] = s;
+  }
+  const int c = tid % 32, j = tid / 32;
+  for (int h = 0; h < H; ++h) {
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < kVeRows / 8; ++r) {
       const int rr = j + 8 * r;
-      if (rr < nr) s = __builtin_fmaf(p.dz[(r0 + rr) * p.Hkv + h], (float)xb[(r0 + rr) * p.ve.x_stride + c], s);
+      if (rr < nr) s = __builtin_fmaf(zs[rr][h], xs[rr][c], s);
     }
     acc[j][h][c] = s;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < p.Hkv * 32; e += 256) {
+  for (int e = tid; e < H * 32; e += 256) {
     const int h = e / 32, cc = e % 32;
     float s = 0.f;
 #pragma unroll
     for (int g = 0; g < 8; ++g) s += acc[g][h][cc];
-    p.part[(long)blockIdx.x * p.Hkv * 32 + e] = s;
+    p.part[(long)blockIdx.x * H * 32 + e] = s;
   }
 }
 
-// dw[h][c] = sum of the blocks' partials: workgroup h, thread (j, c) sums
-// blocks j, j + 8, ... and the 8 sums are added in order.
+// dw[h][c] = sum of the blocks' partials: workgroup (h, column group cg of 8
+// columns), thread (j, c) sums blocks j, j + 32, ... (loads in groups of 8),
+// and the 32 sums are added in order (fixed order: deterministic).
 __global__ void __launch_bounds__(256) ve_bwd_reduce_kernel(VeBwdParams p, int nblk) {
-  __shared__ float acc[8][32];
-  const int h = blockIdx.x;
-  const int c = threadIdx.x % 32, j = threadIdx.x / 32;
+  __shared__ float acc[32][8];
+  const int h = blockIdx.x / 4, cg = blockIdx.x % 4;
+  const int c = threadIdx.x % 8, j = threadIdx.x / 8;
+  const int col = 8 * cg + c;
   float s = 0.f;
-  for (int k0 = j; k0 < nblk; k0 += 64) {
+  for (int k0 = j; k0 < nblk; k0 += 256) {
     float t[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int k = k0 + 8 * u;
-      t[u] = k < nblk ? p.part[((long)k * p.Hkv + h) * 32 + c] : 0.f;
+      const int k = k0 + 32 * u;
+      t[u] = k < nblk ? p.part[((long)k * p.Hkv + h) * 32 + col] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) s += t[u];
@@ -123,8 +139,8 @@ __global__ void __launch_bounds__(256) ve_bwd_reduce_kernel(VeBwdParams p, int n
   if (j == 0) {
     float r = 0.f;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) r += acc[g][c];
-    p.dw[h * 32 + c] = r;
+    for (int g = 0; g < 32; ++g) r += acc[g][c];
+    p.dw[h * 32 + col] = r;
   }
 }
 
@@ -153,7 +169,7 @@ hipError_t launch_ve_bwd(const VeBwdParams& p, int head_dim, hipStream_t stream)
   hipLaunchKernelGGL(ve_bwd_gate_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ve_bwd_reduce_kernel, dim3((unsigned)p.Hkv), dim3(256), 0, stream, p, nblk);
+  hipLaunchKernelGGL(ve_bwd_reduce_kernel, dim3((unsigned)(p.Hkv * 4)), dim3(256), 0, stream, p, nblk);
   return hipGetLastError();
 }
 
