@@ -275,3 +275,24 @@ def test_value_embedding_validation_paths(sa):
     assert bwd(vws=0) == SA_ERR_WORKSPACE
     assert bwd(vws_bytes=64) == SA_ERR_WORKSPACE
     assert bwd(vws=32768 + 128) == SA_ERR_WORKSPACE
+
+
+def test_rope_tables_helper_matches_the_oracle(sa):
+    """The binding's rotary-table helper (the angle ladder t * base^(-2i/D)
+    the GPU tests hand to both sides) is pinned to the oracle's tables, so a
+    wrong frequency ladder cannot pass the GPU parity tests unnoticed."""
+    import torch
+
+    import oracle
+
+    for n_pos, D in ((20480, 128), (4096, 64), (7, 16)):
+        cos, sin = sa.rope_tables(n_pos, D)
+        rc, rs = oracle.rope_tables(n_pos, D)
+        assert cos.dtype == torch.float32 and tuple(cos.shape) == (n_pos, D // 2)
+        # fp32 storage of values in [-1, 1]: within half an ulp of 1.0
+        assert float((cos.double() - rc).abs().max()) <= 6e-8
+        assert float((sin.double() - rs).abs().max()) <= 6e-8
+    # a different ladder (base 1000) is far from the oracle's tables
+    cos, _ = sa.rope_tables(2048, 128, base=1000.0)
+    rc, _ = oracle.rope_tables(2048, 128)
+    assert float((cos.double() - rc).abs().max()) > 0.5
