@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float l_run = 0.f;
+  float l_run[2] = {0.f, 0.f};  // row sums in two independent accumulation chains
   f32x16 s[2];          // logits of the tile between its M- and V-phase
   bf16x8 pf[2][2];      // probabilities of the previous tile (P.V operand)
 
@@ -344,10 +344,11 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   // bf16-rounded probabilities that P.V multiplies (unpacked from the
   // operand registers), so the weights O is normalised with sum to one
   // exactly, and a row that sees few keys is not left with the rounding of
-  // its probabilities.
+  // its probabilities. Each packed pair enters the sum through one
+  // bf16 dot product with (1, 1), straight from the operand register.
   auto v_phase = [&](int t, int r0) {
     const int row = r0 + l32;
-    float lsum[2];
+    const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float pv[16];
@@ -365,17 +366,14 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(s[c][r]);
       }
       uint32_t wd[8];
-      float t8[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         wd[i] = pack2(pv[2 * i], pv[2 * i + 1]);
-        t8[i] = __uint_as_float(wd[i] << 16) + __uint_as_float(wd[i] & 0xffff0000u);
+        l_run[i & 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[i]), ones, l_run[i & 1], false);
       }
-      lsum[c] = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
       pf[c][0] = __builtin_bit_cast(bf16x8, u32x4{wd[0], wd[1], wd[2], wd[3]});
       pf[c][1] = __builtin_bit_cast(bf16x8, u32x4{wd[4], wd[5], wd[6], wd[7]});
     }
-    l_run += lsum[0] + lsum[1];
   };
 
   // Epilogue of a finished item: O / l -> bf16, LSE (natural log); then the
@@ -387,7 +385,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   };
   Epi epi{0, 0, false};
   auto epilogue = [&]() {
-    const float l_tot = pair_sum(l_run);
+    const float l_tot = pair_sum(l_run[0] + l_run[1]);
     if (epi.ok) {
       const float inv = 1.f / l_tot;
       bf16* dst = (bf16*)p.o + epi.o_off;
@@ -406,7 +404,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    l_run = 0.f;
+    l_run[0] = l_run[1] = 0.f;
   };
 
   // ---- prologue: the first tiles of the stream (K tiles 0..NB-1 by group
