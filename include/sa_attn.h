@@ -137,6 +137,27 @@ sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       float softmax_scale, int qk_norm, float eps, void* stream);
 
 /*
+ * sa_attn_bwd_noalloc - sa_attn_bwd for callers that cannot allocate device
+ *   memory (code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid hipMalloc). Same arguments, semantics and outputs as sa_attn_bwd,
+ *   without the workspace: the library uses its own statically allocated
+ *   scratch instead (one copy per GPU, sa_attn_bwd_noalloc_max_bytes() =
+ *   80 MiB, held until the process ends) and calls no allocating routine.
+ *   Sizes whose workspace (sa_attn_bwd_workspace_bytes) exceeds that maximum
+ *   return SA_ERR_WORKSPACE without enqueuing anything; the workloads with
+ *   B*T = 32768 tokens, Hq = 6, Hkv = 3, D = 128 need 73 MiB. Every call on a
+ *   GPU shares that GPU's scratch: calls that overlap in time on one GPU (two
+ *   streams, two host threads) race and must be serialised by the caller.
+ *   Nothing in the scratch needs to start at zero. SA_ERR_HIP if the
+ *   scratch's device address cannot be obtained.
+ */
+size_t sa_attn_bwd_noalloc_max_bytes(void);
+sa_status sa_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv,
+                              int B, int T, int Hq, int Hkv, int head_dim, int window,
+                              float softmax_scale, int qk_norm, float eps, void* stream);
+
+/*
  * sa_attn_fwd_rope / sa_attn_bwd_rope - sa_attn_fwd / sa_attn_bwd with the
  * rotary position embedding of q and k fused into the kernels.
  *   [guide] 8.2.1 lists rotary embeddings built from precomputed tables and

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   sa_attn_fwd(q, k, v, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, o=None, lse=None, workspace=None)
   sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim)
   sa_attn_bwd(q, k, v, o, lse, dout, window=-1, ..., dq=None, dk=None, dv=None, workspace=None)
+  sa_attn_bwd_noalloc(q, k, v, o, lse, dout, ...)   (no workspace: the library's own scratch)
   sa_attn_fwd_rope(q, k, v, rope_cos, rope_sin, ...), sa_attn_bwd_rope(..., rope_cos, rope_sin, ...)
   sa_attn_fwd_ex / sa_attn_bwd_ex (rotary tables and value-embedding gate; also rope=..., ve=... on the plain calls)
   sa_attn_ve_workspace_bytes(B, T, Hkv, head_dim)
@@ -30,7 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa_attn.so")
 
 SA_OK = 0
-ABI_VERSION = 4
+ABI_VERSION = 5
 SA_KERNEL_FWD = 0
 SA_KERNEL_BWD_DQ = 1
 SA_KERNEL_BWD_DKDV = 2
@@ -66,6 +67,11 @@ def _load():
     lib.sa_attn_bwd.restype = i32
     lib.sa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                 i32, i32, i32, i32, i32, i32, f32, i32, f32, vp]
+    lib.sa_attn_bwd_noalloc_max_bytes.restype = sz
+    lib.sa_attn_bwd_noalloc_max_bytes.argtypes = []
+    lib.sa_attn_bwd_noalloc.restype = i32
+    lib.sa_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        i32, i32, i32, i32, i32, i32, f32, i32, f32, vp]
     lib.sa_attn_fwd_rope.restype = i32
     lib.sa_attn_fwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, sz, i32, i32, i32, i32, i32, i32, f32, i32, f32,
                                      vp, vp, i32, vp]
@@ -342,6 +348,33 @@ def sa_attn_bwd(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=Tr
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(workspace), workspace.numel(), B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D),
         int(bool(qk_norm)), float(eps), _stream(q.device, stream)))
+    return dq, dk, dv
+
+
+def sa_attn_bwd_noalloc_max_bytes():
+    return int(_lib.sa_attn_bwd_noalloc_max_bytes())
+
+
+def sa_attn_bwd_noalloc(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6,
+                        dq=None, dk=None, dv=None, stream=None):
+    """sa_attn_bwd without a workspace argument: the library's own per-GPU scratch
+    is used (for callers that cannot allocate; calls overlapping on one GPU race).
+    Outputs are allocated here only when not given."""
+    B, T, Hq, Hkv, D = _dims(q, k)
+    for t, n, shp in ((q, "q", None), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D)),
+                      (o, "o", q.shape), (dout, "dout", q.shape)):
+        _need(t, n, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (B, Hq, T))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, q.shape)
+    _need(dk, "dk", torch.bfloat16, k.shape)
+    _need(dv, "dv", torch.bfloat16, v.shape)
+    _check("sa_attn_bwd_noalloc", _lib.sa_attn_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D), int(bool(qk_norm)), float(eps),
+        _stream(q.device, stream)))
     return dq, dk, dv
 
 

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "sa_attn.h"
 #include "sa_kernels.h"
@@ -15,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 // Benchmarking hook: events recorded around the main kernel of later calls
 // made from this host thread (see sa_set_timing_events).
@@ -116,6 +117,35 @@ sa_status check_ve(const void* x, int64_t x_stride, const void* w, const int32_t
 }
 
 size_t ve_blocks(int B, int T) { return ((size_t)B * T + sa::kVeRows - 1) / sa::kVeRows; }
+
+}  // namespace
+
+// Scratch of the backward's no-allocation entry point: one copy per GPU the
+// library runs on, held until the process ends. Host code never uses this
+// name as an address (on the host it is only a stand-in for the symbol);
+// the per-device address comes from hipGetSymbolAddress below.
+constexpr size_t kScratchBytes = (size_t)80 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current. nullptr on a runtime error.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -356,6 +386,27 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
                              float softmax_scale, int qk_norm, float eps, void* stream) {
   return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window,
+                  softmax_scale, qk_norm, eps, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, 0, nullptr,
+                  nullptr, nullptr, nullptr, 0, stream);
+}
+
+SA_API size_t sa_attn_bwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+SA_API sa_status sa_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                     const void* dout, void* dq, void* dk, void* dv, int B, int T, int Hq, int Hkv,
+                                     int head_dim, int window, float softmax_scale, int qk_norm, float eps,
+                                     void* stream) {
+  // everything that can be checked without the runtime first
+  const sa_status st = check_shape(B, T, Hq, Hkv, head_dim, window, softmax_scale, eps);
+  if (st != SA_OK) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return SA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return SA_ERR_ALIGN;
+  if (sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim) > kScratchBytes) return SA_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return SA_ERR_HIP;
+  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, kScratchBytes, B, T, Hq, Hkv, head_dim, window,
                   softmax_scale, qk_norm, eps, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, 0, nullptr,
                   nullptr, nullptr, nullptr, 0, stream);
 }

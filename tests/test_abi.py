@@ -296,3 +296,29 @@ def test_rope_tables_helper_matches_the_oracle(sa):
     cos, _ = sa.rope_tables(2048, 128, base=1000.0)
     rc, _ = oracle.rope_tables(2048, 128)
     assert float((cos.double() - rc).abs().max()) > 0.5
+
+
+def _bwd_noalloc(lib, B=1, T=8, Hq=4, Hkv=2, D=64, W=-1, dq=16, null_lse=False, eps=1e-6):
+    P = ctypes.c_void_p
+    lse = 0 if null_lse else 16
+    return lib.sa_attn_bwd_noalloc(P(16), P(16), P(16), P(16), P(lse), P(16), P(dq), P(16), P(16),
+                                   B, T, Hq, Hkv, D, W, 0.125, 1, eps, None)
+
+
+def test_backward_noalloc_validation_paths(sa):
+    """The no-allocation backward checks everything, including that the sizes
+    fit its fixed scratch, before touching the HIP runtime."""
+    lib = sa.library()
+    assert lib.sa_attn_bwd_noalloc_max_bytes() == 80 << 20
+    assert _bwd_noalloc(lib, null_lse=True) == SA_ERR_NULL
+    assert _bwd_noalloc(lib, dq=0) == SA_ERR_NULL
+    assert _bwd_noalloc(lib, Hq=5, Hkv=2) == SA_ERR_SHAPE
+    assert _bwd_noalloc(lib, W=-2) == SA_ERR_SHAPE
+    assert _bwd_noalloc(lib, eps=-1.0) == SA_ERR_SHAPE
+    assert _bwd_noalloc(lib, D=32) == SA_ERR_UNSUPPORTED
+    assert _bwd_noalloc(lib, dq=8) == SA_ERR_ALIGN
+    # the 8-layer workload's shape fits; the pages' device batch of 128 (multi-head) does not
+    assert lib.sa_attn_bwd_workspace_bytes(16, 2048, 6, 3, 128) <= lib.sa_attn_bwd_noalloc_max_bytes()
+    assert lib.sa_attn_bwd_workspace_bytes(4, 8192, 6, 3, 128) <= lib.sa_attn_bwd_noalloc_max_bytes()
+    assert _bwd_noalloc(lib, B=128, T=2048, Hq=6, Hkv=6, D=128) == SA_ERR_WORKSPACE
+    assert _bwd_noalloc(lib, B=19, T=2048, Hq=6, Hkv=3, D=128) == SA_ERR_WORKSPACE
