@@ -116,16 +116,17 @@ size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
  *     dv_j = sum_{h in group} sum_i P_ij dout_i,
  *   then the RMS-norm backward dx = r (dx_hat - x_hat <dx_hat, x_hat> / D).
  *   Two kernels, no atomics: a dQ kernel per query block (it also writes the
- *   normed q rows and Delta into the workspace) and a dK/dV kernel per key
- *   block; the GQA sums over the query heads of a group happen inside the
- *   dK/dV kernel. With qk_norm a norm pass first writes the normed k rows
+ *   normed q rows and Delta into the workspace) and a persistent dK/dV kernel
+ *   over the key blocks; the GQA sums over the query heads of a group happen
+ *   inside the dK/dV kernel. With qk_norm a norm pass first writes the normed k rows
  *   into the workspace for both kernels.
  *   q, k, v, o, lse, dout : inputs (o and lse as written by sa_attn_fwd).
  *   dq, dk, dv            : bf16 outputs, fully overwritten.
  *   workspace             : device buffer of at least
  *                           sa_attn_bwd_workspace_bytes(B,T,Hq,Hkv,head_dim)
  *                           bytes (the bf16 normed q rows, the fp32 Delta
- *                           rows and the bf16 normed k rows), 256-byte aligned;
+ *                           rows, the bf16 normed k rows and their fp32
+ *                           1/rms), 256-byte aligned;
  *                           contents on entry are ignored and on return
  *                           unspecified. Two calls that overlap in time must
  *                           use different workspaces.

@@ -257,9 +257,9 @@ static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, 
 SA_API size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
   if (check_shape(B, T, Hq, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
   const size_t rows = (size_t)B * T * Hq;
-  // bf16 normed q rows, fp32 Delta, bf16 normed k rows
+  // bf16 normed q rows, fp32 Delta, bf16 normed k rows, fp32 1/rms of the k rows
   return round256(rows * head_dim * 2) + round256(rows * sizeof(float)) +
-         round256((size_t)B * T * Hkv * head_dim * 2);
+         round256((size_t)B * T * Hkv * head_dim * 2) + round256((size_t)B * T * Hkv * sizeof(float));
 }
 
 static sa_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -321,14 +321,18 @@ static sa_status attn_bwd(const void* q, const void* k, const void* v, const voi
   p.nsub = p.pair_rows ? p.G : p.G / 2;
   p.nqb = p.pair_rows ? (T + 255) / 256 : (T + 127) / 128;
   p.nkb = (T + 127) / 128;
+  p.nwg = persistent_wgs();
+  if (p.nwg <= 0) return SA_ERR_HIP;
   const hipStream_t s = (hipStream_t)stream;
   p.khat = k;
   if (qk_norm) {
     // normed k rows, copied straight into LDS as tiles by the dQ kernel
     void* khat = (char*)workspace + round256(rows * head_dim * 2) + round256(rows * sizeof(float));
-    sa::NormParams np{k, khat, nullptr, (int64_t)B * T * Hkv, eps, rope, Hkv, T};
+    float* rstd_k = (float*)((char*)khat + round256((size_t)B * T * Hkv * head_dim * 2));
+    sa::NormParams np{k, khat, rstd_k, (int64_t)B * T * Hkv, eps, rope, Hkv, T};
     if (sa::launch_qknorm(np, head_dim, s) != hipSuccess) return SA_ERR_HIP;
     p.khat = khat;
+    p.rstd_k = rstd_k;
   }
   p.rope = rope;
   // value embeddings: the attention kernels run on v' = v + g ve, written once

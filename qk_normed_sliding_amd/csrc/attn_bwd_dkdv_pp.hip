@@ -16,6 +16,16 @@
 // dO tiles of 64 rows (plus their LSE and Delta) stream into three LDS slots
 // as direct buffer-to-LDS copies; rows are XOR-swizzled so that the 16-byte
 // row reads (S, dP) and the transpose reads (dV, dK) are bank-conflict free.
+//
+// The kernel is persistent: one workgroup per compute unit takes key blocks
+// in a fixed heavy-first snake order (key blocks near the start of the
+// sequence see the most query rows). At a block's end each wave issues the
+// loads of its rows for the next block (k_hat or v) and that block's first
+// tile before running the finished block's epilogue, so the epilogue, the
+// next block's first loads and the workgroup's start overlap. The epilogue's
+// RMS-norm backward takes k_hat from group A's operand registers (through
+// LDS) and the row's 1/rms from the norm pass, so it reads no k row from
+// memory.
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -42,7 +52,7 @@ __device__ __forceinline__ void sched_mphase() {
   __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
 }
 
-template <int D>
+template <int D, bool ROPE>
 __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   constexpr int NB = 3;
   constexpr int BQ = 64;               // query rows per tile (two 32-row chunks)
@@ -75,20 +85,33 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   const int qstride = p.Hq * D;
   const int kvstride = p.Hkv * D;
 
-  // key blocks in ascending order: the first blocks see the most queries
-  const int bid = blockIdx.x;
-  const int kb = bid / (p.B * p.Hkv);
-  const int g = (bid / p.B) % p.Hkv;
-  const int b = bid % p.B;
-  const int kb0 = kb * BK;
-  const int kw0 = kb0 + 32 * rw;       // first key of this wave
-  const int key = kw0 + l32;
+  // ---- the workgroup's key blocks: ascending key blocks (the first see the
+  // most queries), in a snake order over the workgroups (round k: item
+  // k*G + w, or k*G + G-1-w on odd rounds)
+  const int n_items = p.nkb * p.B * p.Hkv;
+  const int NG = gridDim.x;
+  auto item_index = [&](int k) { return k * NG + ((k & 1) ? NG - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+  int n_blk = 0;
+  while (item_index(n_blk) < n_items) ++n_blk;
+  if (n_blk == 0) return;  // whole workgroup: no barrier has been passed
 
-  // query blocks whose rows can see at least one key of this block
-  const int q_hi = (W < 0) ? T - 1 : min(T - 1, kb0 + BK - 1 + W);
-  const int qb_lo = kb0 / BQ;
-  const int nqb = q_hi / BQ - qb_lo + 1;
-  const int nit = p.G * nqb;           // tiles: (query head of the group, query block)
+  // coordinates of the current block (set per block; the lambdas below read them)
+  int kb = 0, g = 0, b = 0, kb0 = 0, kw0 = 0, key = 0, q_hi = 0, qb_lo = 0, nqb = 0, nit = 0;
+  auto set_block = [&](int k) {
+    const int i = item_index(k);
+    kb = i / (p.B * p.Hkv);
+    g = (i / p.B) % p.Hkv;
+    b = i % p.B;
+    kb0 = kb * BK;
+    kw0 = kb0 + 32 * rw;  // first key of this wave
+    key = kw0 + l32;
+    // query blocks whose rows can see at least one key of this block
+    q_hi = (W < 0) ? T - 1 : min(T - 1, kb0 + BK - 1 + W);
+    qb_lo = kb0 / BQ;
+    nqb = q_hi / BQ - qb_lo + 1;
+    nit = p.G * nqb;  // tiles: (query head of the group, query block)
+  };
+  set_block(0);
 
   // ---- tile loads: instruction j of wave rw fills block m = 4j + rw, rows m*RPI + lane/CPR
   uint32_t ldo;
@@ -98,7 +121,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   }
   const uint32_t qs_lds = lds_addr(&Qs[0][0]);
   const uint32_t os_lds = lds_addr(&Os[0][0]);
-  auto issue = [&](int it) {  // group A: q_hat rows and LSE; group B: dO rows and Delta
+  auto issue = [&](int it) __attribute__((always_inline)) {  // group A: q_hat rows and LSE; group B: dO rows and Delta
     const int hh = it / nqb;
     const int row0 = (qb_lo + it % nqb) * BQ;
     const int head = g * p.G + hh;
@@ -123,14 +146,15 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   // 8half. k_hat comes from the backward's norm pass (turned when rotary
   // tables are given), the same rows the dQ kernel's S uses.
   bf16x8 kf[KST];  // group A: k_hat;  group B: v
-  {
+  auto load_kf = [&](bf16x8 (&dst)[KST]) __attribute__((always_inline)) {
     const long first = ((long)b * T * p.Hkv + g) * D + (long)kb0 * kvstride;
     const uint32_t bytes = (uint32_t)max(0, T - kb0) * kvstride * 2;
     const auto rk = make_rsrc((const bf16*)(grp == 0 ? p.khat : p.v) + first, bytes);
     const uint32_t off = (uint32_t)((32 * rw + l32) * kvstride + 8 * half) * 2;
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, bload16(rk, off + 32 * kk));
-  }
+    for (int kk = 0; kk < KST; ++kk) dst[kk] = __builtin_bit_cast(bf16x8, bload16(rk, off + 32 * kk));
+  };
+  load_kf(kf);
 
   // ---- LDS read addresses (bytes): row reads of rows 32qc + swap23(l32),
   // head_dim 16kk + 8half: (slot + base) ^ (kk << 5); transpose reads of rows
@@ -146,14 +170,14 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   auto lds_tr = [](uint32_t addr) { return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4*)(uintptr_t)addr); };
   // both chunks' rows, interleaved (chunk 0 k-step 0, chunk 1 k-step 0, ...),
   // the order in which the two S (or dP) chains consume them
-  auto rows_load2 = [&](uint32_t slot, bf16x8 (&a0)[KST], bf16x8 (&a1)[KST]) {
+  auto rows_load2 = [&](uint32_t slot, bf16x8 (&a0)[KST], bf16x8 (&a1)[KST]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
       a0[kk] = lds_ld16(((slot + ra_base) ^ (uint32_t)(kk << 5)));
       a1[kk] = lds_ld16(((slot + ra_base) ^ (uint32_t)(kk << 5)) + 32 * D * 2);
     }
   };
-  auto tr_load = [&](uint32_t slot, int qc, bf16x8 (&a)[KST]) {
+  auto tr_load = [&](uint32_t slot, int qc, bf16x8 (&a)[KST]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -188,7 +212,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   // transpose-operand MFMAs of tile t-1 (A: dV from dO^T and P, B: dK from
   // q_hat^T and dS). The first step has no tile t-1, the last no tile t.
   enum { K_FIRST = 0, K_MID = 1, K_LAST = 2 };
-  auto m_phase = [&](int t, auto kind) {
+  auto m_phase = [&](int t, auto kind) __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
     constexpr bool CUR = K != K_LAST, PREV = K != K_FIRST;
     const uint32_t rows_slot = (grp == 0 ? qs_lds : os_lds) + (uint32_t)((t % NB) * TILE * 2);
@@ -229,7 +253,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   // on chunks that cross the band edge; kept as the next dV operand and
   // written to LDS. B: dS of tile t = P (dP - Delta), P from LDS (written by A
   // one interval earlier).
-  auto v_phase = [&](int t) {
+  auto v_phase = [&](int t) __attribute__((always_inline)) {
     if (grp == 0) {
 #pragma unroll
       for (int qc = 0; qc < 2; ++qc) {
@@ -282,11 +306,15 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   // it. Group A runs M(t) in interval 2t and V(t) in 2t+1, group B one
   // interval later; every wave passes 2*nit + 3 barriers (group B one at the
   // start, group A one after its last, empty, V-phase).
-  issue(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (grp == 1) __syncthreads();
-  auto run = [&]() {
+  // ---- the epilogue's k_hat exchange: group A wave rw leaves its k_hat
+  // operands (lane l: key 32rw + l%32, head_dim 16kk + 8(l/32) .. +7) in LDS at
+  // ((kk * 64 + l) * 16) bytes of a KST KB region shared with group B's wave rw
+  // (the same keys), inside tile slots 1 and 2 of Qs, which the next block's
+  // first load (slot 0) does not touch
+  static_assert(4 * KST * 1024 <= 2 * TILE * 2, "the exchange fits in two tile slots");
+  const uint32_t xk_lds = qs_lds + (uint32_t)(TILE * 2) + (uint32_t)(rw * KST * 1024);
+
+  auto run = [&]() __attribute__((always_inline)) {
     if (1 < nit) issue(1);
     m_phase(0, std::integral_constant<int, K_FIRST>{});
     __syncthreads();
@@ -305,124 +333,146 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
     m_phase(nit, std::integral_constant<int, K_LAST>{});
     __syncthreads();
   };
-  run();
-  if (grp == 0) __syncthreads();  // group A's last (empty) V-phase interval
-  __builtin_amdgcn_s_waitcnt(0);
-
-  // ---- epilogue (the accumulators hold head_dim 32db + 8i + 4half + j of key `key`)
-  if (key >= T) return;
-  const long rowoff = ((long)b * T + key) * kvstride + (long)g * D + 4 * half;
-  if (grp == 0) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 w;
-        w[0] = pack2(acc[db][4 * i], acc[db][4 * i + 1]);
-        w[1] = pack2(acc[db][4 * i + 2], acc[db][4 * i + 3]);
-        *(u32x2*)((bf16*)p.dv + rowoff + 32 * db + 8 * i) = w;
-      }
-    return;
-  }
-  // dk = r (dk_hat - k_hat <dk_hat, k_hat> / D), dk_hat = scale * acc; the
-  // lane pair (l, l^32) holds the whole k row, so r comes from its squares.
-  // With rotary tables k_hat is the turned row (as the S MFMAs used it) and
-  // the result is turned back; head_dim d < D/2 (block db < NDB/2) pairs with
-  // d + D/2 (block db + NDB/2).
+  // 1/rms of this lane's key row (from the norm pass), one block ahead of its use
   const bool norm = p.qhat != p.q;
-  const bool rope = p.rope.cos != nullptr;
-  const long tr = (long)key * p.rope.stride + 4 * half;
-  // table entries first: their loads are in flight with the k rows'
-  f32x4 tc[NDB / 2][4], ts[NDB / 2][4];
-  if (rope) {
+  auto load_rk = [&]() { return (grp == 1 && norm && key < T) ? p.rstd_k[((long)b * T + key) * p.Hkv + g] : 1.f; };
+  float r_k = load_rk();
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#pragma clang loop unroll(disable)
+  for (int bk = 0; bk < n_blk; ++bk) {
+    if (grp == 1) __syncthreads();
+    run();
+    if (grp == 0) __syncthreads();  // group A's last (empty) V-phase interval
+    __builtin_amdgcn_s_waitcnt(0);
+    // group A's k_hat rows for the epilogue's exchange, before the next block's rows replace them
+    if (grp == 0 && norm) {
 #pragma unroll
-    for (int db = 0; db < NDB / 2; ++db)
+      for (int kk = 0; kk < KST; ++kk)
+        *(SA_LDS u32x4*)(uintptr_t)(xk_lds + (uint32_t)((kk * 64 + lane) * 16)) = __builtin_bit_cast(u32x4, kf[kk]);
+    }
+    // the finished block, for its epilogue; the next block's rows, 1/rms and first tile are loaded
+    // meanwhile, and the epilogue's stores are issued after they have arrived, so that the wait
+    // for them does not include the stores
+    const int e_b = b, e_g = g, e_key = key;
+    const float e_rk = r_k;
+    const bool more = bk + 1 < n_blk;
+    if (more) {
+      set_block(bk + 1);
+      load_kf(kf);
+      r_k = load_rk();
+      issue(0);
+    }
+    __syncthreads();
+
+    // ---- epilogue (the accumulators hold head_dim 32db + 8i + 4half + j of key `key`)
+    const long rowoff = ((long)e_b * T + e_key) * kvstride + (long)e_g * D + 4 * half;
+    if (grp == 1 && e_key < T) {
+      // dk = r (dk_hat - k_hat <dk_hat, k_hat> / D), dk_hat = scale * acc, with
+      // k_hat as the S MFMAs used it (bf16; with rotary tables the turned row,
+      // and the result is turned back; head_dim d < D/2 in block db < NDB/2
+      // pairs with d + D/2 in block db + NDB/2). Head_dim 32db + 8i + 4half + j
+      // of the key sits in group A's operand kk = 2db + i/2 of lane
+      // 32(i%2) + l%32, elements 4half + j.
+      constexpr bool rope = ROPE;
+      const long tr = (long)e_key * p.rope.stride + 4 * half;
+      f32x4 tc[NDB / 2][4], ts[NDB / 2][4];
+      if (rope) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        tc[db][i] = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
-        ts[db][i] = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+        for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            tc[db][i] = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
+            ts[db][i] = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+          }
       }
-  }
-  float kx[NDB][16];
-  float dot = 0.f, ss = 0.f, r_k = 1.f;
-  if (norm) {
-    const bf16* kp = (const bf16*)p.k + rowoff;
+      float dot = 0.f;
+      u32x2 kh[NDB][4] = {};
+      if (norm) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x2 w = *(const u32x2*)(kp + 32 * db + 8 * i);
-        kx[db][4 * i + 0] = __uint_as_float(w[0] << 16);
-        kx[db][4 * i + 1] = __uint_as_float(w[0] & 0xffff0000u);
-        kx[db][4 * i + 2] = __uint_as_float(w[1] << 16);
-        kx[db][4 * i + 3] = __uint_as_float(w[1] & 0xffff0000u);
+          for (int i = 0; i < 4; ++i) {
+            const int kk = 2 * db + i / 2, ln = 32 * (i % 2) + l32;
+            kh[db][i] = *(SA_LDS const u32x2*)(uintptr_t)(xk_lds + (uint32_t)((kk * 64 + ln) * 16 + 8 * half));
+            dot += acc[db][4 * i + 0] * __uint_as_float(kh[db][i][0] << 16);
+            dot += acc[db][4 * i + 1] * __uint_as_float(kh[db][i][0] & 0xffff0000u);
+            dot += acc[db][4 * i + 2] * __uint_as_float(kh[db][i][1] << 16);
+            dot += acc[db][4 * i + 3] * __uint_as_float(kh[db][i][1] & 0xffff0000u);
+          }
+        dot = pair_sum(dot) * p.scale * (1.f / D);  // <dk_hat, k_hat> / D
       }
-    if (rope) {
 #pragma unroll
-      for (int db = 0; db < NDB / 2; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 c = tc[db][i], sn = ts[db][i];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float a = kx[db][4 * i + j], bb = kx[db + NDB / 2][4 * i + j];
-            kx[db][4 * i + j] = a * c[j] - bb * sn[j];
-            kx[db + NDB / 2][4 * i + j] = a * sn[j] + bb * c[j];
+            const float gh = p.scale * acc[db][4 * i + j];
+            const uint32_t wd = kh[db][i][j >> 1];
+            const float kx = __uint_as_float((j & 1) ? (wd & 0xffff0000u) : (wd << 16));
+            acc[db][4 * i + j] = norm ? e_rk * (gh - kx * dot) : gh;
           }
+      if (rope) {
+#pragma unroll
+        for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 c = tc[db][i], sn = ts[db][i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float a = acc[db][4 * i + j], bb = acc[db + NDB / 2][4 * i + j];
+              acc[db][4 * i + j] = a * c[j] + bb * sn[j];
+              acc[db + NDB / 2][4 * i + j] = bb * c[j] - a * sn[j];
+            }
+          }
+      }
+    }
+    // the rows, 1/rms and first tile of the next block have arrived; then this block's dv (group A)
+    // or dk (group B) rows
+    __builtin_amdgcn_s_waitcnt(0);
+    if (e_key < T) {
+      bf16* dst = (bf16*)(grp == 0 ? p.dv : p.dk) + rowoff;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x2 w;
+          w[0] = pack2(acc[db][4 * i], acc[db][4 * i + 1]);
+          w[1] = pack2(acc[db][4 * i + 2], acc[db][4 * i + 3]);
+          *(u32x2*)(dst + 32 * db + 8 * i) = w;
         }
     }
+    // the next block's accumulators start at zero
+    if (more) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        ss += kx[db][r] * kx[db][r];
-        dot += acc[db][r] * kx[db][r];
-      }
-    r_k = fast_rsqrt(pair_sum(ss) * (1.f / D) + p.eps);
-    dot = pair_sum(dot) * r_k * p.scale * (1.f / D);  // <dk_hat, k_hat> / D with k_hat = r k
-  }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float gh = p.scale * acc[db][r];
-      acc[db][r] = norm ? r_k * (gh - kx[db][r] * r_k * dot) : gh;
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
     }
-  if (rope) {
-#pragma unroll
-    for (int db = 0; db < NDB / 2; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 c = tc[db][i], sn = ts[db][i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float a = acc[db][4 * i + j], bb = acc[db + NDB / 2][4 * i + j];
-          acc[db][4 * i + j] = a * c[j] + bb * sn[j];
-          acc[db + NDB / 2][4 * i + j] = bb * c[j] - a * sn[j];
-        }
-      }
+    __syncthreads();
   }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x2 w;
-      w[0] = pack2(acc[db][4 * i], acc[db][4 * i + 1]);
-      w[1] = pack2(acc[db][4 * i + 2], acc[db][4 * i + 3]);
-      *(u32x2*)((bf16*)p.dk + rowoff + 32 * db + 8 * i) = w;
-    }
 }
 
 hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
-  const dim3 grid((unsigned)(p.nkb * p.B * p.Hkv));
+  const dim3 grid((unsigned)min(p.nkb * p.B * p.Hkv, p.nwg));
   if (ev.start != nullptr) {
     const hipError_t e = hipEventRecord(ev.start, stream);
     if (e != hipSuccess) return e;
   }
-  if (head_dim == 128)
-    hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128>), grid, dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64>), grid, dim3(512), 0, stream, p);
+  const bool rope = p.rope.cos != nullptr;
+  if (head_dim == 128) {
+    if (rope)
+      hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128, true>), grid, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128, false>), grid, dim3(512), 0, stream, p);
+  } else {
+    if (rope)
+      hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64, true>), grid, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64, false>), grid, dim3(512), 0, stream, p);
+  }
   const hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
   return e;

@@ -99,6 +99,7 @@ struct BwdParams {
   void* dv;
   float* delta;   // fp32 [B, Hq, T], written by the dQ kernel
   void* qhat;     // bf16 [B, T, Hq, D]: normed q rows written by the dQ kernel (q itself without the norm)
+  const float* rstd_k;  // fp32 [B, T, Hkv]: 1/rms of the k rows, written by the norm pass (with the QK-norm)
   int B, T, Hq, Hkv, G;
   int window;
   float scale;

@@ -149,8 +149,9 @@ def test_workspace_size(sa):
     B, T, Hq, Hkv, D = 16, 2048, 6, 3, 128
     rows = B * T * Hq
     r256 = lambda x: (x + 255) // 256 * 256
+    # normed q rows, Delta, normed k rows, 1/rms of the k rows
     assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D) == r256(rows * D * 2) + r256(rows * 4) + r256(
-        B * T * Hkv * D * 2)
+        B * T * Hkv * D * 2) + r256(B * T * Hkv * 4)
     assert lib.sa_attn_bwd_workspace_bytes(B, T, 5, Hkv, D) == 0
     assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, 80) == 0
 
