@@ -300,10 +300,13 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
 
   // ---- schedule. Tile t is read in intervals 2t (A: q_hat rows), 2t+1 (A:
   // LSE; B: dO rows), 2t+2 (A: dO^T; B: Delta) and 2t+3 (B: q_hat^T). At the
-  // start of its M-phase of tile s each group issues its half of tile s+1
-  // (into the slot of tile s-2, last read in interval 2s-1), and waits for it
-  // at the end of its V-phase of tile s, before the barrier that publishes
-  // it. Group A runs M(t) in interval 2t and V(t) in 2t+1, group B one
+  // start of its M-phase of tile s group A issues its half of tile s+1 (into
+  // the slot of tile s-2, last read in interval 2s-1), and waits for it at the
+  // end of its V-phase of tile s, before the barrier that publishes it. Group
+  // B, whose matrix phase is the longer one, issues its half of tile s+2 at
+  // the end of its V-phase of tile s instead (interval 2s+2, after the last
+  // reads of the slot's tile s-1 in interval 2s), and waits for it a step
+  // later; its half of tile 1 goes out with group A's at the start. Group A runs M(t) in interval 2t and V(t) in 2t+1, group B one
   // interval later; every wave passes 2*nit + 3 barriers (group B one at the
   // start, group A one after its last, empty, V-phase).
   // ---- the epilogue's k_hat exchange: group A wave rw leaves its k_hat
@@ -320,14 +323,16 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
     __syncthreads();
     v_phase(0);
     __builtin_amdgcn_s_waitcnt(0);
+    if (grp == 1 && 2 < nit) issue(2);
     __syncthreads();
 #pragma clang loop unroll(disable)
     for (int t = 1; t < nit; ++t) {
-      if (t + 1 < nit) issue(t + 1);
+      if (grp == 0 && t + 1 < nit) issue(t + 1);
       m_phase(t, std::integral_constant<int, K_MID>{});
       __syncthreads();
       v_phase(t);
       __builtin_amdgcn_s_waitcnt(0);
+      if (grp == 1 && t + 2 < nit) issue(t + 2);
       __syncthreads();
     }
     m_phase(nit, std::integral_constant<int, K_LAST>{});
