@@ -409,3 +409,47 @@ def test_value_embedding_ids_outside_the_table_read_zero_rows(sa):
     table_ref = torch.cat([table, torch.zeros(1, Hkv * D, dtype=table.dtype)])
     o_r, lse_r = oracle.attn_forward(q, k, v, W, D ** -0.5, ve=(x[..., :32], w, ids_ref, table_ref))
     _check_o_mixed(o, lse, o_r, lse_r)
+
+
+def test_graph_replay_matches_eager(sa):
+    """The forward and backward captured in a HIP graph (as the benchmark and a
+    trainer replay their step) give, on every replay, exactly the eager
+    results; eager work on other data runs between the replays. The library
+    launches kernels only (no memset or copy nodes), so nothing in the graph
+    depends on the capture."""
+    B, T, Hq, Hkv, D, W = 2, 300, 6, 3, 128, 100
+    scale = D ** -0.5
+    log("[graph replay]")
+    q, k, v, do = (x.cuda() for x in synth.small_case(B, T, Hq, Hkv, D, seed=811))
+    q2, k2, v2, do2 = (x.cuda() for x in synth.small_case(B, T, Hq, Hkv, D, seed=812))
+    o, lse = sa.sa_attn_fwd(q, k, v, window=W, softmax_scale=scale)
+    ref = (o.clone(), lse.clone()) + tuple(t.clone() for t in sa.sa_attn_bwd(q, k, v, o, lse, do, window=W,
+                                                                                  softmax_scale=scale))
+    go, glse = torch.empty_like(o), torch.empty_like(lse)
+    gdq, gdk, gdv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsf = torch.empty(sa.sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(sa.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8, device="cuda")
+
+    def body():
+        sa.sa_attn_fwd(q, k, v, window=W, softmax_scale=scale, o=go, lse=glse, workspace=wsf)
+        sa.sa_attn_bwd(q, k, v, go, glse, do, window=W, softmax_scale=scale, dq=gdq, dk=gdk, dv=gdv, workspace=wsb)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            body()
+    torch.cuda.current_stream().wait_stream(cap)
+    for rep in range(3):
+        for t in (go, glse, gdq, gdk, gdv):
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("o", "lse", "dq", "dk", "dv"), (go, glse, gdq, gdk, gdv), ref):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager result"
+        # eager work on other data (same workspaces) between replays
+        o2, lse2 = sa.sa_attn_fwd(q2, k2, v2, window=W, softmax_scale=scale, workspace=wsf)
+        sa.sa_attn_bwd(q2, k2, v2, o2, lse2, do2, window=W, softmax_scale=scale, workspace=wsb)
+        torch.cuda.synchronize()
