@@ -10,6 +10,7 @@ from .attention import (  # noqa: F401
     attn_backward,
     attn_backward_delta,
     attn_forward,
+    attn_forward_rows,
     band_mask,
     kv_head,
     qknorm,

@@ -292,6 +292,40 @@ def attn_forward(q, k, v, window, scale, qk_norm=True, eps=1e-6, rope=None, ve=N
     return o, lse
 
 
+def attn_forward_rows(q, k, v, rows, window, scale, qk_norm=True, eps=1e-6):
+    """O and LSE of selected query rows of every (batch, head), in float64:
+    the forward's definition (masked softmax of the scaled normed logits, then
+    the weighted sum of v) evaluated for the rows listed only, so that every
+    (batch, head) of a full-size layer can be sampled at small cost.
+
+    rows: 1-D sequence of query positions; returns (o [B, R, Hq, D],
+    lse [B, Hq, R]) for the R rows in the order given.
+    """
+    B, T, Hq, Hkv, D = _check_shapes(q, k, v)
+    rows = torch.as_tensor(rows, dtype=torch.long)
+    R = rows.numel()
+    q_sel = q[:, rows]
+    if qk_norm:
+        q_hat, _ = rms_norm(q_sel, eps)
+        k_hat, _ = rms_norm(k, eps)
+    else:
+        q_hat, k_hat = q_sel.to(F64), k.to(F64)
+    vv = v.to(F64)
+    mask = band_mask(T, window)[rows]  # [R, T]
+    o = torch.zeros(B, R, Hq, D, dtype=F64)
+    lse = torch.zeros(B, Hq, R, dtype=F64)
+    for h in range(Hq):
+        g = kv_head(h, Hq, Hkv)
+        S = scale * (q_hat[:, :, h] @ k_hat[:, :, g].transpose(1, 2))  # [B, R, T]
+        S = S.masked_fill(~mask, -math.inf)
+        m = S.max(dim=-1, keepdim=True).values
+        e = torch.exp(S - m)
+        denom = e.sum(dim=-1, keepdim=True)
+        o[:, :, h] = (e / denom) @ vv[:, :, g]
+        lse[:, h] = (m + torch.log(denom)).squeeze(-1)
+    return o, lse
+
+
 # ---------------------------------------------------------------- backward
 
 def attn_backward(q, k, v, do, window, scale, qk_norm=True, eps=1e-6, rope=None, ve=None):

@@ -99,3 +99,29 @@ def compare_backward(dq, dk, dv, q, k, v, do, W, scale, qk_norm=True, eps=1e-6, 
         else:
             assert errs[n] <= tol, f"{n} rel-L2 {errs[n]}"
     return errs
+
+
+# Polar express (Muon's orthogonalisation): per-tile bounds. The GPU keeps X,
+# A = X X^T and B = b A + c A A in bf16 between products (2^-9 relative per
+# element per rounding). After one step the exact result is dominated by the
+# linear term a X (the singular values of G / ||G||_F of these gradients are
+# far below 1, where the step's polynomial does not cancel), so every 128 x 128
+# tile stays within a few 2^-9 of its reference: 1e-2 per tile leaves ~4x
+# margin over the measured ~2e-3. After five steps the roundings of each step
+# compound (measured 1-1.6e-2 per matrix); 5e-2 per tile bounds them. A single
+# tile computed wrongly (a mirrored or split-K tile, say) by 30% fails either
+# bound, which a whole-matrix norm at 36 tiles (30% x 1/6 = 5e-2) would not.
+POLAR_TILE = 128
+POLAR_TILE_REL = {1: 1e-2}
+POLAR_TILE_REL_DEFAULT = 5e-2
+
+
+def polar_tile_rel_errors(got, ref, tile=POLAR_TILE):
+    """Relative Frobenius error of every tile x tile block of [m, n] matrices (float64)."""
+    got, ref = got.double(), ref.double()
+    m, n = ref.shape[-2:]
+    gt = got.reshape(m // tile, tile, n // tile, tile)
+    rt = ref.reshape(m // tile, tile, n // tile, tile)
+    num = (gt - rt).pow(2).sum(dim=(1, 3)).sqrt()
+    den = rt.pow(2).sum(dim=(1, 3)).sqrt().clamp_min(1e-300)
+    return num / den

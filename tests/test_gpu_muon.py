@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import log, set_cpu_threads
+from gpu_helpers import (POLAR_TILE_REL, POLAR_TILE_REL_DEFAULT, log, polar_tile_rel_errors,
+                         set_cpu_threads)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,19 +41,23 @@ def _check(sa, g, steps=5, idx=None):
     torch.cuda.synchronize()
     out = out.cpu()
     idx = range(g.shape[0]) if idx is None else idx
-    worst = 0.0
+    worst = worst_tile = 0.0
+    tile_bound = POLAR_TILE_REL.get(steps, POLAR_TILE_REL_DEFAULT)
     for i in idx:
         ref = oracle.polar_express(g[i:i + 1], steps=steps)[0]
         got = out[i].double()
         assert torch.isfinite(got).all()
         err = float((got - ref).norm() / ref.norm())
         worst = max(worst, err)
+        # every 128 x 128 tile on its own: a wrongly mirrored or split-K tile fails here
+        worst_tile = max(worst_tile, float(polar_tile_rel_errors(got, ref).max()))
         if steps == 5:
             sv = torch.linalg.svdvals(got)
             sr = torch.linalg.svdvals(ref)
             assert float(sv.max()) < float(sr.max()) + 0.1 and float(sv.min()) > float(sr.min()) - 0.1
-    log(f"  {tuple(g.shape)} steps {steps}: worst rel-Frobenius {worst:.3e}")
+    log(f"  {tuple(g.shape)} steps {steps}: worst rel-Frobenius {worst:.3e}, worst 128x128 tile {worst_tile:.3e}")
     assert worst <= POLAR_REL_FRO
+    assert worst_tile <= tile_bound, f"a tile is off by {worst_tile:.3e} (bound {tile_bound})"
     return out
 
 
@@ -67,6 +72,16 @@ def test_polar_express_small(sa, shape):
     _check(sa, _grad(shape, 300 + shape[1]))
 
 
+@pytest.mark.parametrize("shape", [(1, 2048, 2048), (2, 512, 3072), (1, 256, 2048), (2, 384, 256)])
+def test_polar_express_one_step_tiles(sa, shape):
+    """One step, where the per-tile bound is tight (1e-2): the symmetric
+    products' mirrored tiles and the split-K reductions (K = 2048: A = X X^T
+    and A A both split in two, with mirrored tiles; K = 3072: the Gram in
+    three) against the exact iteration, tile by tile."""
+    log(f"[polar, 1 step] {shape}")
+    _check(sa, _grad(shape, 350 + shape[1]), steps=1)
+
+
 @pytest.mark.parametrize("steps", [1, 2, 5])
 def test_polar_express_steps(sa, steps):
     log(f"[polar] steps {steps}")
@@ -78,7 +93,10 @@ def test_polar_express_model_shape_groups(sa, shape):
     """The trainer's Muon groups at n_embd 768: attention projections and the
     MLP's two matrices, every matrix of the stack computed, two compared."""
     log(f"[polar] model group {shape}")
-    _check(sa, _grad(shape, 500 + shape[2]), idx=[0, shape[0] - 1])
+    g = _grad(shape, 500 + shape[2])
+    _check(sa, g, idx=[0, shape[0] - 1])
+    # one step, tile by tile, on more matrices of the stack
+    _check(sa, g, steps=1, idx=sorted({0, 1, shape[0] // 2, shape[0] - 2, shape[0] - 1}))
 
 
 def test_polar_express_transpose_symmetry(sa):

@@ -61,6 +61,25 @@ def _check_slices(w, layer, q, k, v, do, out, slices, o_rel=0.0, rope=None, ve=N
                          eps=w.eps, rope=rope, ve=ve_slice)
 
 
+def _check_rows(w, layer, q, k, v, o, lse, o_rel=0.0, n_random=4):
+    """Every (batch, head) of the full-size layer, on sampled query rows: the
+    first rows (few keys), the middle, the last, and seeded random ones,
+    against the oracle's row-by-row forward."""
+    import oracle
+
+    T = w.T
+    g = torch.Generator().manual_seed(1000 + layer)
+    rows = sorted({0, 1, 2, 3, T // 2, T - 1} | set(torch.randint(0, T, (n_random,), generator=g).tolist()))
+    o_ref, lse_ref = oracle.attn_forward_rows(q, k, v, rows, w.windows[layer], w.scale, eps=w.eps)
+    got_o = o.cpu()[:, rows].double()
+    diff = (got_o - o_ref).abs()
+    bound = 2e-2 + o_rel * o_ref.abs()
+    el = float((lse.cpu()[:, :, rows].double() - lse_ref).abs().max())
+    log(f"  all {w.B}x{w.Hq} (batch, head) on rows {rows}: O max-abs {float(diff.max()):.3e}, LSE max-abs {el:.3e}")
+    assert bool((diff <= bound).all())
+    assert el <= 2e-2
+
+
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_single_layer_workloads(sa, cfg):
     w = synth.WORKLOADS[cfg]
@@ -77,15 +96,20 @@ def test_sssl_stack_workload(sa):
         q, k, v, do = synth.layer_inputs(w, layer)
         out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[layer], w.scale, eps=w.eps)
         _check_slices(w, layer, q, k, v, do, out, [(layer % w.B, layer % w.Hkv)])
+        _check_rows(w, layer, q, k, v, out[0], out[1])
 
 
-@pytest.mark.parametrize("layer", [0, 3])
+@pytest.mark.parametrize("layer", list(range(8)))
 def test_long_context_workload(sa, layer):
+    """All 8 layers of the long-context stack at full size: one (batch, KV
+    group) slice each against the oracle, and every (batch, head) on sampled
+    rows."""
     w = synth.WORKLOADS[5]
     log(f"[workload 5] {w.name} layer {layer}")
     q, k, v, do = synth.layer_inputs(w, layer)
     out = gpu_fwd_bwd(sa, q, k, v, do, w.windows[layer], w.scale, eps=w.eps)
-    _check_slices(w, layer, q, k, v, do, out, [(layer % w.B, 1)], o_rel=2.0 ** -7)
+    _check_slices(w, layer, q, k, v, do, out, [(layer % w.B, layer % w.Hkv)], o_rel=2.0 ** -7)
+    _check_rows(w, layer, q, k, v, out[0], out[1], o_rel=2.0 ** -7)
 
 
 def test_long_context_qk_rows_only(sa):
@@ -147,3 +171,54 @@ def test_sssl_stack_with_value_embeddings(sa, layer):
     e_w, e_x = rel_l2(dw.cpu(), dw_r), rel_l2(dx32.cpu(), dx_r)
     log(f"  dw rel-L2 {e_w:.3e}  dx32 rel-L2 {e_x:.3e}")
     assert e_w <= 5e-2 and e_x <= 5e-2
+
+
+@pytest.mark.parametrize("layer", [1, 3])
+def test_value_embedding_gate_gradients_full_size(sa, layer):
+    """The gate's weight and input gradients at full size, against the oracle
+    alone. dW sums over every position and head, so the full-size call gets an
+    upstream gradient that is zero outside batch row b0: dW, dx32 and dve then
+    hold that row's contributions only, which the oracle computes from the
+    row's q, k, v, dO and gate inputs over all its KV heads (no GPU value
+    enters the reference). Rows with zero upstream gradient must give exactly
+    zero gradients."""
+    import oracle
+    from gpu_helpers import rel_l2
+
+    w = synth.WORKLOADS[4]
+    b0 = 2 + layer
+    log(f"[workload 4 + value embeddings, dO in batch row {b0} only] layer {layer}")
+    q, k, v, do = synth.layer_inputs(w, layer)
+    do_z = torch.zeros_like(do)
+    do_z[b0] = do[b0]
+    ve = synth.ve_inputs(w, layer)
+    x, gw, ids, table = ve
+    W = w.windows[layer]
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do_z))
+    ve_d = tuple(t.cuda() for t in ve)
+    o, lse = sa.sa_attn_fwd(qd, kd, vd, window=W, softmax_scale=w.scale, eps=w.eps, ve=ve_d)
+    dq, dk, dv, dve, dw, dx32 = sa.sa_attn_bwd(qd, kd, vd, o, lse, dod, window=W, softmax_scale=w.scale,
+                                               eps=w.eps, ve=ve_d)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    dw_ref = torch.zeros((w.Hkv, 32), dtype=torch.float64)
+    dx_ref = torch.zeros((w.T, 32), dtype=torch.float64)
+    dve_ref = torch.zeros((w.T, w.Hkv, w.D), dtype=torch.float64)
+    for g in range(w.Hkv):
+        hs = slice(g * G, (g + 1) * G)
+        ve_g = (x[b0:b0 + 1, :, :32], gw[g:g + 1], ids[b0:b0 + 1], table[:, g * w.D:(g + 1) * w.D])
+        _, _, _, dve_g, dw_g, dx_g = oracle.attn_backward(q[b0:b0 + 1, :, hs], k[b0:b0 + 1, :, g:g + 1],
+                                                          v[b0:b0 + 1, :, g:g + 1], do[b0:b0 + 1, :, hs], W,
+                                                          w.scale, eps=w.eps, ve=ve_g)
+        dw_ref[g] = dw_g[0]
+        dx_ref += dx_g[0]
+        dve_ref[:, g] = dve_g[0, :, 0]
+    e_w = rel_l2(dw.cpu(), dw_ref)
+    e_x = rel_l2(dx32[b0].cpu(), dx_ref)
+    e_ve = rel_l2(dve[b0].cpu(), dve_ref)
+    log(f"  dw rel-L2 {e_w:.3e}  dx32 rel-L2 {e_x:.3e}  dve rel-L2 {e_ve:.3e}")
+    assert e_w <= 5e-2 and e_x <= 5e-2 and e_ve <= 5e-2
+    others = torch.ones(w.B, dtype=torch.bool)
+    others[b0] = False
+    for name, t in (("dx32", dx32), ("dve", dve), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert not bool(t[others.cuda()].float().abs().max() > 0), f"{name} nonzero outside batch row {b0}"

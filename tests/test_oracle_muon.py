@@ -105,3 +105,22 @@ def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
     assert _pins_pass()
     monkeypatch.setattr(OM, name, mutant)
     assert not _pins_pass(), f"planted mistake in {name} went unnoticed"
+
+
+def test_polar_tile_check_catches_one_wrong_tile():
+    """The GPU test's per-tile check, exercised on the oracle's own result: a
+    copy passes, and one 128 x 128 tile made 25% wrong (as a wrong mirrored
+    or split-K tile would be) fails the tile bound although the whole-matrix
+    error stays within the per-matrix bound."""
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from gpu_helpers import POLAR_TILE_REL, polar_tile_rel_errors
+
+    g = torch.randn((1, 768, 768), generator=torch.Generator().manual_seed(9), dtype=torch.float64)
+    ref = oracle.polar_express(g, steps=1)[0]
+    assert float(polar_tile_rel_errors(ref.clone(), ref).max()) == 0.0
+    bad = ref.clone()
+    bad[256:384, 512:640] *= 1.25
+    whole = float((bad - ref).norm() / ref.norm())
+    assert whole < 5e-2  # a whole-matrix bound alone would let it through
+    assert float(polar_tile_rel_errors(bad, ref).max()) > POLAR_TILE_REL[1]

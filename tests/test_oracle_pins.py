@@ -616,3 +616,21 @@ def test_pins_catch_planted_mistake(monkeypatch, name, mutant):
     monkeypatch.setitem(OA.__dict__, "_real_probs", OA._probs_one_head)
     monkeypatch.setattr(OA, name, mutant)
     assert not _all_pins_pass(), f"planted mistake in {name} went unnoticed"
+
+
+@pytest.mark.parametrize("W,Hq,Hkv", [(-1, 4, 2), (5, 6, 3), (0, 2, 2), (12, 4, 1)])
+def test_row_sampled_forward_equals_the_full_forward(W, Hq, Hkv):
+    """attn_forward_rows (used to sample every (batch, head) of full-size
+    layers) is the full forward restricted to the rows asked for, in any order,
+    with or without the norm."""
+    B, T, D = 2, 37, 16
+    g = torch.Generator().manual_seed(31 + W)
+    q = torch.randn(B, T, Hq, D, generator=g, dtype=torch.float64)
+    k = torch.randn(B, T, Hkv, D, generator=g, dtype=torch.float64)
+    v = torch.randn(B, T, Hkv, D, generator=g, dtype=torch.float64)
+    rows = [36, 0, 17, 5, 5, 30]
+    for qk_norm in (True, False):
+        o, lse = oracle.attn_forward(q, k, v, W, 0.3, qk_norm=qk_norm)
+        o_r, lse_r = oracle.attn_forward_rows(q, k, v, rows, W, 0.3, qk_norm=qk_norm)
+        assert torch.allclose(o_r, o[:, rows], rtol=0, atol=1e-12)
+        assert torch.allclose(lse_r, lse[:, :, rows], rtol=0, atol=1e-12)
