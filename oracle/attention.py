@@ -292,14 +292,16 @@ def attn_forward(q, k, v, window, scale, qk_norm=True, eps=1e-6, rope=None, ve=N
     return o, lse
 
 
-def attn_forward_rows(q, k, v, rows, window, scale, qk_norm=True, eps=1e-6):
+def attn_forward_rows(q, k, v, rows, window, scale, qk_norm=True, eps=1e-6, with_abs=False):
     """O and LSE of selected query rows of every (batch, head), in float64:
     the forward's definition (masked softmax of the scaled normed logits, then
     the weighted sum of v) evaluated for the rows listed only, so that every
     (batch, head) of a full-size layer can be sampled at small cost.
 
     rows: 1-D sequence of query positions; returns (o [B, R, Hq, D],
-    lse [B, Hq, R]) for the R rows in the order given.
+    lse [B, Hq, R]) for the R rows in the order given, and with with_abs also
+    the weighted sum of |v| with the same probabilities (the scale of O's
+    rounding error when the averaged values have mixed signs).
     """
     B, T, Hq, Hkv, D = _check_shapes(q, k, v)
     rows = torch.as_tensor(rows, dtype=torch.long)
@@ -313,6 +315,7 @@ def attn_forward_rows(q, k, v, rows, window, scale, qk_norm=True, eps=1e-6):
     vv = v.to(F64)
     mask = band_mask(T, window)[rows]  # [R, T]
     o = torch.zeros(B, R, Hq, D, dtype=F64)
+    o_abs = torch.zeros(B, R, Hq, D, dtype=F64)
     lse = torch.zeros(B, Hq, R, dtype=F64)
     for h in range(Hq):
         g = kv_head(h, Hq, Hkv)
@@ -322,8 +325,10 @@ def attn_forward_rows(q, k, v, rows, window, scale, qk_norm=True, eps=1e-6):
         e = torch.exp(S - m)
         denom = e.sum(dim=-1, keepdim=True)
         o[:, :, h] = (e / denom) @ vv[:, :, g]
+        if with_abs:
+            o_abs[:, :, h] = (e / denom) @ vv[:, :, g].abs()
         lse[:, h] = (m + torch.log(denom)).squeeze(-1)
-    return o, lse
+    return (o, lse, o_abs) if with_abs else (o, lse)
 
 
 # ---------------------------------------------------------------- backward

@@ -11,7 +11,11 @@ v rows scaled, |O| reaches ~15-26, where one bf16 step is 0.0625-0.125, so
 storing O in bf16 alone can exceed a 2e-2 absolute bound. For that workload O
 is held to |diff| <= 2e-2 + 2^-7 |O_ref| elementwise (one bf16 step relative
 on top of the absolute bound), and a variant that scales only q and k (the
-rows that reach the softmax) is held to the plain 2e-2 bound.
+rows that reach the softmax) is held to the plain 2e-2 bound. On the rows
+sampled across every (batch, head) the relative part is taken of sum_j P_ij
+|v_j| rather than of |O_ref|: the bf16 rounding of the probabilities and of
+O scales with that sum, which exceeds |O_ref| where large scaled values of
+opposite signs nearly cancel in the average.
 """
 
 import pytest
@@ -48,9 +52,15 @@ def _check_slices(w, layer, q, k, v, do, out, slices, o_rel=0.0, rope=None, ve=N
         os_, ls = o[b:b + 1, :, hs], lse[b:b + 1, hs]
         if o_rel > 0:
             import oracle
-            o_ref, lse_ref = oracle.attn_forward(qs, kk, vs, W, w.scale, eps=w.eps, ve=ve_slice)
+            if ve_slice is None:
+                # relative part of sum_j P_ij |v_j| (see the module docstring)
+                o_ref, lse_ref, o_scale = oracle.attn_forward_rows(qs, kk, vs, range(w.T), W, w.scale, eps=w.eps,
+                                                                   with_abs=True)
+            else:
+                o_ref, lse_ref = oracle.attn_forward(qs, kk, vs, W, w.scale, eps=w.eps, ve=ve_slice)
+                o_scale = o_ref.abs()
             diff = (os_.cpu().double() - o_ref).abs()
-            bound = 2e-2 + o_rel * o_ref.abs()
+            bound = 2e-2 + o_rel * o_scale
             log(f"  O max-abs {float(diff.max()):.3e} (mixed bound), LSE max-abs "
                 f"{float((ls.cpu().double() - lse_ref).abs().max()):.3e}")
             assert bool((diff <= bound).all())
@@ -70,10 +80,11 @@ def _check_rows(w, layer, q, k, v, o, lse, o_rel=0.0, n_random=4):
     T = w.T
     g = torch.Generator().manual_seed(1000 + layer)
     rows = sorted({0, 1, 2, 3, T // 2, T - 1} | set(torch.randint(0, T, (n_random,), generator=g).tolist()))
-    o_ref, lse_ref = oracle.attn_forward_rows(q, k, v, rows, w.windows[layer], w.scale, eps=w.eps)
+    o_ref, lse_ref, o_abs = oracle.attn_forward_rows(q, k, v, rows, w.windows[layer], w.scale, eps=w.eps,
+                                                     with_abs=True)
     got_o = o.cpu()[:, rows].double()
     diff = (got_o - o_ref).abs()
-    bound = 2e-2 + o_rel * o_ref.abs()
+    bound = 2e-2 + o_rel * o_abs
     el = float((lse.cpu()[:, :, rows].double() - lse_ref).abs().max())
     log(f"  all {w.B}x{w.Hq} (batch, head) on rows {rows}: O max-abs {float(diff.max()):.3e}, LSE max-abs {el:.3e}")
     assert bool((diff <= bound).all())

@@ -634,3 +634,12 @@ def test_row_sampled_forward_equals_the_full_forward(W, Hq, Hkv):
         o_r, lse_r = oracle.attn_forward_rows(q, k, v, rows, W, 0.3, qk_norm=qk_norm)
         assert torch.allclose(o_r, o[:, rows], rtol=0, atol=1e-12)
         assert torch.allclose(lse_r, lse[:, :, rows], rtol=0, atol=1e-12)
+    # the absolute weighted sum: P |v| with the full forward's probabilities, never below |O|
+    _, _, o_abs = oracle.attn_forward_rows(q, k, v, rows, W, 0.3, with_abs=True)
+    P = oracle.attention_probs(q, k, W, 0.3)  # [B, Hq, T, T]
+    G = Hq // Hkv
+    for h in range(Hq):
+        want = P[:, h][:, rows] @ v[:, :, h // G].abs()
+        assert torch.allclose(o_abs[:, :, h], want, rtol=0, atol=1e-12)
+    o, _ = oracle.attn_forward(q, k, v, W, 0.3)
+    assert bool((o_abs >= o[:, rows].abs() - 1e-12).all())
