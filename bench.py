@@ -48,7 +48,12 @@ KERNELS = {
     "fwd": ("attn_fwd_pp_kernel", ("attn_fwd_pp.hip", "sa_common.h")),
     "bwd_dq": ("attn_bwd_dq_pp_kernel", ("attn_bwd_dq_pp.hip", "sa_common.h")),
     "bwd_dkdv": ("attn_bwd_dkdv_pp_kernel", ("attn_bwd_dkdv_pp.hip", "sa_common.h")),
+    "kv_prep": ("kv_prep_kernel", ("kv_prep.hip", "sa_common.h", "ve_common.h")),
+    "bwd_knorm": ("qknorm_kernel", ("qknorm.hip", "sa_common.h")),
 }
+# the MFMA-bound attention kernels and the HBM-bound passes that prepare their key/value rows
+MFMA_KINDS = ("fwd", "bwd_dq", "bwd_dkdv")
+HBM_KINDS = ("kv_prep", "bwd_knorm")
 
 
 def source_hash(files) -> str:
@@ -65,6 +70,11 @@ def band_pairs(T: int, W: int) -> int:
     if W < 0 or W >= T - 1:
         return T * (T + 1) // 2
     return (W + 1) * (T - W) + W * (W + 1) // 2
+
+
+def variant_tag(args) -> str:
+    """Suffix of the profile files of a run with rotary tables and/or value embeddings."""
+    return ("_rope" if args.rope else "") + ("_ve" if args.ve else "")
 
 
 def traffic_file(workload: str) -> str:
@@ -110,7 +120,7 @@ def _per_dispatch(rows, counter):
     return out
 
 
-def summarize_pmc(fetch_dir, write_dir, workload):
+def summarize_pmc(fetch_dir, write_dir, workload, extra=""):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernels by
     what the same counters read for the copy probe (COPY_PROBE_BYTES in, same out),
     and write profiles/traffic_<workload>.json."""
@@ -146,10 +156,10 @@ def summarize_pmc(fetch_dir, write_dir, workload):
         "kernels": kernels,
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o pmc -- python -u bench.py --steps 2 "
-            "--warmup 1 --cpu-seconds 0 --no-kernel-events --copy-probe",
+            f"--warmup 1 --cpu-seconds 0 --no-kernel-events --no-graph --copy-probe{extra}",
             "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o pmc -- python -u bench.py --steps 2 "
-            "--warmup 1 --cpu-seconds 0 --no-kernel-events --copy-probe",
-            "python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write",
+            f"--warmup 1 --cpu-seconds 0 --no-kernel-events --no-graph --copy-probe{extra}",
+            f"python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write{extra}",
         ],
     }
     os.makedirs(PROFILES, exist_ok=True)
@@ -185,6 +195,14 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --copy-probe` into profiles/ and exit (no GPU needed)")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS0_DIR", "PASS1_DIR"),
+                    help="summarize the two rocprofv3 --pmc SQ counter passes of this script into profiles/ "
+                         "and exit (no GPU needed)")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "TRACE_JSON", "PLAIN_JSON", "COMMAND"),
+                    help="summarize a rocprofv3 --kernel-trace run of this script (its JSON line in TRACE_JSON) "
+                         "over the dispatches that the run's HIP events timed, beside the events of that run "
+                         "and of a run without the profiler (its JSON line in PLAIN_JSON); COMMAND is the "
+                         "command line that made them. Writes profiles/ and exits (no GPU needed)")
     return ap.parse_args()
 
 
@@ -213,16 +231,195 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(h))
 
 
+def hbm_bytes_per_launch(kind, w, ve_layer=False):
+    """Algorithmic HBM bytes of one launch of an HBM-bound pass: every element it must read,
+    read once, and every element it must write, written once (bf16 rows, fp32 1/rms).
+    kv_prep reads k and v and writes k_hat and the key-padded transposed v; with value
+    embeddings it also reads the gate's 32 input channels, the token id and the table rows.
+    The backward's k-norm pass reads k and writes k_hat and 1/rms per row."""
+    rows = w.B * w.T * w.Hkv
+    tp = (w.T + 63) // 64 * 64
+    if kind == "kv_prep":
+        b = 2 * rows * w.D * 2 + rows * w.D * 2 + w.B * w.Hkv * w.D * tp * 2
+        if ve_layer:
+            b += w.B * w.T * (32 * 2 + 4) + rows * w.D * 2
+        return b
+    if kind == "bwd_knorm":
+        return rows * w.D * 2 * 2 + rows * 4
+    raise ValueError(kind)
+
+
+def _json_line(path):
+    with open(path) as fh:
+        return json.loads([ln for ln in fh if ln.lstrip().startswith("{")][-1])
+
+
+def summarize_trace(trace_dir, trace_json, plain_json, command):
+    """Per-kernel durations of a rocprofv3 --kernel-trace run of this script, averaged over the
+    dispatches of its per-kernel pass (the last steps x layers launches of each kernel: the ones
+    its HIP events bracketed), beside the event figures of the same run and of a run without the
+    profiler; writes profiles/attn_kernels_<workload>_trace.md."""
+    import synth
+
+    rec = _json_line(trace_json)
+    plain = _json_line(plain_json)
+    cfg = rec["config"]
+    w = [x for x in synth.WORKLOADS.values() if x.name == cfg["workload"]][0]
+    n_last = rec["steps"] * w.n_layer
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *kernel_trace.csv under {trace_dir}")
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(r)
+    tag = ("_rope" if cfg.get("rope") else "") + ("_ve" if cfg.get("value_embeddings") else "")
+    out = [f"# Kernel trace: {cfg['workload']}{' with rotary tables' if cfg.get('rope') else ''}"
+           f"{' and value embeddings' if cfg.get('value_embeddings') else ''}", "",
+           f"B={w.B}, T={w.T}, Hq={w.Hq}, Hkv={w.Hkv}, D={w.D}, windows {list(w.windows)}.", "",
+           "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
+           f"Averages over the last {n_last} dispatches of each kernel ({rec['steps']} steps x {w.n_layer} layers: "
+           "the per-kernel pass, whose launches the script's HIP events bracket). Beside them: those events "
+           "(same process, under the profiler, which adds a few microseconds to every event pair), and the "
+           f"events of a run without the profiler ({plain['steps']} steps), which the JSON line's roofline "
+           "comes from. The headline pass before the per-kernel pass replays a HIP graph of the step.", "",
+           "| kernel | dispatches in run | avg us (trace) | min us | max us | avg us (events, profiled run) | "
+           "avg us (events, plain run) | trace / plain events |",
+           "|---|---|---|---|---|---|---|---|"]
+    ev = rec.get("kernels") or {}
+    ev_plain = plain.get("kernels") or {}
+    shapes = []
+    summary = {}
+    for slot, (name, _) in KERNELS.items():
+        hits = [k for k in by if k.startswith(name + "<") or k == name]
+        if not hits:
+            continue
+        disp = sorted((r for k in hits for r in by[k]), key=lambda r: int(r["Start_Timestamp"]))
+        last = disp[-n_last:]
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in last]
+        avg = sum(d) / len(d)
+        e_ms, p_ms = ev.get(f"{slot}_ms_per_step"), ev_plain.get(f"{slot}_ms_per_step")
+        e_us = e_ms * 1e3 / w.n_layer if e_ms is not None else None
+        p_us = p_ms * 1e3 / w.n_layer if p_ms is not None else None
+        summary[slot] = avg
+        out.append(f"| {name} | {len(disp)} | {avg:.1f} | {min(d):.1f} | {max(d):.1f} | "
+                   f"{'%.1f' % e_us if e_us else '-'} | {'%.1f' % p_us if p_us else '-'} | "
+                   f"{'%.3f' % (avg / p_us) if p_us else '-'} |")
+        r0 = last[-1]
+        shapes.append(f"- {name}: grid {r0['Grid_Size_X']}x{r0['Grid_Size_Y']}, wg {r0['Workgroup_Size_X']}, "
+                      f"LDS {r0['LDS_Block_Size']}, VGPR {r0['VGPR_Count']}, AGPR {r0['Accum_VGPR_Count']}, "
+                      f"scratch {r0['Scratch_Size']}")
+    out += ["", "Launch shape (grid threads, workgroup threads, LDS bytes, VGPR/AGPR as reported, scratch):", ""]
+    out += shapes
+    rf = plain.get("roofline")
+    if rf:
+        slot = [s for s, (n, _) in KERNELS.items() if n == rf["kernel"]][0]
+        tr = rf["algorithmic_flop_per_launch"] / (summary[slot] * 1e-6) / 1e12
+        out += ["", f"Roofline of the dominant kernel ({rf['kernel']}): {rf['algorithmic_flop_per_launch']:.4g} "
+                    f"algorithmic FLOP per launch ({rf['flop_per_visible_pair']} per visible pair). From the trace "
+                    f"average: {tr:.0f} TFLOP/s = {tr / PEAK_BF16_TFLOPS:.4f} of {PEAK_BF16_TFLOPS:g}; from the "
+                    f"plain run's events (its JSON line's roofline): {rf['achieved']:.0f} TFLOP/s = "
+                    f"{rf['frac']:.4f}.", ""]
+    for slot in HBM_KINDS:
+        if slot in summary:
+            gb = ev_plain.get(f"{slot}_algorithmic_bytes")
+            if gb:
+                out.append(f"- {KERNELS[slot][0]}: {gb / 1e6:.1f} MB algorithmic per launch; "
+                           f"{gb / (summary[slot] * 1e-6) / 1e9:.0f} GB/s from the trace average, "
+                           f"{ev_plain.get(f'{slot}_gbs', 0):.0f} GB/s from the plain run's events "
+                           f"(peak {PEAK_HBM_GBS:g}).")
+    out += ["", f"Headlines: {rec['ms_per_step']:.3f} ms per step under the profiler, {plain['ms_per_step']:.3f} "
+                f"ms per step ({plain['value']:.1f} TFLOP/s, {plain['pct_bf16_peak']:.2f}% of bf16 peak) in the "
+                f"plain run; {plain['config'].get('launch')}."]
+    path = os.path.join(PROFILES, f"attn_kernels_{cfg['workload']}{tag}_trace.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    print("\n".join(out))
+    print(f"wrote {path}", file=sys.stderr)
+
+
+SQ_PASSES = (
+    "SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS "
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS GRBM_GUI_ACTIVE",
+    "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_MFMA SQ_INSTS_VALU "
+    "SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+)
+
+
+def summarize_sq(dir_a, dir_b, workload, extra=""):
+    """Utilisation ratios of each kernel from two rocprofv3 --pmc passes (SQ_PASSES) of this
+    script; writes profiles/sq_counters_<workload>.md. GRBM_GUI_ACTIVE is summed over the 8 XCDs
+    in the counter output (and present in both passes), so one XCD's busy cycles per dispatch is
+    its per-kernel sum / dispatches / 2 / 8; a SIMD-cycle budget is that times 1024 SIMDs."""
+    agg, disp = {}, {}
+    for d in (dir_a, dir_b):
+        for r in _pmc_rows(d):
+            k = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("sa::", "")
+            c = agg.setdefault(k, {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            disp.setdefault(k, set()).add((d, r["Dispatch_Id"]))
+    lines = []
+    for slot, (name, _) in KERNELS.items():
+        for k, c in agg.items():
+            if not k.startswith(name + "<"):
+                continue
+            nd = len(disp[k]) / 2
+
+            def f(x):
+                return c.get(x, 0.0) / nd
+
+            g = c["GRBM_GUI_ACTIVE"] / nd / 2 / 8
+            simd, cu = g * 1024, g * 256
+            wave = max(1.0, f("SQ_WAVE_CYCLES"))
+            lines.append(
+                f"{k[:40]:40s} GRBM/xcd {g:8.0f}  MFMA-busy {f('SQ_VALU_MFMA_BUSY_CYCLES') / simd:6.1%}  "
+                f"VALU-active {4 * f('SQ_ACTIVE_INST_VALU') / simd:6.1%}  coexec "
+                f"{f('SQ_VALU_MFMA_COEXEC_CYCLES') / simd:6.1%}  LDS-active {f('SQ_LDS_IDX_ACTIVE') / cu:6.1%}  "
+                f"bank-confl {f('SQ_LDS_BANK_CONFLICT') / max(1.0, f('SQ_LDS_IDX_ACTIVE')):6.1%}  "
+                f"wait-LDS {f('SQ_WAIT_INST_LDS') / wave:6.1%}  wait-any {f('SQ_WAIT_ANY') / wave:6.1%}  "
+                f"wait-inst {f('SQ_WAIT_INST_ANY') / wave:6.1%}  MFMA/VALU insts "
+                f"{f('SQ_INSTS_MFMA') / max(1.0, f('SQ_INSTS_VALU')):.3f}")
+    base = f"python -u bench.py --steps 2 --warmup 1 --cpu-seconds 0 --no-kernel-events --no-graph{extra}"
+    cmds = [f"timeout -s KILL 120 rocprofv3 --pmc {SQ_PASSES[i]} -f csv -d gpurun_out/pmc_sq{i} -o pmc -- {base}"
+            for i in range(2)]
+    cmds.append(f"python bench.py --summarize-sq gpurun_out/pmc_sq0 gpurun_out/pmc_sq1{extra}")
+    out = [f"# SQ counters: {workload}", "",
+           "Commands (two counter passes, each its own run, then the summary; from the repository root):", "",
+           "```", *cmds, "```", "",
+           "Per dispatch, averaged over each kernel's dispatches. GRBM/xcd = GRBM_GUI_ACTIVE per XCD (the counter "
+           "sums the 8 XCDs); SIMD cycles = GRBM/xcd x 1024 SIMDs, CU cycles = GRBM/xcd x 256.",
+           "MFMA-busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD cycles; VALU-active = 4 x SQ_ACTIVE_INST_VALU (quad-cycles) "
+           "/ SIMD cycles; coexec = SQ_VALU_MFMA_COEXEC_CYCLES / SIMD cycles; LDS-active = SQ_LDS_IDX_ACTIVE / CU "
+           "cycles; bank-confl = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; wait-LDS, wait-any, wait-inst = "
+           "SQ_WAIT_INST_LDS, SQ_WAIT_ANY, SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES.", "",
+           "```", *lines, "```"]
+    path = os.path.join(PROFILES, f"sq_counters_{workload}.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def cpu_model() -> str:
-    """The host CPU's model name (as lscpu reports it), read from /proc/cpuinfo."""
+    """The host CPU as lscpu names it: model name, family and model numbers, from /proc/cpuinfo
+    (a virtual machine may report a short model name; the numbers still identify the part)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    key, val = (x.strip() for x in line.split(":", 1))
+                    info.setdefault(key, val)
+                if not line.strip() and info:
+                    break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    return f"{name} (family {info.get('cpu family', '?')}, model {info.get('model', '?')}, " \
+           f"stepping {info.get('stepping', '?')})"
 
 
 def cpu_baseline(w, budget_s):
@@ -362,7 +559,19 @@ def main():
     if args.summarize_pmc:
         import synth
 
-        summarize_pmc(*args.summarize_pmc, synth.WORKLOADS[args.workload].name)
+        extra = (f" --workload {args.workload}" if args.workload != 4 else "") + \
+            (" --rope" if args.rope else "") + (" --ve" if args.ve else "")
+        summarize_pmc(*args.summarize_pmc, synth.WORKLOADS[args.workload].name + variant_tag(args), extra)
+        return
+    if args.summarize_sq:
+        import synth
+
+        extra = (f" --workload {args.workload}" if args.workload != 4 else "") + \
+            (" --rope" if args.rope else "") + (" --ve" if args.ve else "")
+        summarize_sq(*args.summarize_sq, synth.WORKLOADS[args.workload].name + variant_tag(args), extra)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
@@ -420,19 +629,22 @@ def main():
     use_ev = not args.no_kernel_events
     # one event pair per launch of each main kernel in the timed region
     n_ev = args.steps * w.n_layer
-    kinds = ("fwd", "bwd_dq", "bwd_dkdv")
-    hook = {"fwd": sa.SA_KERNEL_FWD, "bwd_dq": sa.SA_KERNEL_BWD_DQ, "bwd_dkdv": sa.SA_KERNEL_BWD_DKDV}
+    kinds = MFMA_KINDS + HBM_KINDS
+    hook = {"fwd": sa.SA_KERNEL_FWD, "bwd_dq": sa.SA_KERNEL_BWD_DQ, "bwd_dkdv": sa.SA_KERNEL_BWD_DKDV,
+            "kv_prep": sa.SA_KERNEL_KV_PREP, "bwd_knorm": sa.SA_KERNEL_BWD_KNORM}
     ev = {k: [(hip.event(), hip.event()) for _ in range(n_ev)] if use_ev else [] for k in kinds}
 
     def step(s=None):
         for li, L in enumerate(layers):
             if s is not None and use_ev:
                 sa.sa_set_timing_events(hook["fwd"], *ev["fwd"][s * w.n_layer + li])
+                sa.sa_set_timing_events(hook["kv_prep"], *ev["kv_prep"][s * w.n_layer + li])
             fwd(L)
         for li in reversed(range(w.n_layer)):
             if s is not None and use_ev:
                 sa.sa_set_timing_events(hook["bwd_dq"], *ev["bwd_dq"][s * w.n_layer + li])
                 sa.sa_set_timing_events(hook["bwd_dkdv"], *ev["bwd_dkdv"][s * w.n_layer + li])
+                sa.sa_set_timing_events(hook["bwd_knorm"], *ev["bwd_knorm"][s * w.n_layer + li])
             bwd(layers[li])
         if use_ev:
             for k in kinds:
@@ -496,19 +708,28 @@ def main():
         # backward's duplicated S and dP earn nothing there.
         per_pair = {"fwd": 4.0, "bwd_dq": 6.0, "bwd_dkdv": 8.0}
         ms = {k: sum(hip.elapsed_ms(a, b) for a, b in ev[k]) / args.steps for k in kinds}
-        for k in kinds:
+        for k in MFMA_KINDS:
             kern[f"{k}_ms_per_step"] = ms[k]
             kern[f"{k}_tflops"] = per_pair[k] * w.D * sum(pairs) / (ms[k] * 1e-3) / 1e12
+        ve_set = set(sa.ve_layers(w.n_layer)) if args.ve else set()
+        for k in HBM_KINDS:
+            # bytes per launch averaged over the layers (value-embedding layers read more)
+            nbytes = sum(hbm_bytes_per_launch(k, w, k == "kv_prep" and li in ve_set)
+                         for li in range(w.n_layer)) / w.n_layer
+            kern[f"{k}_ms_per_step"] = ms[k]
+            kern[f"{k}_algorithmic_bytes"] = nbytes
+            kern[f"{k}_gbs"] = nbytes * w.n_layer / (ms[k] * 1e-3) / 1e9
+            kern[f"{k}_traffic"] = traffic_bytes(w.name + variant_tag(args), *KERNELS[k])
         kern["ms_per_step_with_events"] = ms_step_events
         kern["other_ms_per_step"] = ms_step_events - sum(ms.values())
-        dom = max(kinds, key=lambda k: ms[k])
+        dom = max(MFMA_KINDS, key=lambda k: ms[k])
         flop_launch = per_pair[dom] * w.D * sum(pairs) / w.n_layer
         avg_ms = ms[dom] / w.n_layer
         achieved = flop_launch / (avg_ms * 1e-3) / 1e12
         name, files = KERNELS[dom]
         roofline = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                    "traffic": traffic_bytes(w.name, name, files),
+                    "traffic": traffic_bytes(w.name + variant_tag(args), name, files),
                     "avg_launch_ms": avg_ms, "algorithmic_flop_per_launch": flop_launch,
                     "flop_per_visible_pair": f"{per_pair[dom]:g} D"}
         for k in kinds:

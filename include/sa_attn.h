@@ -276,16 +276,22 @@ sa_status sa_polar_express(const void* g, void* out, void* workspace, size_t wor
                            int batch, int rows, int cols, int steps, float eps, void* stream);
 
 /* Kernels that sa_set_timing_events can bracket. */
-enum { SA_KERNEL_FWD = 0, SA_KERNEL_BWD_DQ = 1, SA_KERNEL_BWD_DKDV = 2 };
+enum {
+  SA_KERNEL_FWD = 0,       /* attention kernel of sa_attn_fwd */
+  SA_KERNEL_BWD_DQ = 1,    /* dQ kernel of sa_attn_bwd */
+  SA_KERNEL_BWD_DKDV = 2,  /* dK/dV kernel of sa_attn_bwd */
+  SA_KERNEL_KV_PREP = 3,   /* key-norm / value-transpose pass of sa_attn_fwd (QK-norm, bounded logits) */
+  SA_KERNEL_BWD_KNORM = 4  /* key-norm pass of sa_attn_bwd (QK-norm) */
+};
 
 /*
  * sa_set_timing_events - benchmarking hook (not part of the computation).
- *   While set, every later sa_attn_fwd (kernel = SA_KERNEL_FWD) or
- *   sa_attn_bwd (kernel = SA_KERNEL_BWD_DQ for its dQ kernel,
- *   SA_KERNEL_BWD_DKDV for its dK/dV kernel) call made FROM THE CALLING HOST
- *   THREAD records `start` on its stream right before that kernel and `stop`
- *   right after it, so hipEventElapsedTime(start, stop) is the kernel's own
- *   duration. start/stop are hipEvent_t handles
+ *   While set, every later sa_attn_fwd / sa_attn_bwd call (and their _ex
+ *   and _noalloc forms) made FROM THE CALLING HOST THREAD that runs the
+ *   kernel named by `kernel` (one of the SA_KERNEL_ ids above) attaches
+ *   `start` and `stop` to that kernel's own dispatch on its stream
+ *   (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is the
+ *   kernel's duration, without the gaps of separate event packets. start/stop are hipEvent_t handles
  *   passed as void*, created and owned by the caller; pass NULL, NULL to clear.
  *   Returns SA_ERR_SHAPE for an unknown kernel id, SA_ERR_NULL if exactly one
  *   of start/stop is NULL.

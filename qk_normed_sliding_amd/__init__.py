@@ -31,10 +31,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa_attn.so")
 
 SA_OK = 0
-ABI_VERSION = 5
+ABI_VERSION = 6
 SA_KERNEL_FWD = 0
 SA_KERNEL_BWD_DQ = 1
 SA_KERNEL_BWD_DKDV = 2
+SA_KERNEL_KV_PREP = 3
+SA_KERNEL_BWD_KNORM = 4
 
 
 class SAError(RuntimeError):
@@ -430,8 +432,9 @@ def sa_polar_express(g, out=None, steps=5, eps=1e-7, workspace=None, stream=None
 
 
 def sa_set_timing_events(kernel, start_event, stop_event):
-    """Benchmarking hook: record raw hipEvent_t handles (ints, or None to clear)
-    around the main kernel of later calls from this thread."""
+    """Benchmarking hook: attach raw hipEvent_t handles (ints, or None to clear)
+    to the dispatch of kernel `kernel` (an SA_KERNEL_ id) in later calls from
+    this thread."""
     _check("sa_set_timing_events", _lib.sa_set_timing_events(
         int(kernel), ctypes.c_void_p(start_event) if start_event else None,
         ctypes.c_void_p(stop_event) if stop_event else None))

@@ -16,11 +16,11 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
-// Benchmarking hook: events recorded around the main kernel of later calls
-// made from this host thread (see sa_set_timing_events).
-thread_local sa::TimingEvents tl_events[3];
+// Benchmarking hook: events recorded around a kernel of later calls made
+// from this host thread (see sa_set_timing_events).
+thread_local sa::TimingEvents tl_events[5];
 // Testing hook: cap on the workgroups of a persistent launch (0 = none).
 thread_local int tl_max_wg = 0;
 
@@ -180,7 +180,7 @@ SA_API sa_status sa_qknorm(const void* x, void* y, float* rstd, int64_t rows, in
   if (!aligned16(x) || !aligned16(y) || (rstd != nullptr && !aligned4(rstd))) return SA_ERR_ALIGN;
   if (rows > (int64_t)1 << 56) return SA_ERR_SHAPE;
   sa::NormParams p{x, y, rstd, rows, eps};
-  return sa::launch_qknorm(p, head_dim, (hipStream_t)stream) == hipSuccess ? SA_OK : SA_ERR_HIP;
+  return sa::launch_qknorm(p, head_dim, (hipStream_t)stream, sa::TimingEvents{}) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
 SA_API size_t sa_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
@@ -241,7 +241,7 @@ static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, 
     p.vt = (char*)workspace + round256((size_t)B * T * Hkv * head_dim * 2);
     p.rope = rope;
     sa::KvPrepParams kp{k, v, (void*)p.khat, (void*)p.vt, B, T, Hkv, p.Tp, eps, rope, ve, ve_bytes};
-    if (sa::launch_kv_prep(kp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+    if (sa::launch_kv_prep(kp, head_dim, s, tl_events[SA_KERNEL_KV_PREP]) != hipSuccess) return SA_ERR_HIP;
     return sa::launch_fwd_pp(p, head_dim, s, tl_events[SA_KERNEL_FWD]) == hipSuccess ? SA_OK : SA_ERR_HIP;
   }
   // online-softmax kernel (logits without the QK-norm bound); no rotary tables or value embeddings there
@@ -330,7 +330,7 @@ static sa_status attn_bwd(const void* q, const void* k, const void* v, const voi
     void* khat = (char*)workspace + round256(rows * head_dim * 2) + round256(rows * sizeof(float));
     float* rstd_k = (float*)((char*)khat + round256((size_t)B * T * Hkv * head_dim * 2));
     sa::NormParams np{k, khat, rstd_k, (int64_t)B * T * Hkv, eps, rope, Hkv, T};
-    if (sa::launch_qknorm(np, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+    if (sa::launch_qknorm(np, head_dim, s, tl_events[SA_KERNEL_BWD_KNORM]) != hipSuccess) return SA_ERR_HIP;
     p.khat = khat;
     p.rstd_k = rstd_k;
   }
@@ -558,7 +558,7 @@ SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, siz
 }
 
 SA_API sa_status sa_set_timing_events(int kernel, void* start, void* stop) {
-  if (kernel != SA_KERNEL_FWD && kernel != SA_KERNEL_BWD_DQ && kernel != SA_KERNEL_BWD_DKDV) return SA_ERR_SHAPE;
+  if (kernel < SA_KERNEL_FWD || kernel > SA_KERNEL_BWD_KNORM) return SA_ERR_SHAPE;
   if ((start == nullptr) != (stop == nullptr)) return SA_ERR_NULL;
   tl_events[kernel].start = (hipEvent_t)start;
   tl_events[kernel].stop = (hipEvent_t)stop;

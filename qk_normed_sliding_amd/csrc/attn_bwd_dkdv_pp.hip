@@ -462,25 +462,19 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
 
 hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
   const dim3 grid((unsigned)min(p.nkb * p.B * p.Hkv, p.nwg));
-  if (ev.start != nullptr) {
-    const hipError_t e = hipEventRecord(ev.start, stream);
-    if (e != hipSuccess) return e;
-  }
   const bool rope = p.rope.cos != nullptr;
   if (head_dim == 128) {
     if (rope)
-      hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128, true>), grid, dim3(512), 0, stream, p);
+      hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128, false>), grid, dim3(512), 0, stream, p);
+      hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
   } else {
     if (rope)
-      hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64, true>), grid, dim3(512), 0, stream, p);
+      hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64, false>), grid, dim3(512), 0, stream, p);
+      hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
   }
-  const hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
-  return e;
+  return hipGetLastError();
 }
 
 }  // namespace sa

@@ -476,17 +476,11 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
 
 hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
   const dim3 grid((unsigned)(p.nqb * p.B * p.Hkv * p.nsub));
-  if (ev.start != nullptr) {
-    const hipError_t e = hipEventRecord(ev.start, stream);
-    if (e != hipSuccess) return e;
-  }
   if (head_dim == 128)
-    hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<128>), grid, dim3(512), 0, stream, p);
+    hipExtLaunchKernelGGL((attn_bwd_dq_pp_kernel<128>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
   else
-    hipLaunchKernelGGL((attn_bwd_dq_pp_kernel<64>), grid, dim3(512), 0, stream, p);
-  const hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
-  return e;
+    hipExtLaunchKernelGGL((attn_bwd_dq_pp_kernel<64>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+  return hipGetLastError();
 }
 
 }  // namespace sa

@@ -340,19 +340,13 @@ static hipError_t launch_fwd_d(const FwdParams& p, bool qk_norm, bool fixed_max,
   constexpr int BN = 64;
   const dim3 grid((unsigned)(p.nqb * p.B * p.Hkv * p.nsub));
   const dim3 block(HPW * 4 * 64);
-  if (ev.start != nullptr) {
-    const hipError_t e = hipEventRecord(ev.start, stream);
-    if (e != hipSuccess) return e;
-  }
   if (qk_norm && fixed_max)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, BN, true, true>), grid, block, 0, stream, p);
+    hipExtLaunchKernelGGL((attn_fwd_kernel<D, HPW, BN, true, true>), grid, block, 0, stream, ev.start, ev.stop, 0, p);
   else if (qk_norm)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, BN, true, false>), grid, block, 0, stream, p);
+    hipExtLaunchKernelGGL((attn_fwd_kernel<D, HPW, BN, true, false>), grid, block, 0, stream, ev.start, ev.stop, 0, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, HPW, BN, false, false>), grid, block, 0, stream, p);
-  const hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
-  return e;
+    hipExtLaunchKernelGGL((attn_fwd_kernel<D, HPW, BN, false, false>), grid, block, 0, stream, ev.start, ev.stop, 0, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int heads_per_wg, bool qk_norm, bool fixed_max,

@@ -492,25 +492,19 @@ hipError_t launch_fwd_pp(const FwdParams& p, int head_dim, hipStream_t stream, c
   constexpr int NB = 3;
   const int n_items = p.nqb * p.B * p.Hkv * p.nsub;
   const dim3 grid((unsigned)min(n_items, p.nwg));
-  if (ev.start != nullptr) {
-    const hipError_t e = hipEventRecord(ev.start, stream);
-    if (e != hipSuccess) return e;
-  }
   const bool rope = p.rope.cos != nullptr;
   if (head_dim == 128) {
     if (rope)
-      hipLaunchKernelGGL((attn_fwd_pp_kernel<128, NB, true>), grid, dim3(512), 0, stream, p);
+      hipExtLaunchKernelGGL((attn_fwd_pp_kernel<128, NB, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
     else
-      hipLaunchKernelGGL((attn_fwd_pp_kernel<128, NB, false>), grid, dim3(512), 0, stream, p);
+      hipExtLaunchKernelGGL((attn_fwd_pp_kernel<128, NB, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
   } else {
     if (rope)
-      hipLaunchKernelGGL((attn_fwd_pp_kernel<64, NB, true>), grid, dim3(512), 0, stream, p);
+      hipExtLaunchKernelGGL((attn_fwd_pp_kernel<64, NB, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
     else
-      hipLaunchKernelGGL((attn_fwd_pp_kernel<64, NB, false>), grid, dim3(512), 0, stream, p);
+      hipExtLaunchKernelGGL((attn_fwd_pp_kernel<64, NB, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
   }
-  const hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev.stop != nullptr) return hipEventRecord(ev.stop, stream);
-  return e;
+  return hipGetLastError();
 }
 
 }  // namespace sa

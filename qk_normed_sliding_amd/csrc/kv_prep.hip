@@ -101,12 +101,12 @@ __global__ void __launch_bounds__(256) kv_prep_kernel(KvPrepParams p) {
   }
 }
 
-hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
   const dim3 grid((unsigned)(p.Tp / 64), (unsigned)(p.B * p.Hkv));
   if (head_dim == 128)
-    hipLaunchKernelGGL((kv_prep_kernel<128>), grid, dim3(256), 0, stream, p);
+    hipExtLaunchKernelGGL((kv_prep_kernel<128>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, p);
   else
-    hipLaunchKernelGGL((kv_prep_kernel<64>), grid, dim3(256), 0, stream, p);
+    hipExtLaunchKernelGGL((kv_prep_kernel<64>), grid, dim3(256), 0, stream, ev.start, ev.stop, 0, p);
   return hipGetLastError();
 }
 

@@ -38,14 +38,14 @@ __global__ void __launch_bounds__(256) qknorm_kernel(NormParams p) {
   }
 }
 
-hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream) {
+hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
   const int rpb = 256 / (head_dim / 8);
   const long nblk = (p.rows + rpb - 1) / rpb;
   const unsigned grid = (unsigned)(nblk < 16384L ? nblk : 16384L);
   if (head_dim == 128)
-    hipLaunchKernelGGL((qknorm_kernel<128>), dim3(grid), dim3(256), 0, stream, p);
+    hipExtLaunchKernelGGL((qknorm_kernel<128>), dim3(grid), dim3(256), 0, stream, ev.start, ev.stop, 0, p);
   else
-    hipLaunchKernelGGL((qknorm_kernel<64>), dim3(grid), dim3(256), 0, stream, p);
+    hipExtLaunchKernelGGL((qknorm_kernel<64>), dim3(grid), dim3(256), 0, stream, ev.start, ev.stop, 0, p);
   return hipGetLastError();
 }
 

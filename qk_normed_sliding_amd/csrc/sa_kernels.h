@@ -1,6 +1,7 @@
 // Kernel parameter blocks and host-side launchers (internal to libsa_attn.so).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -148,7 +149,8 @@ __host__ __device__ inline int gemm_tiles(int M, int N, int sym) {
 }
 constexpr int kFroChunks = 64;  // partial sums per matrix of the Frobenius norm
 
-// Optional events recorded around a call's main kernel (benchmarking hook).
+// Optional events of a kernel launch (benchmarking hook), attached to the kernel's own
+// dispatch (hipExtLaunchKernelGGL), so their elapsed time is the kernel's duration.
 struct TimingEvents {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
@@ -164,7 +166,7 @@ hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream
 // dK/dV kernel whose two warp groups (per-key state split by role) alternate on the matrix cores
 // (any query-heads-per-KV-head ratio).
 hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
-hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
 // Polar-express pieces: GEMM (b_kn: B given as [K][N]), partial sums of
 // squares for ||X||_F per matrix (part: batch * kFroChunks floats), and
 // per-matrix transpose [R][C] -> [C][R].
@@ -174,6 +176,6 @@ hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, 
 // Value-embedding gate: v' and g for the backward; then dve, dx32 and dw from dL/dv'.
 hipError_t launch_ve_prep(const VePrepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_ve_bwd(const VeBwdParams& p, int head_dim, hipStream_t stream);
-hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
 
 }  // namespace sa

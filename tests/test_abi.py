@@ -159,13 +159,14 @@ def test_workspace_size(sa):
 def test_timing_hook_validation(sa):
     lib = sa.library()
     P = ctypes.c_void_p
-    assert lib.sa_set_timing_events(3, None, None) == SA_ERR_SHAPE
+    assert lib.sa_set_timing_events(5, None, None) == SA_ERR_SHAPE
     assert lib.sa_set_timing_events(-1, None, None) == SA_ERR_SHAPE
     assert lib.sa_set_timing_events(0, P(16), None) == SA_ERR_NULL
     assert lib.sa_set_max_workgroups(-1) == SA_ERR_SHAPE
     assert lib.sa_set_max_workgroups(3) == SA_OK
     assert lib.sa_set_max_workgroups(0) == SA_OK
-    for k in range(3):
+    for k in (sa.SA_KERNEL_FWD, sa.SA_KERNEL_BWD_DQ, sa.SA_KERNEL_BWD_DKDV, sa.SA_KERNEL_KV_PREP,
+              sa.SA_KERNEL_BWD_KNORM):
         assert lib.sa_set_timing_events(k, None, None) == SA_OK
 
 

@@ -453,3 +453,53 @@ def test_graph_replay_matches_eager(sa):
         o2, lse2 = sa.sa_attn_fwd(q2, k2, v2, window=W, softmax_scale=scale, workspace=wsf)
         sa.sa_attn_bwd(q2, k2, v2, o2, lse2, do2, window=W, softmax_scale=scale, workspace=wsb)
         torch.cuda.synchronize()
+
+
+def test_timing_events_bracket_each_kernel(sa):
+    """With benchmarking events attached to all five kernels of a forward and
+    backward call, each event pair records a positive duration no longer than
+    the whole call, and the results equal those of the same call without
+    events (the events are attached to the kernel dispatches and change
+    nothing they compute)."""
+    import ctypes
+
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    B, T, Hq, Hkv, D, W = 2, 700, 6, 3, 128, 255
+    scale = D ** -0.5
+    log("[timing events]")
+    q, k, v, do = (x.cuda() for x in synth.small_case(B, T, Hq, Hkv, D, seed=813))
+    ids = (sa.SA_KERNEL_FWD, sa.SA_KERNEL_KV_PREP, sa.SA_KERNEL_BWD_DQ, sa.SA_KERNEL_BWD_DKDV, sa.SA_KERNEL_BWD_KNORM)
+    evs = {}
+    for i in ids:
+        pair = [ctypes.c_void_p(), ctypes.c_void_p()]
+        for h in pair:
+            assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        evs[i] = (pair[0].value, pair[1].value)
+    ref_o, ref_lse = sa.sa_attn_fwd(q, k, v, window=W, softmax_scale=scale)
+    ref = (ref_o, ref_lse) + tuple(sa.sa_attn_bwd(q, k, v, ref_o, ref_lse, do, window=W, softmax_scale=scale))
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    try:
+        for i in ids:
+            sa.sa_set_timing_events(i, *evs[i])
+        t0.record()
+        o, lse = sa.sa_attn_fwd(q, k, v, window=W, softmax_scale=scale)
+        got = (o, lse) + tuple(sa.sa_attn_bwd(q, k, v, o, lse, do, window=W, softmax_scale=scale))
+        t1.record()
+    finally:
+        for i in ids:
+            sa.sa_set_timing_events(i, None, None)
+    torch.cuda.synchronize()
+    whole = t0.elapsed_time(t1)
+    for i in ids:
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[i][0]), ctypes.c_void_p(evs[i][1])) == 0
+        log(f"  kernel {i}: {ms.value * 1e3:.1f} us (call {whole * 1e3:.1f} us)")
+        assert 0.0 < ms.value <= whole
+        for h in evs[i]:
+            hip.hipEventDestroy(ctypes.c_void_p(h))
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, ref):
+        assert torch.equal(a, b), name
