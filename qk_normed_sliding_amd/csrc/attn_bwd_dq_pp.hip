@@ -251,13 +251,11 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
     }
   };
 
-  // ---- prologue loads: K tiles 0..2 by group 1, V tiles 0..1 by group 0
-  if (grp == 1) {
-    for (int tau = 0; tau < 3 && tau < ntile; ++tau) issue_k(tau);
-  } else {
-    for (int tau = 0; tau < 2 && tau < ntile; ++tau) issue_v(tau);
-  }
-  // the rows of this wave (in flight together with the tiles)
+  // ---- prologue loads: this wave's rows first, then the first tiles (K
+  // tiles 0..2 by group 1, V tiles 0..1 by group 0). Vector memory
+  // operations retire in issue order, so the rows, issued first, can be
+  // processed while the tiles are still arriving.
+  const long lrow = ((long)b * p.Hq + head) * T + row;
   {
     const long first = ((long)b * T * p.Hq + head) * D;
     const uint32_t bytes = (uint32_t)T * qstride * 2;
@@ -272,6 +270,11 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
       xq[m] = bload16(rq, off);
       xd[m] = bload16(rd, off);
       xo[m] = bload16(ro, off);
+    }
+    if (grp == 1) {
+      for (int tau = 0; tau < 3 && tau < ntile; ++tau) issue_k(tau);
+    } else {
+      for (int tau = 0; tau < 2 && tau < ntile; ++tau) issue_v(tau);
     }
     // rotary table entries of the lane's rows and dimensions, in flight with the rows
     const bool rope = p.rope.cos != nullptr;
@@ -328,6 +331,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
         scal[32 + r] = dd;
       }
     }
+    const float lse_raw = row < T ? p.lse[lrow] : 0.f;  // (its latency overlaps the staging below)
     // lane = row reads (the same wave wrote them; LDS keeps a wave's order)
     const uint32_t rbase = stage + (uint32_t)(l32 * D * 2);
 #pragma unroll
@@ -343,8 +347,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk)
       df[kk] = *(SA_LDS const bf16x8*)(uintptr_t)(rbase + (uint32_t)((((2 * kk + half) ^ (l32 % CPR))) << 4));
-    const long lrow = ((long)b * p.Hq + head) * T + row;
-    lse2 = row < T ? p.lse[lrow] * kLog2e : INFINITY;
+    lse2 = row < T ? lse_raw * kLog2e : INFINITY;
     if (half == 0 && row < T) p.delta[lrow] = delta;
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -400,14 +403,15 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   // lane-pair swap per dword of (low quad, high quad) delivers, in the low
   // quad register, the elements for c = 0 and in the high quad register those
   // for c = 1, in both lane halves.
-  if (!wave_active || row >= T) return;
-  const long rowoff = ((long)b * T + row) * qstride + (long)head * D + 4 * half;
+  // Lanes of rows past T compute on zero accumulators (their probabilities
+  // were zero) and are not stored; they stay for the staged stores below.
+  if (!wave_active) return;
   // rotary table entries of the row, loaded first (head_dim d < D/2 in block
   // db < NDB/2 pairs with d + D/2 in block db + NDB/2)
   const bool rope = p.rope.cos != nullptr;
   f32x4 tc[NDB / 2][4], ts[NDB / 2][4];
   if (rope) {
-    const long tr = (long)row * p.rope.stride + 4 * half;
+    const long tr = (long)min(row, T - 1) * p.rope.stride + 4 * half;
 #pragma unroll
     for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
@@ -463,6 +467,16 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
         }
       }
   }
+  // The wave's 32 rows go through its staging area (free again: every M-phase
+  // ended before the last barrier), row r's 16-byte chunk j at chunk
+  // j ^ (r mod CPR) as in the prologue, and leave as whole rows: each store
+  // instruction writes QRPI rows of D contiguous values. (The lane index is
+  // made opaque so that these addresses are computed here, not kept in
+  // registers from the prologue's equal ones.)
+  int el = lane;
+  asm volatile("" : "+v"(el));
+  const int el32 = el & 31;
+  const uint32_t wbase = stage + (uint32_t)(el32 * D * 2 + 8 * (el >> 5));
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -470,8 +484,17 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
       u32x2 w;
       w[0] = pack2(dq[db][4 * i], dq[db][4 * i + 1]);
       w[1] = pack2(dq[db][4 * i + 2], dq[db][4 * i + 3]);
-      *(u32x2*)((bf16*)p.dq + rowoff + 32 * db + 8 * i) = w;
+      const int c = 4 * db + i;  // 16-byte chunk of head_dim 32db + 8i
+      *(SA_LDS u32x2*)(uintptr_t)(wbase + (uint32_t)((c ^ (el32 % CPR)) << 4)) = w;
     }
+  const int crow = el / CPR, cch = el % CPR;
+  const long first = ((long)b * T * p.Hq + head) * D;
+#pragma unroll
+  for (int m = 0; m < QM; ++m) {
+    const int r = QRPI * m + crow;  // row within the wave's 32
+    const u32x4 w = *(SA_LDS const u32x4*)(uintptr_t)(stage + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4)));
+    if (r0 + r < T) st16((bf16*)p.dq + first + (long)(r0 + r) * qstride + 8 * cch, w);
+  }
 }
 
 hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
