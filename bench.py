@@ -3,8 +3,10 @@
 
 One step = the whole hot path over one batch: the forward of all 8 layers
 (sa_attn_fwd, each layer on its own seeded inputs) followed by the backward of
-all 8 layers in reverse order (sa_attn_bwd). Inputs, outputs and the backward
-workspace are resident in HBM before the timed region starts.
+all 8 layers in reverse order (sa_attn_bwd_ex, which reads the normed k rows
+back from the workspace its layer's forward kept, as a trainer keeps a
+layer's saved tensors). Inputs, outputs and workspaces are resident in HBM
+before the timed region starts.
 
 Work is counted on the band only: a (query, key) pair is counted when key j is
 visible to query i (0 <= i - j <= W, or j <= i for a full causal layer), at
@@ -48,12 +50,12 @@ KERNELS = {
     "fwd": ("attn_fwd_pp_kernel", ("attn_fwd_pp.hip", "sa_common.h")),
     "bwd_dq": ("attn_bwd_dq_pp_kernel", ("attn_bwd_dq_pp.hip", "sa_common.h")),
     "bwd_dkdv": ("attn_bwd_dkdv_pp_kernel", ("attn_bwd_dkdv_pp.hip", "sa_common.h")),
-    "kv_prep": ("kv_prep_kernel", ("kv_prep.hip", "sa_common.h", "ve_common.h")),
-    "bwd_knorm": ("qknorm_kernel", ("qknorm.hip", "sa_common.h")),
+    "knorm": ("qknorm_kernel", ("qknorm.hip", "sa_common.h")),
 }
-# the MFMA-bound attention kernels and the HBM-bound passes that prepare their key/value rows
+# the MFMA-bound attention kernels and the HBM-bound pass that norms the key rows (the
+# forward's; the backward reads its output back from the forward's workspace)
 MFMA_KINDS = ("fwd", "bwd_dq", "bwd_dkdv")
-HBM_KINDS = ("kv_prep", "bwd_knorm")
+HBM_KINDS = ("knorm",)
 
 
 def source_hash(files) -> str:
@@ -187,6 +189,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the headline pass's steps one call at a time instead of replaying a captured "
                          "HIP graph of the step")
+    ap.add_argument("--recompute-k", action="store_true",
+                    help="run each backward without the forward's workspace (it norms the k rows again) instead "
+                         "of reading back the normed rows the layer's forward kept")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="do not bracket the main kernels with HIP events")
     ap.add_argument("--copy-probe", action="store_true",
@@ -231,20 +236,12 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(h))
 
 
-def hbm_bytes_per_launch(kind, w, ve_layer=False):
+def hbm_bytes_per_launch(kind, w):
     """Algorithmic HBM bytes of one launch of an HBM-bound pass: every element it must read,
-    read once, and every element it must write, written once (bf16 rows, fp32 1/rms).
-    kv_prep reads k and v and writes k_hat and the key-padded transposed v; with value
-    embeddings it also reads the gate's 32 input channels, the token id and the table rows.
-    The backward's k-norm pass reads k and writes k_hat and 1/rms per row."""
+    read once, and every element it must write, written once. The k-norm pass reads the bf16
+    k rows and writes the bf16 normed rows and an fp32 1/rms per row."""
     rows = w.B * w.T * w.Hkv
-    tp = (w.T + 63) // 64 * 64
-    if kind == "kv_prep":
-        b = 2 * rows * w.D * 2 + rows * w.D * 2 + w.B * w.Hkv * w.D * tp * 2
-        if ve_layer:
-            b += w.B * w.T * (32 * 2 + 4) + rows * w.D * 2
-        return b
-    if kind == "bwd_knorm":
+    if kind == "knorm":
         return rows * w.D * 2 * 2 + rows * 4
     raise ValueError(kind)
 
@@ -597,12 +594,15 @@ def main():
         if args.ve and layer in sa.ve_layers(w.n_layer):
             ve = tuple(t.to(dev) for t in synth.ve_inputs(w, layer))
         print(f"inputs of layer {layer} resident", file=sys.stderr, flush=True)
+        # each layer keeps its forward's workspace (normed k rows and their 1/rms; v' and the
+        # gate on gated layers) for its backward, as a trainer keeps a layer's saved tensors
         layers.append(dict(
             W=w.windows[layer], q=q, k=k, v=v, do=do,
             o=torch.empty_like(q), lse=torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev),
-            dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), ve=ve))
+            dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), ve=ve,
+            wsf=torch.empty(sa.sa_attn_fwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8,
+                            device=dev)))
     ws = torch.empty(sa.sa_attn_bwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(sa.sa_attn_fwd_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D), dtype=torch.uint8, device=dev)
     rope = sa.rope_tables(10 * w.T, w.D, device=dev) if args.rope else None
     ws_ve = (torch.empty(sa.sa_attn_ve_workspace_bytes(w.B, w.T, w.Hkv, w.D), dtype=torch.uint8, device=dev)
              if args.ve else None)
@@ -611,40 +611,40 @@ def main():
     def fwd(L):
         if L["ve"] is not None:
             sa.sa_attn_fwd_ex(L["q"], L["k"], L["v"], window=L["W"], softmax_scale=w.scale, eps=w.eps, o=L["o"],
-                              lse=L["lse"], workspace=ws_f, rope=rope, ve=L["ve"])
+                              lse=L["lse"], workspace=L["wsf"], rope=rope, ve=L["ve"])
             return
         sa.sa_attn_fwd(L["q"], L["k"], L["v"], window=L["W"], softmax_scale=w.scale, eps=w.eps, o=L["o"], lse=L["lse"],
-                       workspace=ws_f, rope=rope)
+                       workspace=L["wsf"], rope=rope)
 
     def bwd(L):
-        if L["ve"] is not None:
-            sa.sa_attn_bwd_ex(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=L["W"], softmax_scale=w.scale,
-                              eps=w.eps, dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=ws, rope=rope, ve=L["ve"],
-                              ve_workspace=ws_ve)
-            return
-        sa.sa_attn_bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=L["W"], softmax_scale=w.scale,
-                       eps=w.eps, dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=ws, rope=rope)
+        sa.sa_attn_bwd_ex(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=L["W"], softmax_scale=w.scale,
+                          eps=w.eps, dq=L["dq"], dk=L["dk"], dv=L["dv"], workspace=ws, rope=rope, ve=L["ve"],
+                          ve_workspace=ws_ve if L["ve"] is not None else None,
+                          fwd_workspace=None if args.recompute_k else L["wsf"])
 
     hip = Hip()
     use_ev = not args.no_kernel_events
     # one event pair per launch of each main kernel in the timed region
     n_ev = args.steps * w.n_layer
-    kinds = MFMA_KINDS + HBM_KINDS
+    # (with --recompute-k the backward's own k-norm pass too: the same kernel)
+    hbm_kinds = HBM_KINDS + (("bwd_knorm",) if args.recompute_k else ())
+    kinds = MFMA_KINDS + hbm_kinds
     hook = {"fwd": sa.SA_KERNEL_FWD, "bwd_dq": sa.SA_KERNEL_BWD_DQ, "bwd_dkdv": sa.SA_KERNEL_BWD_DKDV,
-            "kv_prep": sa.SA_KERNEL_KV_PREP, "bwd_knorm": sa.SA_KERNEL_BWD_KNORM}
+            "knorm": sa.SA_KERNEL_FWD_KNORM, "bwd_knorm": sa.SA_KERNEL_BWD_KNORM}
     ev = {k: [(hip.event(), hip.event()) for _ in range(n_ev)] if use_ev else [] for k in kinds}
 
     def step(s=None):
         for li, L in enumerate(layers):
             if s is not None and use_ev:
                 sa.sa_set_timing_events(hook["fwd"], *ev["fwd"][s * w.n_layer + li])
-                sa.sa_set_timing_events(hook["kv_prep"], *ev["kv_prep"][s * w.n_layer + li])
+                sa.sa_set_timing_events(hook["knorm"], *ev["knorm"][s * w.n_layer + li])
             fwd(L)
         for li in reversed(range(w.n_layer)):
             if s is not None and use_ev:
                 sa.sa_set_timing_events(hook["bwd_dq"], *ev["bwd_dq"][s * w.n_layer + li])
                 sa.sa_set_timing_events(hook["bwd_dkdv"], *ev["bwd_dkdv"][s * w.n_layer + li])
-                sa.sa_set_timing_events(hook["bwd_knorm"], *ev["bwd_knorm"][s * w.n_layer + li])
+                if args.recompute_k:
+                    sa.sa_set_timing_events(hook["bwd_knorm"], *ev["bwd_knorm"][s * w.n_layer + li])
             bwd(layers[li])
         if use_ev:
             for k in kinds:
@@ -711,15 +711,12 @@ def main():
         for k in MFMA_KINDS:
             kern[f"{k}_ms_per_step"] = ms[k]
             kern[f"{k}_tflops"] = per_pair[k] * w.D * sum(pairs) / (ms[k] * 1e-3) / 1e12
-        ve_set = set(sa.ve_layers(w.n_layer)) if args.ve else set()
-        for k in HBM_KINDS:
-            # bytes per launch averaged over the layers (value-embedding layers read more)
-            nbytes = sum(hbm_bytes_per_launch(k, w, k == "kv_prep" and li in ve_set)
-                         for li in range(w.n_layer)) / w.n_layer
+        for k in hbm_kinds:
+            nbytes = hbm_bytes_per_launch("knorm", w)
             kern[f"{k}_ms_per_step"] = ms[k]
             kern[f"{k}_algorithmic_bytes"] = nbytes
             kern[f"{k}_gbs"] = nbytes * w.n_layer / (ms[k] * 1e-3) / 1e9
-            kern[f"{k}_traffic"] = traffic_bytes(w.name + variant_tag(args), *KERNELS[k])
+            kern[f"{k}_traffic"] = traffic_bytes(w.name + variant_tag(args), *KERNELS["knorm"])
         kern["ms_per_step_with_events"] = ms_step_events
         kern["other_ms_per_step"] = ms_step_events - sum(ms.values())
         dom = max(MFMA_KINDS, key=lambda k: ms[k])
@@ -772,6 +769,7 @@ def main():
             "flop_count": "band pairs x (4D fwd + 10D bwd)",
             "flop_per_step": flop_step,
             "launch": "HIP graph of the step, replayed" if graph is not None else "one call per layer",
+            "backward_k_rows": "recomputed" if args.recompute_k else "read back from the layer's forward workspace",
             "parallelism": "single GPU",
         },
         "wall_s_timed": wall,

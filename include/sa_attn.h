@@ -92,10 +92,16 @@ sa_status sa_qknorm(const void* x, void* y, float* rstd, int64_t rows, int head_
  *   q, k, v : inputs (layouts above).  o : bf16 output [B,T,Hq,D].
  *   lse     : fp32 output [B,Hq,T]; required (the backward needs it).
  *   workspace: device buffer of at least sa_attn_fwd_workspace_bytes(...)
- *            bytes, 256-byte aligned; it receives the normed k rows and the
- *            v rows transposed per KV head (keys padded to a multiple of 64).
- *            May be NULL when qk_norm == 0. Contents on entry are ignored, on return
- *            unspecified; overlapping calls need different workspaces.
+ *            bytes, 256-byte aligned. Contents on entry are ignored. With
+ *            qk_norm (and the fixed row maximum: |softmax_scale| * head_dim
+ *            within its bound) it receives, and keeps on return, the bf16
+ *            normed (with rotary tables: turned) k rows [B,T,Hkv,D] and their
+ *            fp32 1/rms [B,T,Hkv], and with the value-embedding gate the
+ *            bf16 rows v' [B,T,Hkv,D] and the fp32 gate [B,T,Hkv]: the
+ *            backward of the same layer can read them back instead of
+ *            recomputing them (sa_attn_bwd_ex's fwd_workspace). Otherwise
+ *            the contents on return are unspecified. May be NULL when
+ *            qk_norm == 0. Overlapping calls need different workspaces.
  *   Tiles of the band outside every query's window are never loaded.
  */
 size_t sa_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
@@ -116,7 +122,7 @@ size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
  *     dv_j = sum_{h in group} sum_i P_ij dout_i,
  *   then the RMS-norm backward dx = r (dx_hat - x_hat <dx_hat, x_hat> / D).
  *   Two kernels, no atomics: a dQ kernel per query block (it also writes the
- *   normed q rows and Delta into the workspace) and a persistent dK/dV kernel
+ *   normed q rows, Delta and the base-2 LSE into the workspace) and a persistent dK/dV kernel
  *   over the key blocks; the GQA sums over the query heads of a group happen
  *   inside the dK/dV kernel. With qk_norm a norm pass first writes the normed k rows
  *   into the workspace for both kernels.
@@ -125,8 +131,9 @@ size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim);
  *   workspace             : device buffer of at least
  *                           sa_attn_bwd_workspace_bytes(B,T,Hq,Hkv,head_dim)
  *                           bytes (the bf16 normed q rows, the fp32 Delta
- *                           rows, the bf16 normed k rows and their fp32
- *                           1/rms), 256-byte aligned;
+ *                           rows, the fp32 LSE rows in base 2, the bf16
+ *                           normed k rows and their fp32 1/rms), 256-byte
+ *                           aligned;
  *                           contents on entry are ignored and on return
  *                           unspecified. Two calls that overlap in time must
  *                           use different workspaces.
@@ -224,6 +231,16 @@ sa_status sa_attn_bwd_rope(const void* q, const void* k, const void* v, const vo
  *   Both extras need qk_norm (SA_ERR_UNSUPPORTED otherwise, for the gate with
  *   Hkv > 16, and when
  *   |softmax_scale| * head_dim is too large for the fixed row maximum).
+ *   fwd_workspace (backward; optional, NULL: none): the workspace that
+ *   sa_attn_fwd / sa_attn_fwd_rope / sa_attn_fwd_ex wrote for this layer,
+ *   with the same q, k, v, window, scale, eps, tables and gate inputs, and
+ *   not written since; fwd_workspace_bytes its size. The backward then
+ *   reads the normed k rows, their 1/rms and (gate) v' and the gate from it
+ *   instead of recomputing them, so a trainer that keeps the forward's
+ *   workspace per layer saves those passes. Read only; 256-byte aligned, at
+ *   least sa_attn_fwd_workspace_bytes(...) bytes (SA_ERR_WORKSPACE);
+ *   SA_ERR_UNSUPPORTED when qk_norm == 0 or the scale is beyond the fixed
+ *   row maximum (the forward then does not write it).
  *   Other errors as for the plain calls, plus SA_ERR_NULL for a partial group,
  *   SA_ERR_SHAPE for a bad stride or vocabulary, SA_ERR_ALIGN, SA_ERR_WORKSPACE.
  */
@@ -238,6 +255,7 @@ size_t sa_attn_ve_workspace_bytes(int B, int T, int Hkv, int head_dim);
 sa_status sa_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv,
                          void* workspace, size_t workspace_bytes,
+                         const void* fwd_workspace, size_t fwd_workspace_bytes,
                          int B, int T, int Hq, int Hkv, int head_dim, int window,
                          float softmax_scale, int qk_norm, float eps,
                          const float* rope_cos, const float* rope_sin, int rope_stride,
@@ -280,8 +298,8 @@ enum {
   SA_KERNEL_FWD = 0,       /* attention kernel of sa_attn_fwd */
   SA_KERNEL_BWD_DQ = 1,    /* dQ kernel of sa_attn_bwd */
   SA_KERNEL_BWD_DKDV = 2,  /* dK/dV kernel of sa_attn_bwd */
-  SA_KERNEL_KV_PREP = 3,   /* key-norm / value-transpose pass of sa_attn_fwd (QK-norm, bounded logits) */
-  SA_KERNEL_BWD_KNORM = 4  /* key-norm pass of sa_attn_bwd (QK-norm) */
+  SA_KERNEL_FWD_KNORM = 3, /* key-norm pass of sa_attn_fwd (QK-norm, bounded logits) */
+  SA_KERNEL_BWD_KNORM = 4  /* key-norm pass of sa_attn_bwd (QK-norm, no fwd_workspace) */
 };
 
 /*

@@ -31,11 +31,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa_attn.so")
 
 SA_OK = 0
-ABI_VERSION = 6
+ABI_VERSION = 7
 SA_KERNEL_FWD = 0
 SA_KERNEL_BWD_DQ = 1
 SA_KERNEL_BWD_DKDV = 2
-SA_KERNEL_KV_PREP = 3
+SA_KERNEL_FWD_KNORM = 3
 SA_KERNEL_BWD_KNORM = 4
 
 
@@ -87,7 +87,7 @@ def _load():
     lib.sa_attn_ve_workspace_bytes.restype = sz
     lib.sa_attn_ve_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.sa_attn_bwd_ex.restype = i32
-    lib.sa_attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+    lib.sa_attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz,
                                    i32, i32, i32, i32, i32, i32, f32, i32, f32, vp, vp, i32,
                                    vp, i64t, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.sa_polar_express_workspace_bytes.restype = sz
@@ -230,8 +230,10 @@ def sa_attn_ve_workspace_bytes(B, T, Hkv, head_dim):
 
 
 def sa_attn_bwd_ex(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6, dq=None, dk=None,
-                   dv=None, workspace=None, stream=None, rope=None, ve=None, ve_workspace=None):
-    """Backward with the optional extras. Returns (dq, dk, dv), plus (dve, dw, dx32) with ve."""
+                   dv=None, workspace=None, stream=None, rope=None, ve=None, ve_workspace=None, fwd_workspace=None):
+    """Backward with the optional extras. Returns (dq, dk, dv), plus (dve, dw, dx32) with ve.
+    fwd_workspace: the workspace the forward of this layer wrote (same inputs, tables and
+    embeddings); the backward then reads the normed k rows (and v', the gate) from it."""
     B, T, Hq, Hkv, D = _dims(q, k)
     for t, n, shp in ((q, "q", None), (k, "k", (B, T, Hkv, D)), (v, "v", (B, T, Hkv, D)),
                       (o, "o", q.shape), (dout, "dout", q.shape)):
@@ -256,9 +258,12 @@ def sa_attn_bwd_ex(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm
                    ve_workspace.numel())
     else:
         ve_ptrs = (None, 0, None, None, None, 0, None, None, None, None, 0)
+    if fwd_workspace is not None:
+        _need(fwd_workspace, "fwd_workspace", torch.uint8)
     _check("sa_attn_bwd_ex", _lib.sa_attn_bwd_ex(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(workspace), workspace.numel(), B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D),
+        _ptr(workspace), workspace.numel(), _ptr(fwd_workspace),
+        0 if fwd_workspace is None else fwd_workspace.numel(), B, T, Hq, Hkv, D, int(window), _scale(softmax_scale, D),
         int(bool(qk_norm)), float(eps), rc, rs, rstride, *ve_ptrs, _stream(q.device, stream)))
     return (dq, dk, dv) if ve is None else (dq, dk, dv, dve, dw, dx32)
 
@@ -322,12 +327,13 @@ def sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim):
 
 
 def sa_attn_bwd(q, k, v, o, lse, dout, window=-1, softmax_scale=None, qk_norm=True, eps=1e-6,
-                dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None, ve=None):
+                dq=None, dk=None, dv=None, workspace=None, stream=None, rope=None, ve=None, fwd_workspace=None):
     """Backward of one layer. Returns (dq, dk, dv) with respect to the raw q, k, v
-    (with ve also (dve, dw, dx32)); rope/ve as for sa_attn_fwd."""
-    if ve is not None:
+    (with ve also (dve, dw, dx32)); rope/ve as for sa_attn_fwd; fwd_workspace as for
+    sa_attn_bwd_ex."""
+    if ve is not None or fwd_workspace is not None:
         return sa_attn_bwd_ex(q, k, v, o, lse, dout, window, softmax_scale, qk_norm, eps, dq, dk, dv, workspace,
-                              stream, rope, ve)
+                              stream, rope, ve, fwd_workspace=fwd_workspace)
     if rope is not None:
         return sa_attn_bwd_rope(q, k, v, o, lse, dout, rope[0], rope[1], window, softmax_scale, qk_norm, eps,
                                 dq, dk, dv, workspace, stream)

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 
 // Benchmarking hook: events recorded around a kernel of later calls made
 // from this host thread (see sa_set_timing_events).
@@ -183,11 +183,29 @@ SA_API sa_status sa_qknorm(const void* x, void* y, float* rstd, int64_t rows, in
   return sa::launch_qknorm(p, head_dim, (hipStream_t)stream, sa::TimingEvents{}) == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
+// The forward's workspace, which the backward may read back: bf16 normed k
+// rows [B,T,Hkv,D], fp32 1/rms of the k rows [B,T,Hkv], and with value
+// embeddings the mixed value rows v' [B,T,Hkv,D] (bf16) and the gate [B,T,Hkv].
+struct FwdWorkspace {
+  char* khat;
+  float* rstd_k;
+  char* v_mixed;
+  float* gate;
+};
+FwdWorkspace fwd_workspace_of(const void* base, int B, int T, int Hkv, int head_dim) {
+  const size_t rh = (size_t)B * T * Hkv;
+  FwdWorkspace w;
+  w.khat = (char*)base;
+  w.rstd_k = (float*)(w.khat + round256(rh * head_dim * 2));
+  w.v_mixed = (char*)w.rstd_k + round256(rh * 4);
+  w.gate = (float*)(w.v_mixed + round256(rh * head_dim * 2));
+  return w;
+}
+
 SA_API size_t sa_attn_fwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
   if (check_shape(B, T, Hq, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
-  const size_t Tp = ((size_t)T + 63) / 64 * 64;
-  // bf16 normed k rows [B,T,Hkv,D], bf16 transposed v rows [B,Hkv,D,Tp]
-  return round256((size_t)B * T * Hkv * head_dim * 2) + round256((size_t)B * Hkv * head_dim * Tp * 2);
+  const size_t rh = (size_t)B * T * Hkv;
+  return 2 * round256(rh * head_dim * 2) + 2 * round256(rh * 4);
 }
 
 static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
@@ -233,15 +251,22 @@ static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, 
     p.pair_rows = p.G % 2 != 0;
     p.nsub = p.pair_rows ? p.G : p.G / 2;
     p.nqb = p.pair_rows ? (T + 255) / 256 : (T + 127) / 128;
-    // prologue: normed k rows and transposed v rows, so the attention kernel copies tiles
-    p.Tp = (T + 63) / 64 * 64;
     p.nwg = persistent_wgs();
     if (p.nwg <= 0) return SA_ERR_HIP;
-    p.khat = workspace;
-    p.vt = (char*)workspace + round256((size_t)B * T * Hkv * head_dim * 2);
+    // norm pass: normed (and turned) k rows and their 1/rms, which the attention kernel
+    // copies as tiles and the backward can reuse; with value embeddings the mixed rows v'
+    // and the gate, on which the attention (and the backward) runs
+    const FwdWorkspace fw = fwd_workspace_of(workspace, B, T, Hkv, head_dim);
+    sa::NormParams np{k, fw.khat, fw.rstd_k, (int64_t)B * T * Hkv, eps, rope, Hkv, T};
+    if (sa::launch_qknorm(np, head_dim, s, tl_events[SA_KERNEL_FWD_KNORM]) != hipSuccess) return SA_ERR_HIP;
+    p.khat = fw.khat;
+    p.vrows = v;
+    if (ve.x != nullptr) {
+      sa::VePrepParams vp{ve, v, fw.v_mixed, fw.gate, (long)B * T, Hkv, ve_bytes};
+      if (sa::launch_ve_prep(vp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+      p.vrows = fw.v_mixed;
+    }
     p.rope = rope;
-    sa::KvPrepParams kp{k, v, (void*)p.khat, (void*)p.vt, B, T, Hkv, p.Tp, eps, rope, ve, ve_bytes};
-    if (sa::launch_kv_prep(kp, head_dim, s, tl_events[SA_KERNEL_KV_PREP]) != hipSuccess) return SA_ERR_HIP;
     return sa::launch_fwd_pp(p, head_dim, s, tl_events[SA_KERNEL_FWD]) == hipSuccess ? SA_OK : SA_ERR_HIP;
   }
   // online-softmax kernel (logits without the QK-norm bound); no rotary tables or value embeddings there
@@ -257,14 +282,14 @@ static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, 
 SA_API size_t sa_attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int head_dim) {
   if (check_shape(B, T, Hq, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
   const size_t rows = (size_t)B * T * Hq;
-  // bf16 normed q rows, fp32 Delta, bf16 normed k rows, fp32 1/rms of the k rows
-  return round256(rows * head_dim * 2) + round256(rows * sizeof(float)) +
+  // bf16 normed q rows, fp32 Delta, fp32 base-2 LSE, bf16 normed k rows, fp32 1/rms of the k rows
+  return round256(rows * head_dim * 2) + 2 * round256(rows * sizeof(float)) +
          round256((size_t)B * T * Hkv * head_dim * 2) + round256((size_t)B * T * Hkv * sizeof(float));
 }
 
 static sa_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                           const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                          int B, int T, int Hq, int Hkv, int head_dim, int window, float softmax_scale, int qk_norm,
+                          const void* fwd_workspace, size_t fwd_workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window, float softmax_scale, int qk_norm,
                           float eps, const float* rope_cos, const float* rope_sin, int rope_stride, const void* ve_x,
                           int64_t ve_x_stride, const void* ve_w, const int32_t* ve_ids, const void* ve_table,
                           int ve_vocab, void* dve, float* dve_w, float* dve_x32, void* ve_workspace,
@@ -289,6 +314,14 @@ static sa_status attn_bwd(const void* q, const void* k, const void* v, const voi
   const size_t need = sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim);
   if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
     return SA_ERR_WORKSPACE;
+  if (fwd_workspace != nullptr) {
+    // only the QK-norm forward with the fixed row maximum writes what the backward reads back
+    float c2 = 0.f;
+    if (!fixed_max_ok(qk_norm, softmax_scale, head_dim, &c2)) return SA_ERR_UNSUPPORTED;
+    if (fwd_workspace_bytes < sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, head_dim) ||
+        ((uintptr_t)fwd_workspace & 255u) != 0)
+      return SA_ERR_WORKSPACE;
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return SA_ERR_ALIGN;
@@ -306,6 +339,7 @@ static sa_status attn_bwd(const void* q, const void* k, const void* v, const voi
   const size_t rows = (size_t)B * T * Hq;
   p.qhat = qk_norm ? workspace : (void*)q;
   p.delta = (float*)((char*)workspace + round256(rows * head_dim * 2));
+  p.lse2 = (float*)((char*)p.delta + round256(rows * sizeof(float)));
   p.B = B;
   p.T = T;
   p.Hq = Hq;
@@ -325,9 +359,14 @@ static sa_status attn_bwd(const void* q, const void* k, const void* v, const voi
   if (p.nwg <= 0) return SA_ERR_HIP;
   const hipStream_t s = (hipStream_t)stream;
   p.khat = k;
-  if (qk_norm) {
+  const FwdWorkspace fw = fwd_workspace_of(fwd_workspace, B, T, Hkv, head_dim);
+  if (fwd_workspace != nullptr) {
+    // the forward's normed k rows and their 1/rms
+    p.khat = fw.khat;
+    p.rstd_k = fw.rstd_k;
+  } else if (qk_norm) {
     // normed k rows, copied straight into LDS as tiles by the dQ kernel
-    void* khat = (char*)workspace + round256(rows * head_dim * 2) + round256(rows * sizeof(float));
+    void* khat = (char*)workspace + round256(rows * head_dim * 2) + 2 * round256(rows * sizeof(float));
     float* rstd_k = (float*)((char*)khat + round256((size_t)B * T * Hkv * head_dim * 2));
     sa::NormParams np{k, khat, rstd_k, (int64_t)B * T * Hkv, eps, rope, Hkv, T};
     if (sa::launch_qknorm(np, head_dim, s, tl_events[SA_KERNEL_BWD_KNORM]) != hipSuccess) return SA_ERR_HIP;
@@ -344,8 +383,14 @@ static sa_status attn_bwd(const void* q, const void* k, const void* v, const voi
   float* dz = (float*)((char*)gate + round256(rh * 4));
   float* part = (float*)((char*)dz + round256(rh * 4));
   if (ve.x != nullptr) {
-    sa::VePrepParams vp{ve, v, v_mixed, gate, nrows, Hkv, ve_bytes};
-    if (sa::launch_ve_prep(vp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+    if (fwd_workspace != nullptr) {
+      // the forward's v' and gate
+      v_mixed = fw.v_mixed;
+      gate = fw.gate;
+    } else {
+      sa::VePrepParams vp{ve, v, v_mixed, gate, nrows, Hkv, ve_bytes};
+      if (sa::launch_ve_prep(vp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
+    }
     p.v = v_mixed;
   }
   if (sa::launch_bwd_dq_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DQ]) != hipSuccess) return SA_ERR_HIP;
@@ -389,7 +434,7 @@ SA_API sa_status sa_attn_bwd(const void* q, const void* k, const void* v, const 
                              const void* dout, void* dq, void* dk, void* dv, void* workspace,
                              size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
                              float softmax_scale, int qk_norm, float eps, void* stream) {
-  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window,
+  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, nullptr, 0, B, T, Hq, Hkv, head_dim, window,
                   softmax_scale, qk_norm, eps, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, 0, nullptr,
                   nullptr, nullptr, nullptr, 0, stream);
 }
@@ -410,7 +455,7 @@ SA_API sa_status sa_attn_bwd_noalloc(const void* q, const void* k, const void* v
   if (sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, head_dim) > kScratchBytes) return SA_ERR_WORKSPACE;
   void* ws = scratch_ptr();
   if (ws == nullptr) return SA_ERR_HIP;
-  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, kScratchBytes, B, T, Hq, Hkv, head_dim, window,
+  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, kScratchBytes, nullptr, 0, B, T, Hq, Hkv, head_dim, window,
                   softmax_scale, qk_norm, eps, nullptr, nullptr, 0, nullptr, 0, nullptr, nullptr, nullptr, 0, nullptr,
                   nullptr, nullptr, nullptr, 0, stream);
 }
@@ -421,20 +466,21 @@ SA_API sa_status sa_attn_bwd_rope(const void* q, const void* k, const void* v, c
                                   float softmax_scale, int qk_norm, float eps, const float* rope_cos,
                                   const float* rope_sin, int rope_stride, void* stream) {
   if (rope_cos == nullptr || rope_sin == nullptr) return SA_ERR_NULL;
-  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window,
+  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, nullptr, 0, B, T, Hq, Hkv, head_dim, window,
                   softmax_scale, qk_norm, eps, rope_cos, rope_sin, rope_stride, nullptr, 0, nullptr, nullptr, nullptr,
                   0, nullptr, nullptr, nullptr, nullptr, 0, stream);
 }
 
 SA_API sa_status sa_attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                                size_t workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
+                                size_t workspace_bytes, const void* fwd_workspace, size_t fwd_workspace_bytes, int B, int T, int Hq, int Hkv, int head_dim, int window,
                                 float softmax_scale, int qk_norm, float eps, const float* rope_cos,
                                 const float* rope_sin, int rope_stride, const void* ve_x, int64_t ve_x_stride,
                                 const void* ve_w, const int32_t* ve_ids, const void* ve_table, int ve_vocab,
                                 void* dve, float* dve_w, float* dve_x32, void* ve_workspace,
                                 size_t ve_workspace_bytes, void* stream) {
-  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, T, Hq, Hkv, head_dim, window,
+  return attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, fwd_workspace, fwd_workspace_bytes,
+                  B, T, Hq, Hkv, head_dim, window,
                   softmax_scale, qk_norm, eps, rope_cos, rope_sin, rope_stride, ve_x, ve_x_stride, ve_w, ve_ids,
                   ve_table, ve_vocab, dve, dve_w, dve_x32, ve_workspace, ve_workspace_bytes, stream);
 }

@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 Qs[NB][TILE];
   __shared__ __attribute__((aligned(1024))) bf16 Os[NB][TILE];
   __shared__ __attribute__((aligned(1024))) bf16 Xs[4][2][2 * 512];  // P of a tile (2 chunks), per wave pair
-  __shared__ __attribute__((aligned(16))) float Ls[NB][BQ];          // LSE of the tile's rows
+  __shared__ __attribute__((aligned(16))) float Ls[NB][BQ];          // base-2 LSE of the tile's rows
   __shared__ __attribute__((aligned(16))) float Dl[NB][BQ];          // Delta of the tile's rows
 
   const int tid = threadIdx.x;
@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   }
   const uint32_t qs_lds = lds_addr(&Qs[0][0]);
   const uint32_t os_lds = lds_addr(&Os[0][0]);
-  auto issue = [&](int it) __attribute__((always_inline)) {  // group A: q_hat rows and LSE; group B: dO rows and Delta
+  auto issue = [&](int it) __attribute__((always_inline)) {  // group A: q_hat rows and base-2 LSE; group B: dO rows and Delta
     const int hh = it / nqb;
     const int row0 = (qb_lo + it % nqb) * BQ;
     const int head = g * p.G + hh;
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
       dma16(rs, uniform((int)(slot + m * 1024)), ldo + toff + (uint32_t)(m * RPI * qstride * 2), 0u);
     }
     if (rw == 0) {
-      const float* src = (grp == 0 ? p.lse : p.delta) + ((long)b * p.Hq + head) * T;
+      const float* src = (grp == 0 ? p.lse2 : p.delta) + ((long)b * p.Hq + head) * T;
       const u32x4 rl = rsrc_words(src, (uint32_t)T * 4);
       const uint32_t dst = lds_addr(grp == 0 ? &Ls[it % NB][0] : &Dl[it % NB][0]);
       dma4(rl, uniform((int)dst), (uint32_t)(row0 + lane) * 4);
@@ -196,14 +196,15 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   bf16x8 op[2][2];  // P (A) or dS (B) of the previous tile: B operands of dV / dK
 
   // band test of chunk qc of tile it: register r of a lane holds query row
-  // q0 + 16(r>>3) + 8half + (r&7) and key `key`
+  // q0 + 16(r>>3) + 8half + (r&7) and key `key`. Rows past T need no mask:
+  // their q_hat, dO, LSE and Delta arrive as zeros (the copies' range check),
+  // so their finite P meets zero dO rows in dV and a zero dS in dK.
   auto chunk_q0 = [&](int it, int qc) { return (qb_lo + it % nqb) * BQ + 32 * qc; };
   auto chunk_edge = [&](int q0) {  // not every (row, key) pair of the chunk is inside the band
-    return !(q0 >= kw0 + 31 && (W < 0 || q0 + 31 - kw0 <= W)) || q0 + 31 >= T;
+    return !(q0 >= kw0 + 31 && (W < 0 || q0 + 31 - kw0 <= W));
   };
-  auto band_ok = [&](int q0, int r) {  // bitwise and: no branch per element
-    const int q = q0 + 16 * (r >> 3) + 8 * half + (r & 7);
-    return ((uint32_t)(q - key) <= Wm) & (q < T);
+  auto band_ok = [&](int q0, int r) {
+    return (uint32_t)(q0 + 16 * (r >> 3) + 8 * half + (r & 7) - key) <= Wm;
   };
   auto xs_addr = [&](int qc, int ks) { return lds_addr(&Xs[rw][qc][ks * 512 + 8 * lane]); };
 
@@ -266,7 +267,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
           const f32x4 l1 = *(const f32x4*)(lse + 16 * ks + 8 * half + 4);
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            pr[8 * ks + e] = fast_exp2(__builtin_fmaf(sc[qc][8 * ks + e], p.c1, -(e < 4 ? l0[e] : l1[e - 4]) * kLog2e));
+            pr[8 * ks + e] = fast_exp2(__builtin_fmaf(sc[qc][8 * ks + e], p.c1, -(e < 4 ? l0[e] : l1[e - 4])));
         }
         if (chunk_edge(q0)) {  // one branch per chunk; the mask itself is a select per element
 #pragma unroll

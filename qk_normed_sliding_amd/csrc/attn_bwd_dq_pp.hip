@@ -348,7 +348,10 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
     for (int kk = 0; kk < KST; ++kk)
       df[kk] = *(SA_LDS const bf16x8*)(uintptr_t)(rbase + (uint32_t)((((2 * kk + half) ^ (l32 % CPR))) << 4));
     lse2 = row < T ? lse_raw * kLog2e : INFINITY;
-    if (half == 0 && row < T) p.delta[lrow] = delta;
+    if (half == 0 && row < T) {
+      p.delta[lrow] = delta;
+      p.lse2[lrow] = lse2;  // for the dK/dV kernel's probabilities
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

@@ -14,12 +14,14 @@
 //     heavy-first "snake" order (round k: item k*G + w, or k*G + G-1-w on
 //     odd rounds), which balances the causal triangle as well as a dynamic
 //     queue would, without a counter.
-//   - A prologue kernel has written k_hat (normed key rows) and v_t (value
-//     rows transposed to [D, keys]), so both tiles of 64 keys are plain
-//     copies, issued as buffer loads straight into LDS (no registers, no
-//     VALU) and XOR-swizzled so that the 16-byte operand reads of S = K Q^T
-//     and of O^T += V^T P^T are bank-conflict free. Three buffers per operand
-//     let the loads run two phases ahead of their use. The tiles of all the
+//   - The norm pass has written k_hat (normed key rows); the value rows are
+//     read as stored (v, or v' with value embeddings). Both tiles of 64 keys
+//     are plain copies, issued as buffer loads straight into LDS (no
+//     registers, no VALU) in one XOR-swizzled row layout: S = K Q^T reads K
+//     rows with 16-byte reads, O^T += V^T P^T reads V^T with the LDS
+//     transpose read (two 8-byte reads per operand), both bank-conflict
+//     free. Three buffers per operand let the loads run two phases ahead of
+//     their use. The tiles of all the
 //     workgroup's items form one stream: the loads of the next item start
 //     while the current one computes, its q rows are prefetched into
 //     registers a whole item ahead, and an item's epilogue (O / l, LSE) runs
@@ -37,17 +39,18 @@
 
 namespace sa {
 
-// Instruction order of an M-phase for the scheduler: LEAD operand reads,
-// then N - LEAD pairs of (MFMA, read of the operand LEAD places ahead), then
-// the last LEAD MFMAs. Each read so has LEAD MFMAs (LEAD x 32 cycles) to land
-// before it is used, while only about LEAD operands occupy registers.
-template <int N, int LEAD>
+// Instruction order of an M-phase for the scheduler: the reads of LEAD
+// operands (RPO LDS reads each), then N - LEAD groups of (MFMA, reads of the
+// operand LEAD places ahead), then the last LEAD MFMAs. Each read so has LEAD
+// MFMAs (LEAD x 32 cycles) to land before it is used, while only about LEAD
+// operands occupy registers.
+template <int N, int LEAD, int RPO>
 __device__ __forceinline__ void sched_ring() {
-  __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);  // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x100, LEAD * RPO, 0);  // DS reads
 #pragma unroll
   for (int i = 0; i < N - LEAD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, RPO, 0);  // DS reads
   }
   __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
 }
@@ -60,15 +63,14 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   constexpr int NDB = D / 32;         // 32-wide head_dim blocks of O
   constexpr int CPR = D / 8;          // 16-byte chunks per K row
   constexpr int TILE = BN * D;        // elements of a K tile [64][D] or a V^T tile [D][64]
-  constexpr int KRPI = 64 / CPR;      // K rows per direct-to-LDS instruction (1 KB)
-  constexpr int KIPW = BN / KRPI / 4; // K instructions per wave of the loading group, per tile
-  constexpr int VIPW = D / 8 / 4;     // V^T instructions per wave (8 rows of 128 B each)
+  constexpr int KRPI = 64 / CPR;      // key rows per direct-to-LDS instruction (1 KB)
+  constexpr int KIPW = BN / KRPI / 4; // instructions per wave of the loading group, per tile
   static_assert(KST == 2 * NDB, "one operand register set serves S and P.V chunks");
-  static_assert(KIPW >= 1 && VIPW >= 1, "tile rows must split over the 4 waves of a group");
+  static_assert(KIPW >= 1, "tile rows must split over the 4 waves of a group");
   static_assert(NB >= 3, "loads run two phases ahead of their first use");
 
   __shared__ __attribute__((aligned(1024))) bf16 Ks[NB][TILE];
-  __shared__ __attribute__((aligned(1024))) bf16 Vt[NB][TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[NB][TILE];
   __shared__ __attribute__((aligned(1024))) bf16 Qn[8][32 * D];  // next item's q rows, per wave
 
   const int tid = threadIdx.x;
@@ -122,22 +124,20 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   int n_steps = 0;
   for (int k = 0; k < nk; ++k) n_steps += item(k).ntile;
 
-  // ---- direct-to-LDS loads. Instruction j of wave rw fills the 1 KB block
-  // m = 4j + rw of a tile: K rows m*KRPI + lane/CPR, V^T rows 8m + lane/8.
-  // The lane's physical chunk holds logical chunk (physical ^ swizzle(row));
-  // with this block order the swizzle depends on rw and the lane only, so a
-  // lane's offset is one per-lane base plus a uniform part. The whole offset
-  // goes in the per-lane operand: the buffer's range check (rows past T read
-  // as zero) covers that operand only.
-  uint32_t kdo, vdo;
+  // ---- direct-to-LDS loads (the same layout for K and V tiles). Instruction
+  // j of wave rw fills the 1 KB block m = 4j + rw of a tile: rows m*KRPI +
+  // lane/CPR. The lane's physical chunk holds logical chunk (physical ^
+  // swizzle(row)); with this block order the swizzle depends on rw and the
+  // lane only, so a lane's offset is one per-lane base plus a uniform part.
+  // The whole offset goes in the per-lane operand: the buffer's range check
+  // (rows past T read as zero) covers that operand only.
+  uint32_t ldo;
   {
     const int r = rw * KRPI + lane / CPR;  // row of block m = rw (same swizzle as every m = 4j + rw)
-    kdo = (uint32_t)((lane / CPR) * kvstride + 8 * ((lane % CPR) ^ swz<CPR>(r))) * 2;
-    const int d = 8 * rw + lane / 8;
-    vdo = (uint32_t)((lane / 8) * p.Tp + 8 * ((lane & 7) ^ swz<8>(d))) * 2;
+    ldo = (uint32_t)((lane / CPR) * kvstride + 8 * ((lane % CPR) ^ swz<CPR>(r))) * 2;
   }
   const uint32_t ks_lds = lds_addr(&Ks[0][0]);
-  const uint32_t vt_lds = lds_addr(&Vt[0][0]);
+  const uint32_t vs_lds = lds_addr(&Vs[0][0]);
 
   // Load cursor: the next tile of the stream this wave's group loads (group 1
   // the K tiles, group 0 the V^T tiles), as (item, tile of the item).
@@ -149,31 +149,19 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
     const Item it = item(c.k);
     c.ntile = it.ntile;
     c.n_lo = it.n_lo;
-    if (grp == 1)
-      c.rsrc = rsrc_words((const bf16*)p.khat + ((long)it.b * T * p.Hkv + it.g) * D, (uint32_t)T * kvstride * 2);
-    else
-      c.rsrc = rsrc_words((const bf16*)p.vt + ((long)it.b * p.Hkv + it.g) * D * p.Tp, (uint32_t)D * p.Tp * 2);
+    c.rsrc = rsrc_words((const bf16*)(grp == 1 ? p.khat : p.vrows) + ((long)it.b * T * p.Hkv + it.g) * D,
+                        (uint32_t)T * kvstride * 2);
   };
   Cursor cur{0, 0, 0, 0, {0u, 0u, 0u, 0u}};
   cursor_item(cur);
   // issues the cursor's tile into LDS slot `s % NB` (s = its index in the stream) and advances
   auto issue = [&](int s) {
-    if (grp == 1) {
-      const uint32_t toff = (uint32_t)((cur.n_lo + cur.tau) * BN) * kvstride * 2;
-      const uint32_t base = ks_lds + (uint32_t)((s % NB) * TILE * 2);
+    const uint32_t toff = (uint32_t)((cur.n_lo + cur.tau) * BN) * kvstride * 2;
+    const uint32_t base = (grp == 1 ? ks_lds : vs_lds) + (uint32_t)((s % NB) * TILE * 2);
 #pragma unroll
-      for (int j = 0; j < KIPW; ++j) {
-        const int m = 4 * j + rw;
-        dma16(cur.rsrc, uniform((int)(base + m * 1024)), kdo + toff + (uint32_t)(m * KRPI * kvstride * 2), 0u);
-      }
-    } else {
-      const uint32_t toff = (uint32_t)((cur.n_lo + cur.tau) * BN) * 2;
-      const uint32_t base = vt_lds + (uint32_t)((s % NB) * TILE * 2);
-#pragma unroll
-      for (int j = 0; j < VIPW; ++j) {
-        const int m = 4 * j + rw;
-        dma16(cur.rsrc, uniform((int)(base + m * 1024)), vdo + toff + (uint32_t)(m * 8 * p.Tp * 2), 0u);
-      }
+    for (int j = 0; j < KIPW; ++j) {
+      const int m = 4 * j + rw;
+      dma16(cur.rsrc, uniform((int)(base + m * 1024)), ldo + toff + (uint32_t)(m * KRPI * kvstride * 2), 0u);
     }
     if (++cur.tau == cur.ntile) {
       cur.tau = 0;
@@ -181,13 +169,22 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
     }
   };
 
-  // ---- LDS operand reads (16 bytes each). Tile slots are 16 KB aligned and
-  // the swizzle only flips byte-offset bits 4..7, so each read address is
-  // (slot + lane base) ^ constant.
-  // K: row 32c + swap23(l32), head_dim 16kk + 8half -> chunk (2kk + half) ^ swz(row)
+  // ---- LDS operand reads. Tile slots are 16 KB aligned and the swizzle only
+  // flips byte-offset bits 4..7, so each read address is (slot + lane base)
+  // ^ constant.
+  // K rows (16-byte reads): row 32c + swap23(l32), head_dim 16kk + 8half ->
+  // chunk (2kk + half) ^ swz(row)
   const uint32_t ka_base = (uint32_t)(swap23(l32) * D * 2 + (((half ^ swz<CPR>(swap23(l32))) & (CPR - 1)) << 4));
-  // V^T: row l32 (+32db), keys 32c + 16ks + 8half -> chunk (4c + 2ks + half) ^ swz8(row)
-  const uint32_t va_base = (uint32_t)(l32 * 128 + ((half ^ swz<8>(l32)) << 4));
+  // V^T operands (transpose reads of 4 keys each): key rows 32c + 16ks +
+  // 8half + tq (+4), head_dim columns 32db + 16g1 + 4qq; for another db only
+  // chunk bits 2.. change, and the swizzle XORs them, so the address of
+  // block db is that of block 0 XOR (db << 6)
+  uint32_t vt_base[2];
+  {
+    const int tq = (lane >> 2) & 3, g1 = (lane >> 4) & 1, qq = lane & 3;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) vt_base[hi] = (uint32_t)swz_off<CPR>(8 * half + tq + 4 * hi, 16 * g1 + 4 * qq) * 2;
+  }
 
   bf16x8 qf[KST];  // q_hat rows of the current item (B operand of S)
   f32x16 oacc[NDB];
@@ -280,11 +277,13 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   // tile st (chunk c, k-step kk: A = K rows, B = Q^T). S needs no mask here:
   // the V-phase zeroes probabilities of keys outside the band.
   constexpr int NPV = 2 * KST;        // P.V operands of a tile (2 chunks)
-  constexpr int LEAD = 6;             // operand reads in flight ahead of the MFMAs
+  constexpr int LEAD = 4;             // operand reads in flight ahead of the MFMAs (more ran slower)
   auto lds_ld16 = [](uint32_t addr) { return *(SA_LDS const bf16x8*)(uintptr_t)addr; };
+  auto lds_tr = [](uint32_t addr) { return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4*)(uintptr_t)addr); };
   auto pv_read = [&](uint32_t vslot, int i) {  // i = (c * 2 + ks) * NDB + db
     const int db = i % NDB, ks = (i / NDB) & 1, c = i / (2 * NDB);
-    return lds_ld16(((vslot + va_base) ^ (uint32_t)((4 * c + 2 * ks) << 4)) + db * 32 * 128);
+    const uint32_t rb = vslot + (uint32_t)((32 * c + 16 * ks) * D * 2);
+    return cat(lds_tr(rb + (vt_base[0] ^ (uint32_t)(db << 6))), lds_tr(rb + (vt_base[1] ^ (uint32_t)(db << 6))));
   };
   auto pv_op = [&](int i, bf16x8 a) {
     const int db = i % NDB, ks = (i / NDB) & 1, c = i / (2 * NDB);
@@ -309,7 +308,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   // forward by ~4% (the backward kernels, whose matrix phases are longer,
   // keep the matrix phase first).
   auto m_phase = [&](int st, bool do_pv, bool do_s) {
-    const uint32_t Vb = vt_lds + (uint32_t)(((st + NB - 1) % NB) * TILE * 2);
+    const uint32_t Vb = vs_lds + (uint32_t)(((st + NB - 1) % NB) * TILE * 2);
     const uint32_t Kb = ks_lds + (uint32_t)((st % NB) * TILE * 2);
     __builtin_amdgcn_s_setprio(0);
     if (do_pv) {
@@ -322,7 +321,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
         pv_op(i, a);
         if (i + LEAD < NPV) ring[i % LEAD] = pv_read(Vb, i + LEAD);
       }
-      sched_ring<NPV, LEAD>();
+      sched_ring<NPV, LEAD, 2>();
     }
     if (do_s) {
       constexpr int N = 2 * KST;
@@ -335,7 +334,7 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
         s_op(i, a);
         if (i + LEAD < N) ring[i % LEAD] = s_read(Kb, i + LEAD);
       }
-      sched_ring<N, LEAD>();
+      sched_ring<N, LEAD, 1>();
     }
     __builtin_amdgcn_s_setprio(1);
   };

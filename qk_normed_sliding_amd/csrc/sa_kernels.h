@@ -56,9 +56,9 @@ struct VeBwdParams {
 struct FwdParams {
   const void* q;
   const void* k;
-  const void* khat;      // normed k rows [B, T, Hkv, D] (prologue kernel output)
+  const void* khat;      // normed k rows [B, T, Hkv, D] (norm pass output)
   const void* v;
-  const void* vt;        // v transposed per (b, g): [B, Hkv, D, Tp], keys >= T zero (prologue output)
+  const void* vrows;     // value rows the attention runs on [B, T, Hkv, D]: v, or v' with value embeddings
   void* o;
   float* lse;
   int B, T, Hq, Hkv, G;  // G = Hq / Hkv
@@ -70,22 +70,10 @@ struct FwdParams {
   int nsub;              // workgroups per (batch, KV head, query block) = G / heads-per-workgroup
   int pair_rows;         // two-group kernels: 0 = the two warp groups take the same 128 rows of two
                          // query heads; 1 = they take alternate 32-row slices of 256 rows of one head (odd G)
-  int Tp;                // T rounded up to a multiple of 64 (key axis of vt)
   int nwg;               // workgroups of a persistent launch (one per compute unit)
   Rope rope;             // rotary tables for q (k is turned by the prologue kernel)
 };
 
-struct KvPrepParams {
-  const void* k;
-  const void* v;
-  void* khat;  // [B, T, Hkv, D]
-  void* vt;    // [B, Hkv, D, Tp]
-  int B, T, Hkv, Tp;
-  float eps;
-  Rope rope;   // rotary tables for k (turned before the norm)
-  VeParams ve; // value-embedding gate mixed into v (ve.x == nullptr: none)
-  uint32_t ve_table_bytes;
-};
 
 struct BwdParams {
   const void* q;
@@ -99,6 +87,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;   // fp32 [B, Hq, T], written by the dQ kernel
+  float* lse2;    // fp32 [B, Hq, T]: the forward's LSE times log2(e), written by the dQ kernel
   void* qhat;     // bf16 [B, T, Hq, D]: normed q rows written by the dQ kernel (q itself without the norm)
   const float* rstd_k;  // fp32 [B, T, Hkv]: 1/rms of the k rows, written by the norm pass (with the QK-norm)
   int B, T, Hq, Hkv, G;
@@ -176,6 +165,5 @@ hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, 
 // Value-embedding gate: v' and g for the backward; then dve, dx32 and dw from dL/dv'.
 hipError_t launch_ve_prep(const VePrepParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_ve_bwd(const VeBwdParams& p, int head_dim, hipStream_t stream);
-hipError_t launch_kv_prep(const KvPrepParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
 
 }  // namespace sa

@@ -3,9 +3,10 @@
 // learned embedding of the token ids into v):
 //   g[b,t,h] = 2 sigmoid(sum_c x[b,t,c] w[h,c]), c < 32,
 //   v'[b,t,h,:] = v[b,t,h,:] + g[b,t,h] ve[b,t,h,:],  ve = table[ids[b,t]] viewed [Hkv, D].
-// The forward mixes inside the key/value prologue (kv_prep.hip). The backward
-// writes v' and g once (ve_prep_kernel), runs the attention kernels on v',
-// then maps dL/dv' to the embedding, gate and input gradients:
+// The forward writes v' and g once (ve_prep_kernel) into its workspace and
+// runs the attention on v'; the backward reads them back from there (or
+// writes them itself without the forward's workspace), runs its kernels on
+// v', then maps dL/dv' to the embedding, gate and input gradients:
 //   dve = g dv',  dz = <dv', ve> g (1 - g/2),  dx32 = dz w,  dw = sum_{b,t} dz^T x32,
 // the last as fixed-order partial sums per block of rows and one reduction.
 // dv (the raw v's gradient) is dv' itself. Embedding rows are read through a

@@ -142,15 +142,16 @@ def test_rope_validation_paths(sa):
 
 def test_workspace_size(sa):
     lib = sa.library()
-    assert lib.sa_attn_fwd_workspace_bytes(16, 2048, 6, 3, 128) == 2 * (16 * 2048 * 3 * 128 * 2)
-    # k_hat (5 rows of 2 x 64, rounded to 256 B) + v_t (2 x 64 rows of 64 padded keys)
-    assert lib.sa_attn_fwd_workspace_bytes(1, 5, 4, 2, 64) == 1280 + 2 * 64 * 64 * 2
+    # k_hat and v' (bf16 rows), 1/rms and gate (fp32 per row and KV head), each rounded to 256 B
+    assert lib.sa_attn_fwd_workspace_bytes(16, 2048, 6, 3, 128) == 2 * (16 * 2048 * 3 * 128 * 2) + 2 * (
+        16 * 2048 * 3 * 4)
+    assert lib.sa_attn_fwd_workspace_bytes(1, 5, 4, 2, 64) == 2 * 1280 + 2 * 256
     assert lib.sa_attn_fwd_workspace_bytes(1, 5, 4, 3, 64) == 0
     B, T, Hq, Hkv, D = 16, 2048, 6, 3, 128
     rows = B * T * Hq
     r256 = lambda x: (x + 255) // 256 * 256
-    # normed q rows, Delta, normed k rows, 1/rms of the k rows
-    assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D) == r256(rows * D * 2) + r256(rows * 4) + r256(
+    # normed q rows, Delta, base-2 LSE, normed k rows, 1/rms of the k rows
+    assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D) == r256(rows * D * 2) + 2 * r256(rows * 4) + r256(
         B * T * Hkv * D * 2) + r256(B * T * Hkv * 4)
     assert lib.sa_attn_bwd_workspace_bytes(B, T, 5, Hkv, D) == 0
     assert lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, 80) == 0
@@ -165,7 +166,7 @@ def test_timing_hook_validation(sa):
     assert lib.sa_set_max_workgroups(-1) == SA_ERR_SHAPE
     assert lib.sa_set_max_workgroups(3) == SA_OK
     assert lib.sa_set_max_workgroups(0) == SA_OK
-    for k in (sa.SA_KERNEL_FWD, sa.SA_KERNEL_BWD_DQ, sa.SA_KERNEL_BWD_DKDV, sa.SA_KERNEL_KV_PREP,
+    for k in (sa.SA_KERNEL_FWD, sa.SA_KERNEL_BWD_DQ, sa.SA_KERNEL_BWD_DKDV, sa.SA_KERNEL_FWD_KNORM,
               sa.SA_KERNEL_BWD_KNORM):
         assert lib.sa_set_timing_events(k, None, None) == SA_OK
 
@@ -254,11 +255,14 @@ def test_value_embedding_validation_paths(sa):
         return lib.sa_attn_fwd_ex(P(16), P(16), P(16), P(16), P(16), P(256), ws, B, T, Hq, Hkv, D, -1, 0.125, norm,
                                   1e-6, None, None, 0, P(x), xs, P(w), P(ids), P(tab), vocab, None)
 
-    def bwd(dve=20480, dw=24576, dx=28672, vws=32768, vws_bytes=None, ids=12288):
+    def bwd(dve=20480, dw=24576, dx=28672, vws=32768, vws_bytes=None, ids=12288, fws=0, fws_bytes=None, norm=1,
+            scale=0.125):
         ws = lib.sa_attn_bwd_workspace_bytes(B, T, Hq, Hkv, D)
         need = lib.sa_attn_ve_workspace_bytes(B, T, Hkv, D) if vws_bytes is None else vws_bytes
+        fneed = lib.sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D) if fws_bytes is None else fws_bytes
         return lib.sa_attn_bwd_ex(P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(16), P(256), ws,
-                                  B, T, Hq, Hkv, D, -1, 0.125, 1, 1e-6, None, None, 0,
+                                  P(fws) if fws else None, fneed if fws else 0,
+                                  B, T, Hq, Hkv, D, -1, scale, norm, 1e-6, None, None, 0,
                                   P(4096), 768, P(8192), P(ids), P(16384), 100,
                                   P(dve), P(dw), P(dx), P(vws), need, None)
 
@@ -277,6 +281,10 @@ def test_value_embedding_validation_paths(sa):
     assert bwd(vws=0) == SA_ERR_WORKSPACE
     assert bwd(vws_bytes=64) == SA_ERR_WORKSPACE
     assert bwd(vws=32768 + 128) == SA_ERR_WORKSPACE
+    # the forward's workspace handed back to the backward
+    assert bwd(fws=65536, fws_bytes=64) == SA_ERR_WORKSPACE          # too small
+    assert bwd(fws=65536 + 128) == SA_ERR_WORKSPACE                  # not 256-byte aligned
+    assert bwd(fws=65536, scale=2.0) == SA_ERR_UNSUPPORTED           # beyond the fixed row maximum
 
 
 def test_rope_tables_helper_matches_the_oracle(sa):

@@ -471,7 +471,7 @@ def test_timing_events_bracket_each_kernel(sa):
     scale = D ** -0.5
     log("[timing events]")
     q, k, v, do = (x.cuda() for x in synth.small_case(B, T, Hq, Hkv, D, seed=813))
-    ids = (sa.SA_KERNEL_FWD, sa.SA_KERNEL_KV_PREP, sa.SA_KERNEL_BWD_DQ, sa.SA_KERNEL_BWD_DKDV, sa.SA_KERNEL_BWD_KNORM)
+    ids = (sa.SA_KERNEL_FWD, sa.SA_KERNEL_FWD_KNORM, sa.SA_KERNEL_BWD_DQ, sa.SA_KERNEL_BWD_DKDV, sa.SA_KERNEL_BWD_KNORM)
     evs = {}
     for i in ids:
         pair = [ctypes.c_void_p(), ctypes.c_void_p()]
@@ -503,3 +503,33 @@ def test_timing_events_bracket_each_kernel(sa):
             hip.hipEventDestroy(ctypes.c_void_p(h))
     for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), got, ref):
         assert torch.equal(a, b), name
+
+
+FWD_WS_CASES = [  # B, T, Hq, Hkv, D, W, rope, ve
+    (2, 300, 6, 3, 128, 100, False, False),
+    (1, 257, 4, 4, 64, -1, True, False),
+    (2, 200, 4, 2, 128, 64, True, True),
+]
+
+
+@pytest.mark.parametrize("case", FWD_WS_CASES, ids=[f"B{c[0]}T{c[1]}Hq{c[2]}Hkv{c[3]}D{c[4]}W{c[5]}r{int(c[6])}v{int(c[7])}"
+                                                    for c in FWD_WS_CASES])
+def test_backward_reads_the_forward_workspace(sa, case):
+    """A backward handed the forward's workspace (normed k rows, their 1/rms,
+    and with the value-embedding gate v' and the gate) gives exactly the
+    results of a backward that recomputes them: the same passes wrote them."""
+    B, T, Hq, Hkv, D, W, use_rope, use_ve = case
+    scale = D ** -0.5
+    log(f"[fwd workspace] {case}")
+    q, k, v, do = (t.cuda() for t in synth.small_case(B, T, Hq, Hkv, D, seed=820 + T))
+    rope = sa.rope_tables(T, D, device="cuda") if use_rope else None
+    ve = tuple(t.cuda() for t in _ve_case_inputs(B, T, Hkv, D, 64, 821)) if use_ve else None
+    wsf = torch.empty(sa.sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D), dtype=torch.uint8, device="cuda")
+    o, lse = sa.sa_attn_fwd(q, k, v, window=W, softmax_scale=scale, rope=rope, ve=ve, workspace=wsf)
+    own = sa.sa_attn_bwd_ex(q, k, v, o, lse, do, window=W, softmax_scale=scale, rope=rope, ve=ve)
+    reused = sa.sa_attn_bwd_ex(q, k, v, o, lse, do, window=W, softmax_scale=scale, rope=rope, ve=ve,
+                               fwd_workspace=wsf)
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dve", "dw", "dx32")
+    for n, a, b in zip(names, own, reused):
+        assert torch.equal(a, b), n
