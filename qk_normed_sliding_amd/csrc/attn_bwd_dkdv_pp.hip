@@ -71,6 +71,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) bf16 Xs[4][2][2 * 512];  // P of a tile (2 chunks), per wave pair
   __shared__ __attribute__((aligned(16))) float Ls[NB][BQ];          // base-2 LSE of the tile's rows
   __shared__ __attribute__((aligned(16))) float Dl[NB][BQ];          // Delta of the tile's rows
+  __shared__ __attribute__((aligned(1024))) bf16 Bs[4][32 * D];      // group B's per-key rows at a block change
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,6 +156,38 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
     for (int kk = 0; kk < KST; ++kk) dst[kk] = __builtin_bit_cast(bf16x8, bload16(rk, off + 32 * kk));
   };
   load_kf(kf);
+
+  // ---- per-key rows at a block change, through a per-wave staging area of 32
+  // rows (group A: tile slots 1-2 of Os, which the next block does not load
+  // before its first barrier; group B: Bs), row r's 16-byte chunk j at chunk
+  // j ^ (r mod CPR), so that both directions are conflict free. The next
+  // block's rows arrive by coalesced buffer-to-LDS copies (RPI whole rows per
+  // instruction) and are read into the operand registers; the finished
+  // block's dv or dk rows leave through the same area as whole rows. (The
+  // lane index is made opaque where the addresses are formed, so that they
+  // are computed at the block change, not kept in registers in between.)
+  const uint32_t kst_lds = grp == 0 ? lds_addr(&Os[1][0]) + (uint32_t)(rw * 32 * D * 2) : lds_addr(&Bs[rw][0]);
+  auto stage_rows = [&]() __attribute__((always_inline)) {
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const long first = ((long)b * T * p.Hkv + g) * D + (long)kb0 * kvstride;
+    const uint32_t bytes = (uint32_t)max(0, T - kb0) * kvstride * 2;
+    const u32x4 rs = rsrc_words((const bf16*)(grp == 0 ? p.khat : p.v) + first, bytes);
+#pragma unroll
+    for (int m = 0; m < 32 / RPI; ++m) {
+      const int r = m * RPI + el / CPR;  // row within the wave's 32 keys
+      const int lc = (el % CPR) ^ (r % CPR);
+      dma16(rs, uniform((int)(kst_lds + m * 1024)), (uint32_t)((32 * rw + r) * kvstride + 8 * lc) * 2, 0u);
+    }
+  };
+  auto kf_from_stage = [&]() __attribute__((always_inline)) {
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int e32 = el & 31, eh = el >> 5;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      kf[kk] = *(SA_LDS const bf16x8*)(uintptr_t)(kst_lds + (uint32_t)(e32 * D * 2 + (((2 * kk + eh) ^ (e32 % CPR)) << 4)));
+  };
 
   // ---- LDS read addresses (bytes): row reads of rows 32qc + swap23(l32),
   // head_dim 16kk + 8half: (slot + base) ^ (kk << 5); transpose reads of rows
@@ -361,19 +394,18 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
     // the finished block, for its epilogue; the next block's rows, 1/rms and first tile are loaded
     // meanwhile, and the epilogue's stores are issued after they have arrived, so that the wait
     // for them does not include the stores
-    const int e_b = b, e_g = g, e_key = key;
+    const int e_b = b, e_g = g, e_key = key, e_kw0 = kw0;
     const float e_rk = r_k;
     const bool more = bk + 1 < n_blk;
     if (more) {
       set_block(bk + 1);
-      load_kf(kf);
+      stage_rows();
       r_k = load_rk();
       issue(0);
     }
     __syncthreads();
 
     // ---- epilogue (the accumulators hold head_dim 32db + 8i + 4half + j of key `key`)
-    const long rowoff = ((long)e_b * T + e_key) * kvstride + (long)e_g * D + 4 * half;
     if (grp == 1 && e_key < T) {
       // dk = r (dk_hat - k_hat <dk_hat, k_hat> / D), dk_hat = scale * acc, with
       // k_hat as the S MFMAs used it (bf16; with rotary tables the turned row,
@@ -435,11 +467,16 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
           }
       }
     }
-    // the rows, 1/rms and first tile of the next block have arrived; then this block's dv (group A)
-    // or dk (group B) rows
+    // the rows, 1/rms and first tile of the next block have arrived: the next rows go to the
+    // operand registers, then this block's dv (group A) or dk (group B) rows leave through the
+    // staging area (a wave's LDS accesses stay in order, so the reads see the rows first)
     __builtin_amdgcn_s_waitcnt(0);
-    if (e_key < T) {
-      bf16* dst = (bf16*)(grp == 0 ? p.dv : p.dk) + rowoff;
+    if (more) kf_from_stage();
+    {
+      int el = lane;
+      asm volatile("" : "+v"(el));
+      const int e32 = el & 31, eh = el >> 5;
+      const uint32_t wbase = kst_lds + (uint32_t)(e32 * D * 2 + 8 * eh);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -447,8 +484,18 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
           u32x2 w;
           w[0] = pack2(acc[db][4 * i], acc[db][4 * i + 1]);
           w[1] = pack2(acc[db][4 * i + 2], acc[db][4 * i + 3]);
-          *(u32x2*)(dst + 32 * db + 8 * i) = w;
+          const int c = 4 * db + i;  // 16-byte chunk of head_dim 32db + 8i
+          *(SA_LDS u32x2*)(uintptr_t)(wbase + (uint32_t)((c ^ (e32 % CPR)) << 4)) = w;
         }
+      const int nrows = min(32, T - e_kw0);  // rows of the wave's keys below T
+      bf16* dst = (bf16*)(grp == 0 ? p.dv : p.dk) + ((long)e_b * T + e_kw0) * kvstride + (long)e_g * D;
+      const int crow = el / CPR, cch = el % CPR;
+#pragma unroll
+      for (int m = 0; m < 32 / RPI; ++m) {
+        const int r = RPI * m + crow;
+        const u32x4 w = *(SA_LDS const u32x4*)(uintptr_t)(kst_lds + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4)));
+        if (r < nrows) st16(dst + (long)r * kvstride + 8 * cch, w);
+      }
     }
     // the next block's accumulators start at zero
     if (more) {
