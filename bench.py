@@ -203,6 +203,8 @@ def parse():
     ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS0_DIR", "PASS1_DIR"),
                     help="summarize the two rocprofv3 --pmc SQ counter passes of this script into profiles/ "
                          "and exit (no GPU needed)")
+    ap.add_argument("--summarize-polar-trace", nargs=3, metavar=("TRACE_DIR", "BENCH_JSON", "COMMAND"),
+                    help="summarize a rocprofv3 --kernel-trace run of `bench.py --polar` into profiles/ and exit")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "TRACE_JSON", "PLAIN_JSON", "COMMAND"),
                     help="summarize a rocprofv3 --kernel-trace run of this script (its JSON line in TRACE_JSON) "
                          "over the dispatches that the run's HIP events timed, beside the events of that run "
@@ -400,6 +402,47 @@ def summarize_sq(dir_a, dir_b, workload, extra=""):
     print("\n".join(out))
 
 
+def summarize_polar_trace(trace_dir, bench_json, command):
+    """Per-kernel statistics over every dispatch of a rocprofv3 --kernel-trace run of
+    `bench.py --polar`, beside that run's JSON line; writes
+    profiles/polar_express_muon_groups_n768_trace.md."""
+    rec = _json_line(bench_json)
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *kernel_trace.csv under {trace_dir}")
+    by = {}
+    for r in rows:
+        name = r["Kernel_Name"].split("<")[0]
+        if name.startswith(("gemm", "sumsq", "transpose")):
+            by.setdefault(name, []).append(r)
+    tot = sum((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for v in by.values() for r in v)
+    out = [f"# Kernel trace: {rec['config']['workload']} (Muon polar express, 5 steps)", "",
+           "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
+           "| kernel | dispatches | total us | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    shapes = []
+    for name, v in sorted(by.items(), key=lambda kv: -len(kv[1])):
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in v]
+        out.append(f"| {name} | {len(d)} | {sum(d):.1f} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} | "
+                   f"{100 * sum(d) / tot:.2f} |")
+        seen = set()
+        for r in v:
+            key = (r["Grid_Size_X"], r["Grid_Size_Y"])
+            if key not in seen:
+                seen.add(key)
+                shapes.append(f"- {name}: grid {r['Grid_Size_X']}x{r['Grid_Size_Y']}, wg {r['Workgroup_Size_X']}, "
+                              f"LDS {r['LDS_Block_Size']}, VGPR {r['VGPR_Count']}, AGPR {r['Accum_VGPR_Count']}")
+    out += ["", "Launch shapes:", ""] + shapes
+    out += ["", f"The same run's JSON line: {rec['value']:.1f} TFLOP/s, {rec['ms_per_step']:.3f} ms per optimizer step "
+                f"({rec['steps']} timed steps after {rec['warmup']} warm-up; the trace counts the warm-up too)."]
+    path = os.path.join(PROFILES, "polar_express_muon_groups_n768_trace.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def cpu_model() -> str:
     """The host CPU as lscpu names it: model name, family and model numbers, from /proc/cpuinfo
     (a virtual machine may report a short model name; the numbers still identify the part)."""
@@ -569,6 +612,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_polar_trace:
+        summarize_polar_trace(*args.summarize_polar_trace)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU path "
