@@ -238,13 +238,18 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(h))
 
 
-def hbm_bytes_per_launch(kind, w):
+def hbm_bytes_per_launch(kind, w, gated=False):
     """Algorithmic HBM bytes of one launch of an HBM-bound pass: every element it must read,
     read once, and every element it must write, written once. The k-norm pass reads the bf16
-    k rows and writes the bf16 normed rows and an fp32 1/rms per row."""
+    k rows and writes the bf16 normed rows and an fp32 1/rms per row. On a layer with the
+    value-embedding gate the same launch also reads v, the gathered embedding rows, the ids
+    and the first 32 channels of x, and writes v' and the fp32 gate."""
     rows = w.B * w.T * w.Hkv
     if kind == "knorm":
-        return rows * w.D * 2 * 2 + rows * 4
+        nbytes = rows * w.D * 2 * 2 + rows * 4
+        if gated:
+            nbytes += rows * w.D * 2 * 3 + rows * 4 + w.B * w.T * (4 + 64)
+        return nbytes
     raise ValueError(kind)
 
 
@@ -758,10 +763,11 @@ def main():
             kern[f"{k}_ms_per_step"] = ms[k]
             kern[f"{k}_tflops"] = per_pair[k] * w.D * sum(pairs) / (ms[k] * 1e-3) / 1e12
         for k in hbm_kinds:
-            nbytes = hbm_bytes_per_launch("knorm", w)
+            # (the backward's own pass, run only without the forward's workspace, mixes v' too)
+            step_bytes = sum(hbm_bytes_per_launch("knorm", w, gated=L["ve"] is not None) for L in layers)
             kern[f"{k}_ms_per_step"] = ms[k]
-            kern[f"{k}_algorithmic_bytes"] = nbytes
-            kern[f"{k}_gbs"] = nbytes * w.n_layer / (ms[k] * 1e-3) / 1e9
+            kern[f"{k}_algorithmic_bytes"] = step_bytes / w.n_layer
+            kern[f"{k}_gbs"] = step_bytes / (ms[k] * 1e-3) / 1e9
             kern[f"{k}_traffic"] = traffic_bytes(w.name + variant_tag(args), *KERNELS["knorm"])
         kern["ms_per_step_with_events"] = ms_step_events
         kern["other_ms_per_step"] = ms_step_events - sum(ms.values())

@@ -154,8 +154,8 @@ SA_API int sa_abi_version(void) { return kAbiVersion; }
 SA_API size_t sa_attn_ve_workspace_bytes(int B, int T, int Hkv, int head_dim) {
   if (check_shape(B, T, Hkv, Hkv, head_dim, -1, 1.f, 0.f) != SA_OK) return 0;
   const size_t rh = (size_t)B * T * Hkv;
-  // v' (bf16), gate and dz (fp32 per row and head), per-block partial sums of dw
-  return round256(rh * head_dim * 2) + 2 * round256(rh * 4) + round256(ve_blocks(B, T) * Hkv * 32 * 4);
+  // v' (bf16), the gate (fp32 per row and head), per-block partial sums of dw
+  return round256(rh * head_dim * 2) + round256(rh * 4) + round256(ve_blocks(B, T) * Hkv * 32 * 4);
 }
 
 SA_API const char* sa_status_string(int status) {
@@ -258,14 +258,12 @@ static sa_status attn_fwd(const void* q, const void* k, const void* v, void* o, 
     // and the gate, on which the attention (and the backward) runs
     const FwdWorkspace fw = fwd_workspace_of(workspace, B, T, Hkv, head_dim);
     sa::NormParams np{k, fw.khat, fw.rstd_k, (int64_t)B * T * Hkv, eps, rope, Hkv, T};
-    if (sa::launch_qknorm(np, head_dim, s, tl_events[SA_KERNEL_FWD_KNORM]) != hipSuccess) return SA_ERR_HIP;
+    const sa::VePrepParams vp{ve, v, fw.v_mixed, fw.gate, (long)B * T, Hkv, ve_bytes};
+    if (sa::launch_qknorm(np, head_dim, s, tl_events[SA_KERNEL_FWD_KNORM], ve.x != nullptr ? &vp : nullptr) !=
+        hipSuccess)
+      return SA_ERR_HIP;
     p.khat = fw.khat;
-    p.vrows = v;
-    if (ve.x != nullptr) {
-      sa::VePrepParams vp{ve, v, fw.v_mixed, fw.gate, (long)B * T, Hkv, ve_bytes};
-      if (sa::launch_ve_prep(vp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
-      p.vrows = fw.v_mixed;
-    }
+    p.vrows = ve.x != nullptr ? fw.v_mixed : v;
     p.rope = rope;
     return sa::launch_fwd_pp(p, head_dim, s, tl_events[SA_KERNEL_FWD]) == hipSuccess ? SA_OK : SA_ERR_HIP;
   }
@@ -360,44 +358,37 @@ static sa_status attn_bwd(const void* q, const void* k, const void* v, const voi
   const hipStream_t s = (hipStream_t)stream;
   p.khat = k;
   const FwdWorkspace fw = fwd_workspace_of(fwd_workspace, B, T, Hkv, head_dim);
+  // value embeddings: the attention kernels run on v' = v + g ve, written once (by the
+  // forward's norm pass, or below with the k rows)
+  const long nrows = (long)B * T;
+  const size_t rh = (size_t)nrows * Hkv;
+  char* vw = (char*)ve_workspace;
+  void* v_mixed = fwd_workspace != nullptr ? fw.v_mixed : vw;
+  float* gate = fwd_workspace != nullptr ? fw.gate : (float*)(vw + round256(rh * head_dim * 2));
+  float* part = (float*)(vw + round256(rh * head_dim * 2) + round256(rh * 4));
+  if (ve.x != nullptr) p.v = v_mixed;
   if (fwd_workspace != nullptr) {
     // the forward's normed k rows and their 1/rms
     p.khat = fw.khat;
     p.rstd_k = fw.rstd_k;
   } else if (qk_norm) {
-    // normed k rows, copied straight into LDS as tiles by the dQ kernel
+    // normed k rows, copied straight into LDS as tiles by the dQ kernel (and v', g)
     void* khat = (char*)workspace + round256(rows * head_dim * 2) + 2 * round256(rows * sizeof(float));
     float* rstd_k = (float*)((char*)khat + round256((size_t)B * T * Hkv * head_dim * 2));
     sa::NormParams np{k, khat, rstd_k, (int64_t)B * T * Hkv, eps, rope, Hkv, T};
-    if (sa::launch_qknorm(np, head_dim, s, tl_events[SA_KERNEL_BWD_KNORM]) != hipSuccess) return SA_ERR_HIP;
+    const sa::VePrepParams vp{ve, v, v_mixed, gate, nrows, Hkv, ve_bytes};
+    if (sa::launch_qknorm(np, head_dim, s, tl_events[SA_KERNEL_BWD_KNORM], ve.x != nullptr ? &vp : nullptr) !=
+        hipSuccess)
+      return SA_ERR_HIP;
     p.khat = khat;
     p.rstd_k = rstd_k;
   }
   p.rope = rope;
-  // value embeddings: the attention kernels run on v' = v + g ve, written once
-  const long nrows = (long)B * T;
-  const size_t rh = (size_t)nrows * Hkv;
-  char* vw = (char*)ve_workspace;
-  void* v_mixed = vw;
-  float* gate = (float*)(vw + round256(rh * head_dim * 2));
-  float* dz = (float*)((char*)gate + round256(rh * 4));
-  float* part = (float*)((char*)dz + round256(rh * 4));
-  if (ve.x != nullptr) {
-    if (fwd_workspace != nullptr) {
-      // the forward's v' and gate
-      v_mixed = fw.v_mixed;
-      gate = fw.gate;
-    } else {
-      sa::VePrepParams vp{ve, v, v_mixed, gate, nrows, Hkv, ve_bytes};
-      if (sa::launch_ve_prep(vp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
-    }
-    p.v = v_mixed;
-  }
   if (sa::launch_bwd_dq_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DQ]) != hipSuccess) return SA_ERR_HIP;
   if (sa::launch_bwd_dkdv_pp(p, head_dim, s, tl_events[SA_KERNEL_BWD_DKDV]) != hipSuccess) return SA_ERR_HIP;
   if (ve.x != nullptr) {
     // dv holds dL/dv' (also the raw v's gradient); the gate's and embedding's gradients from it
-    sa::VeBwdParams bp{ve, dv, gate, dve, dz, dve_x32, part, dve_w, nrows, Hkv, ve_bytes};
+    sa::VeBwdParams bp{ve, dv, gate, dve, dve_x32, part, dve_w, nrows, Hkv, ve_bytes};
     if (sa::launch_ve_bwd(bp, head_dim, s) != hipSuccess) return SA_ERR_HIP;
   }
   return SA_OK;

@@ -26,7 +26,7 @@ struct VeParams {
   const int32_t* ids;
   const void* table;
 };
-constexpr int kVeRows = 64;  // rows per block of the gate backward's partial sums
+constexpr int kVeRows = 32;  // rows per workgroup of the gate's passes (and per partial sum of dw)
 constexpr int kVeMaxHeads = 16;  // KV heads the value-embedding gate supports
 
 struct VePrepParams {
@@ -44,9 +44,8 @@ struct VeBwdParams {
   const void* dv;      // dL/dv' (bf16 [rows, Hkv, D])
   const float* gate;   // as written by ve_prep
   void* dve;           // bf16 [rows, Hkv, D]
-  float* dz;           // fp32 [rows, Hkv] (workspace)
   float* dx32;         // fp32 [rows, 32]
-  float* part;         // fp32 [ceil(rows / kVeRows), Hkv, 32] (workspace)
+  float* part;         // fp32 [Hkv * 32, ceil(rows / kVeRows)] (workspace): per (head, channel), the blocks' partials
   float* dw;           // fp32 [Hkv, 32]
   long rows;
   int Hkv;
@@ -155,15 +154,16 @@ hipError_t launch_bwd_dq_pp(const BwdParams& p, int head_dim, hipStream_t stream
 // dK/dV kernel whose two warp groups (per-key state split by role) alternate on the matrix cores
 // (any query-heads-per-KV-head ratio).
 hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
-hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev);
+// With ve: the same launch also writes the value-embedding mix v' and the gate.
+hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev,
+                         const VePrepParams* ve = nullptr);
 // Polar-express pieces: GEMM (b_kn: B given as [K][N]), partial sums of
 // squares for ||X||_F per matrix (part: batch * kFroChunks floats), and
 // per-matrix transpose [R][C] -> [C][R].
 hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream);
 hipError_t launch_fro_sumsq(const void* x, float* part, int batch, long per_matrix, hipStream_t stream);
 hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, hipStream_t stream);
-// Value-embedding gate: v' and g for the backward; then dve, dx32 and dw from dL/dv'.
-hipError_t launch_ve_prep(const VePrepParams& p, int head_dim, hipStream_t stream);
+// Value-embedding gate backward: dve, dx32 and dw from dL/dv' (v' and g come from the norm pass).
 hipError_t launch_ve_bwd(const VeBwdParams& p, int head_dim, hipStream_t stream);
 
 }  // namespace sa

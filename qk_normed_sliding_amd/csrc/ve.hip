@@ -3,12 +3,13 @@
 // learned embedding of the token ids into v):
 //   g[b,t,h] = 2 sigmoid(sum_c x[b,t,c] w[h,c]), c < 32,
 //   v'[b,t,h,:] = v[b,t,h,:] + g[b,t,h] ve[b,t,h,:],  ve = table[ids[b,t]] viewed [Hkv, D].
-// The forward writes v' and g once (ve_prep_kernel) into its workspace and
+// The forward's norm pass writes v' and g once (qknorm.hip) into its workspace and
 // runs the attention on v'; the backward reads them back from there (or
 // writes them itself without the forward's workspace), runs its kernels on
 // v', then maps dL/dv' to the embedding, gate and input gradients:
 //   dve = g dv',  dz = <dv', ve> g (1 - g/2),  dx32 = dz w,  dw = sum_{b,t} dz^T x32,
-// the last as fixed-order partial sums per block of rows and one reduction.
+// in one pass per block of rows (dz stays in LDS), dw as fixed-order partial
+// sums per block and one reduction.
 // dv (the raw v's gradient) is dv' itself. Embedding rows are read through a
 // buffer descriptor over the table: an id past the table reads zeros.
 #include "sa_common.h"
@@ -17,83 +18,93 @@
 
 namespace sa {
 
-// v' and g for the backward: one 16-byte chunk per lane, D/8 lanes per (row, head).
+// Chunk tasks per pass of the backward's streaming loop: CPR lanes per (row,
+// head), one 16-byte chunk each; the workgroup covers kVeRows rows, all heads
+// (pairs rh0 .. rh0 + npair, pair i = (row r0 + i / H, head i % H)), U passes
+// per group, whose loads are all issued before the first result is used (ids,
+// rows and gates first, then the embedding rows the ids select).
 template <int D>
-__global__ void __launch_bounds__(256) ve_prep_kernel(VePrepParams p) {
-  constexpr int CPR = D / 8;
-  const long nrh = (long)p.rows * p.Hkv;
-  const auto rt = make_rsrc(p.ve.table, p.table_bytes);
-  const int ch = threadIdx.x % CPR;
-  for (long rh = (long)blockIdx.x * (256 / CPR) + threadIdx.x / CPR; rh < nrh; rh += (long)gridDim.x * (256 / CPR)) {
-    const long row = rh / p.Hkv;
-    const int h = (int)(rh % p.Hkv);
-    const float g = ve_gate_of(p.ve, row, h);
-    float v[8], e[8];
-    unpack8(ld16((const bf16*)p.v + rh * D + 8 * ch), v);
-    unpack8(ve_chunk(p.ve, rt, p.table_bytes, row, p.Hkv, D, h, ch), e);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = __builtin_fmaf(g, e[k], v[k]);
-    st16((bf16*)p.v_mixed + rh * D + 8 * ch, pack8(v));
-    if (ch == 0) p.gate[rh] = g;
-  }
-}
+struct VeStream {
+  static constexpr int CPR = D / 8;
+  static constexpr int PPP = 256 / CPR;     // pairs per pass
+  static constexpr int U = (kVeRows * 3 + PPP - 1) / PPP;  // passes per group (one group at 3 heads)
+};
 
-// dve = g dv' and dz = <dv', ve> g (1 - g/2) per (row, head): D/8 lanes per
-// (row, head), the dot reduced over those lanes.
+// The backward of the gate, per block of kVeRows rows, in one pass:
+//  1. dve = g dv' per chunk, and dz = <dv', ve> g (1 - g/2) per (row, head)
+//     (the dot summed over the pair's lanes) into LDS;
+//  2. dx32[row][c] = sum_h dz[row][h] w[h][c];
+//  3. the block's partial dw[h][c] = sum_row dz[row][h] x[row][c]: thread
+//     (j, c) sums rows j, j + 8, ..., then the 8 row groups are added in
+//     order, and the sum is stored at part[(h * 32 + c) * nblk + block] (all
+//     blocks of one (h, c) contiguous, for the reduction; fixed order
+//     throughout: deterministic).
 template <int D>
-__global__ void __launch_bounds__(256) ve_bwd_rows_kernel(VeBwdParams p) {
-  constexpr int CPR = D / 8;
-  const long nrh = (long)p.rows * p.Hkv;
-  const auto rt = make_rsrc(p.ve.table, p.table_bytes);
-  const int ch = threadIdx.x % CPR;
-  for (long rh = (long)blockIdx.x * (256 / CPR) + threadIdx.x / CPR; rh < nrh; rh += (long)gridDim.x * (256 / CPR)) {
-    const long row = rh / p.Hkv;
-    const int h = (int)(rh % p.Hkv);
-    const float g = p.gate[rh];
-    float d[8], e[8];
-    unpack8(ld16((const bf16*)p.dv + rh * D + 8 * ch), d);
-    unpack8(ve_chunk(p.ve, rt, p.table_bytes, row, p.Hkv, D, h, ch), e);
-    float dot = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      dot = __builtin_fmaf(d[k], e[k], dot);
-      d[k] *= g;
-    }
-    st16((bf16*)p.dve + rh * D + 8 * ch, pack8(d));
-    dot = group_sum<CPR>(dot);
-    if (ch == 0) p.dz[rh] = dot * g * (1.f - 0.5f * g);
-  }
-}
-
-// Per block of kVeRows rows: dx32[row][c] = sum_h dz[row][h] w[h][c], and the
-// block's partial dw[h][c] = sum_row dz[row][h] x[row][c]. The block's x rows
-// (16-byte loads), dz and w are staged in LDS first. For dw, thread (j, c)
-// sums rows j, j + 8, ... of the block for every head; the 8 row groups are
-// then added in order (fixed order: deterministic).
-__global__ void __launch_bounds__(256) ve_bwd_gate_kernel(VeBwdParams p) {
-  static_assert(kVeRows == 64, "one 16-byte chunk of x per thread");
+__global__ void __launch_bounds__(256) ve_bwd_kernel(VeBwdParams p, int nblk) {
+  using S = VeStream<D>;
+  static_assert(4 * kVeRows <= 256 && kVeRows % 8 == 0, "one 16-byte chunk of x per thread");
   __shared__ float xs[kVeRows][33];
-  __shared__ float zs[kVeRows][kVeMaxHeads + 1];
+  __shared__ float zs[kVeRows * kVeMaxHeads];  // dz of pair i (row i / H, head i % H)
   __shared__ float wsh[kVeMaxHeads][32];
   __shared__ float acc[8][kVeMaxHeads][32];
   const int tid = threadIdx.x;
+  const int H = p.Hkv;
   const long r0 = (long)blockIdx.x * kVeRows;
   const int nr = (int)min((long)kVeRows, p.rows - r0);
-  const int H = p.Hkv;
-  {
-    const int r = tid >> 2, ch = tid & 3;
-    float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (r < nr) unpack8(ld16((const bf16*)p.ve.x + (r0 + r) * p.ve.x_stride + 8 * ch), f);
+  const long rh0 = r0 * H;
+  const int npair = nr * H;
+  // the block's x rows (first 32 channels), used after the stream
+  u32x4 xrow = {0u, 0u, 0u, 0u};
+  if ((tid >> 2) < min(nr, kVeRows)) xrow = ld16((const bf16*)p.ve.x + (r0 + (tid >> 2)) * p.ve.x_stride + 8 * (tid & 3));
+  const auto rt = make_rsrc(p.ve.table, p.table_bytes);
+  const int ch = tid % S::CPR;
+  for (int base = 0; base < npair; base += S::U * S::PPP) {
+    u32x4 dd[S::U], ee[S::U];
+    int id[S::U];
+    float g[S::U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xs[r][8 * ch + e] = f[e];
+    for (int u = 0; u < S::U; ++u) {
+      const int i = min(base + u * S::PPP + tid / S::CPR, npair - 1);  // (duplicates are not stored)
+      id[u] = p.ve.ids[r0 + i / H];
+      g[u] = p.gate[rh0 + i];
+      dd[u] = ld16((const bf16*)p.dv + (rh0 + i) * D + 8 * ch);
+    }
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const int i = min(base + u * S::PPP + tid / S::CPR, npair - 1);
+      ee[u] = ve_chunk(rt, p.table_bytes, id[u], H, D, i % H, ch);
+    }
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const int i = base + u * S::PPP + tid / S::CPR;
+      float d[8], e[8];
+      unpack8(dd[u], d);
+      unpack8(ee[u], e);
+      float dot = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        dot = __builtin_fmaf(d[k], e[k], dot);
+        d[k] *= g[u];
+      }
+      dot = group_sum<S::CPR>(dot);
+      if (i < npair) {
+        st16((bf16*)p.dve + (rh0 + i) * D + 8 * ch, pack8(d));
+        if (ch == 0) zs[i] = dot * g[u] * (1.f - 0.5f * g[u]);
+      }
+    }
   }
-  for (int e = tid; e < nr * H; e += 256) zs[e / H][e % H] = p.dz[r0 * H + e];
+  if (tid < 4 * kVeRows) {
+    float f[8];
+    unpack8(xrow, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xs[tid >> 2][8 * (tid & 3) + e] = f[e];
+  }
   for (int e = tid; e < H * 32; e += 256) wsh[e / 32][e % 32] = (float)((const bf16*)p.ve.w)[e];
   __syncthreads();
   for (int e = tid; e < nr * 32; e += 256) {
     const int r = e / 32, c = e % 32;
     float s = 0.f;
-    for (int h = 0; h < H; ++h) s = __builtin_fmaf(zs[r][h], wsh[h][c], s);
+    for (int h = 0; h < H; ++h) s = __builtin_fmaf(zs[r * H + h], wsh[h][c], s);
     p.dx32[(r0 + r) * 32 + c] = s;
   }
   const int c = tid % 32, j = tid / 32;
@@ -102,7 +113,7 @@ __global__ void __launch_bounds__(256) ve_bwd_gate_kernel(VeBwdParams p) {
 #pragma unroll
     for (int r = 0; r < kVeRows / 8; ++r) {
       const int rr = j + 8 * r;
-      if (rr < nr) s = __builtin_fmaf(zs[rr][h], xs[rr][c], s);
+      if (rr < nr) s = __builtin_fmaf(zs[rr * H + h], xs[rr][c], s);
     }
     acc[j][h][c] = s;
   }
@@ -111,66 +122,39 @@ __global__ void __launch_bounds__(256) ve_bwd_gate_kernel(VeBwdParams p) {
     const int h = e / 32, cc = e % 32;
     float s = 0.f;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) s += acc[g][h][cc];
-    p.part[(long)blockIdx.x * H * 32 + e] = s;
+    for (int q = 0; q < 8; ++q) s += acc[q][h][cc];
+    p.part[(long)e * nblk + blockIdx.x] = s;
   }
 }
 
-// dw[h][c] = sum of the blocks' partials: workgroup (h, column group cg of 8
-// columns), thread (j, c) sums blocks j, j + 32, ... (loads in groups of 8),
-// and the 32 sums are added in order (fixed order: deterministic).
-__global__ void __launch_bounds__(256) ve_bwd_reduce_kernel(VeBwdParams p, int nblk) {
-  __shared__ float acc[32][8];
-  const int h = blockIdx.x / 4, cg = blockIdx.x % 4;
-  const int c = threadIdx.x % 8, j = threadIdx.x / 8;
-  const int col = 8 * cg + c;
+// dw[e] (e = h * 32 + c) = the sum of the blocks' partials part[e * nblk ..]:
+// one wave per e; lane l adds blocks l, l + 64, ... in order, then the lanes'
+// sums are added by a fixed butterfly (fixed order: deterministic).
+__global__ void __launch_bounds__(64) ve_bwd_reduce_kernel(VeBwdParams p, int nblk) {
+  const int e = blockIdx.x, l = threadIdx.x;
+  const float* src = p.part + (long)e * nblk;
   float s = 0.f;
-  for (int k0 = j; k0 < nblk; k0 += 256) {
+  for (int k0 = l; k0 < nblk; k0 += 8 * 64) {
     float t[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int k = k0 + 32 * u;
-      t[u] = k < nblk ? p.part[((long)k * p.Hkv + h) * 32 + col] : 0.f;
-    }
+    for (int u = 0; u < 8; ++u) t[u] = k0 + 64 * u < nblk ? src[k0 + 64 * u] : 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) s += t[u];
   }
-  acc[j][c] = s;
-  __syncthreads();
-  if (j == 0) {
-    float r = 0.f;
 #pragma unroll
-    for (int g = 0; g < 32; ++g) r += acc[g][c];
-    p.dw[h * 32 + col] = r;
-  }
-}
-
-hipError_t launch_ve_prep(const VePrepParams& p, int head_dim, hipStream_t stream) {
-  const long nrh = (long)p.rows * p.Hkv;
-  const long per = 256 / (head_dim / 8);
-  const unsigned grid = (unsigned)min((nrh + per - 1) / per, 16384L);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((ve_prep_kernel<128>), dim3(grid), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((ve_prep_kernel<64>), dim3(grid), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (l == 0) p.dw[e] = s;
 }
 
 hipError_t launch_ve_bwd(const VeBwdParams& p, int head_dim, hipStream_t stream) {
-  const long nrh = (long)p.rows * p.Hkv;
-  const long per = 256 / (head_dim / 8);
-  const unsigned grid = (unsigned)min((nrh + per - 1) / per, 16384L);
+  const int nblk = (int)((p.rows + kVeRows - 1) / kVeRows);
   if (head_dim == 128)
-    hipLaunchKernelGGL((ve_bwd_rows_kernel<128>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ve_bwd_kernel<128>), dim3((unsigned)nblk), dim3(256), 0, stream, p, nblk);
   else
-    hipLaunchKernelGGL((ve_bwd_rows_kernel<64>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ve_bwd_kernel<64>), dim3((unsigned)nblk), dim3(256), 0, stream, p, nblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nblk = (int)((p.rows + kVeRows - 1) / kVeRows);
-  hipLaunchKernelGGL(ve_bwd_gate_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ve_bwd_reduce_kernel, dim3((unsigned)(p.Hkv * 4)), dim3(256), 0, stream, p, nblk);
+  hipLaunchKernelGGL(ve_bwd_reduce_kernel, dim3((unsigned)(p.Hkv * 32)), dim3(64), 0, stream, p, nblk);
   return hipGetLastError();
 }
 

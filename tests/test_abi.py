@@ -248,7 +248,7 @@ def test_value_embedding_validation_paths(sa):
     B, T, Hq, Hkv, D = 1, 8, 4, 2, 64
     r256 = lambda x: (x + 255) // 256 * 256
     rh = B * T * Hkv
-    assert lib.sa_attn_ve_workspace_bytes(B, T, Hkv, D) == r256(rh * D * 2) + 2 * r256(rh * 4) + r256(1 * Hkv * 32 * 4)
+    assert lib.sa_attn_ve_workspace_bytes(B, T, Hkv, D) == r256(rh * D * 2) + r256(rh * 4) + r256(1 * Hkv * 32 * 4)
 
     def fwd(x=4096, xs=768, w=8192, ids=12288, tab=16384, vocab=100, norm=1):
         ws = lib.sa_attn_fwd_workspace_bytes(B, T, Hq, Hkv, D)

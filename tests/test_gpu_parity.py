@@ -331,6 +331,7 @@ VE_CASES = [
     (1, 513, 6, 3, 128, 256, 500, True),     # with the rotary tables as well
     (1, 400, 6, 6, 64, 100, 64, False),      # MHA, D = 64
     (2, 129, 3, 1, 128, 0, 31, False),       # G = 3, window 0
+    (1, 130, 16, 16, 128, 64, 20, False),    # 16 KV heads: several load groups per block of rows
 ]
 
 
