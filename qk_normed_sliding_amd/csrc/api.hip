@@ -517,6 +517,29 @@ int polar_splits(long jobs, int K) {
   return best;
 }
 
+// Tile of an unsplit polar-express product C [M][N] (K a multiple of 128): the shape whose
+// rounds of workgroups (two per compute unit) take the least time, a round's time taken as
+// the tile's area over its relative rate per element, measured on B X at m = 768 (K = 768):
+// 128 x 128 1 (19.3 us per round), 96 x 128 0.81 (B given as [K][N] only; 17.9 us),
+// 192 x 192 0.85 (50.9 us).
+int polar_tile(int batch, int M, int N, bool b_kn, bool sym) {
+  const long slots = 2L * cu_count();
+  int best = 128;
+  double best_cost = 0.0;
+  for (int t : {128, 96, 192}) {
+    const int tn = t == 192 ? 192 : 128;
+    if (M % t != 0 || N % tn != 0 || (t == 96 && (!b_kn || sym))) continue;
+    const long tiles = (long)batch * sa::gemm_tiles(M, N, sym, t, tn);
+    const double rate = t == 128 ? 1.0 : (t == 96 ? 0.81 : 0.85);
+    const double cost = (double)((tiles + slots - 1) / slots) * t * tn / rate;
+    if (t == 128 || cost < best_cost) {
+      best = t;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 // The two symmetric products of a step on [m][n] matrices: A = X X^T (K = n)
 // and A A (K = m), both with upper tiles only; their splits and the floats
 // of split partials they need.
@@ -580,14 +603,16 @@ SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, siz
     const float* nsum = k == 0 ? part : nullptr;
     // A = X X^T (symmetric: upper tiles only); X = G / (||G|| + eps) on the first step
     sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f, 1, pl.s_xx, kpart, nsum, 2, eps};
-    if (sa::launch_gemm(pg, false, batch, s) != hipSuccess) return SA_ERR_HIP;
+    if (sa::launch_gemm(pg, false, batch, s, pl.s_xx > 1 ? 128 : polar_tile(batch, m, m, false, true)) != hipSuccess)
+      return SA_ERR_HIP;
     // B = c A A + b A  (A is symmetric: A A = A A^T, and so is B)
     sa::GemmParams pb{A, A, A, Bm, m, m, m, c, b, 1, pl.s_aa, kpart};
-    if (sa::launch_gemm(pb, false, batch, s) != hipSuccess) return SA_ERR_HIP;
+    if (sa::launch_gemm(pb, false, batch, s, pl.s_aa > 1 ? 128 : polar_tile(batch, m, m, false, true)) != hipSuccess)
+      return SA_ERR_HIP;
     // X <- B X + a X, straight into the output on the last step of a wide matrix
     void* dst = (k == steps - 1 && !tall) ? out : bufs[k % 2];
     sa::GemmParams px{Bm, cur, cur, dst, m, n, m, 1.f, a, 0, 0, nullptr, nsum, 1, eps};
-    if (sa::launch_gemm(px, true, batch, s) != hipSuccess) return SA_ERR_HIP;
+    if (sa::launch_gemm(px, true, batch, s, polar_tile(batch, m, n, true, false)) != hipSuccess) return SA_ERR_HIP;
     cur = bufs[k % 2];
   }
   if (tall && sa::launch_transpose(cur, out, batch, m, n, s) != hipSuccess) return SA_ERR_HIP;

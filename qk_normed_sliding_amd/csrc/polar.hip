@@ -10,7 +10,11 @@
 // accumulation, C = alpha A op(B) + beta C0, op(B) = B^T ("bt": B given as
 // [N][K], both operands read along K) or B ("bn": B given as [K][N], read
 // with LDS transpose reads). A 256-thread workgroup owns a 128 x 128 tile of
-// C (a 64 x 64 quarter per wave, 2 x 2 blocks of 32 x 32); K advances in
+// C (a 64 x 64 quarter per wave, 2 x 2 blocks of 32 x 32), or (bn only) a
+// 96 x 128 tile (a 96 x 32 column strip per wave, 3 blocks), which the host
+// picks when its tile count fills the compute units' workgroup slots in
+// fewer rounds of work (at m = 768: 1536 tiles, three full rounds of 512,
+// against 1152 tiles of 128 x 128 in two and a quarter); K advances in
 // steps of 64 through two LDS stages filled by direct buffer-to-LDS copies,
 // XOR-swizzled so that the operand reads are bank-conflict free. The MFMA
 // takes the N-side operand first, so each lane's accumulators hold one row of
@@ -69,9 +73,12 @@ __device__ __forceinline__ void gemm_scales(const GemmParams& p, long bz, float&
   }
 }
 
-template <bool BN>
+template <bool BN, int TM>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
-  constexpr int TM = 128, TN = 128, TK = 64;
+  constexpr int TN = 128, TK = 64;
+  static_assert(TM == 128 || (TM == 96 && BN), "128 x 128 tiles, or 96 x 128 with B given as [K][N]");
+  constexpr int MB = TM == 128 ? 2 : 3;  // 32-row blocks per wave
+  constexpr int NB = TM == 128 ? 2 : 1;  // 32-column blocks per wave
   __shared__ __attribute__((aligned(1024))) bf16 As[2][TM * TK];  // [m][k], 8 chunks per row
   __shared__ __attribute__((aligned(1024))) bf16 Bs[2][TN * TK];  // bt: [n][k] (8 chunks); bn: [k][n] (16 chunks)
 
@@ -80,14 +87,15 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   const int w = uniform(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int wm = w >> 1, wn = w & 1;  // this wave's 64 x 64 quarter of the tile
+  // this wave's part of the tile: row blocks MB wm .., column blocks NB wn ..
+  const int wm = TM == 128 ? w >> 1 : 0, wn = TM == 128 ? w & 1 : w;
   const int tiles_n = p.N / TN;
   const int splits = p.splits > 1 ? p.splits : 1;
   // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
   // work item w = (matrix, tile, split) in that order goes to the XCD that
   // runs a contiguous range of items, so the tiles of a matrix, which share
   // its row and column panels, meet in one L2.
-  const int per_mat = gemm_tiles(p.M, p.N, p.sym) * splits;
+  const int per_mat = gemm_tiles(p.M, p.N, p.sym, TM) * splits;
   const int w_item = xcd_item((int)blockIdx.x, (int)gridDim.x);
   const int tile = (w_item % per_mat) / splits, sp = w_item % splits;
   int tm, tn;
@@ -103,7 +111,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   const u32x4 rb = rsrc_words(B, (uint32_t)(p.N * p.K * 2));
 
   // Copies: instruction j of wave w fills the 1 KB block blk = 4j + w of a
-  // tile. [x][k] tiles (8 chunks per row): rows 8 blk + lane/8; the row's
+  // tile (A: TM / 8 blocks). [x][k] tiles (8 chunks per row): rows 8 blk + lane/8; the row's
   // swizzle depends on blk only through its parity, which is w's. [k][n]
   // tiles (16 chunks per row): rows 4 blk + lane/16; swizzle from blk mod 4 = w.
   uint32_t oa, ob;
@@ -124,7 +132,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int blk = 4 * j + w;
-      dma16(ra, uniform((int)(la + blk * 1024)), oa + (uint32_t)(((m0 + 8 * blk) * p.K + k0) * 2), 0u);
+      if (j < TM / 32) dma16(ra, uniform((int)(la + blk * 1024)), oa + (uint32_t)(((m0 + 8 * blk) * p.K + k0) * 2), 0u);
       if constexpr (BN)
         dma16(rb, uniform((int)(lb + blk * 1024)), ob + (uint32_t)(((k0 + 4 * blk) * p.N + n0) * 2), 0u);
       else
@@ -155,11 +163,11 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     return cat(lo, hi);
   };
 
-  f32x16 acc[2][2];  // [n block][m block]: register 4i + j of lane l = C[row l32][column 8i + 4half + j]
+  f32x16 acc[NB][MB];  // [n block][m block]: register 4i + j of lane l = C[row l32][column 8i + 4half + j]
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < NB; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < MB; ++y)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
@@ -173,23 +181,25 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     if (ks + 1 < nk) issue(ks + 1, st ^ 1);  // the other stage was last read before the previous barrier
     const uint32_t la = lds_addr(&As[st][0]);
     const uint32_t lb = lds_addr(&Bs[st][0]);
-    bf16x8 bo[4][2], ao[4][2];
+    bf16x8 bo[4][MB], ao[4][NB];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        bo[kk][x] = row_op(la, 2 * wm + x, kk);
+      for (int y = 0; y < MB; ++y) bo[kk][y] = row_op(la, MB * wm + y, kk);
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
         if constexpr (BN)
-          ao[kk][x] = tr_op(lb, 2 * wn + x, kk);
+          ao[kk][x] = tr_op(lb, NB * wn + x, kk);
         else
-          ao[kk][x] = row_op(lb, 2 * wn + x, kk);
+          ao[kk][x] = row_op(lb, NB * wn + x, kk);
       }
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < NB; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = mfma32(ao[kk][x], bo[kk][y], acc[x][y]);
+        for (int y = 0; y < MB; ++y) acc[x][y] = mfma32(ao[kk][x], bo[kk][y], acc[x][y]);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next stage have landed
     __syncthreads();
   }
@@ -197,12 +207,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   if (splits > 1) {  // fp32 partial tile, row-major 128 x 128
     float* dst = p.part + (((long)bz * splits + sp) * gemm_tiles(p.M, p.N, p.sym) + tile) * (TM * TN);
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < MB; ++y)
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < NB; ++x)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 32 * (2 * wm + y) + l32, c = 32 * (2 * wn + x) + 8 * i + 4 * half;
+          const int r = 32 * (MB * wm + y) + l32, c = 32 * (NB * wn + x) + 8 * i + 4 * half;
           *(f32x4*)(dst + r * TN + c) = f32x4{acc[x][y][4 * i], acc[x][y][4 * i + 1], acc[x][y][4 * i + 2],
                                              acc[x][y][4 * i + 3]};
         }
@@ -217,13 +227,13 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   float al, be;
   gemm_scales(p, bz, al, be);
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
-    const long row = m0 + 32 * (2 * wm + y) + l32;
+  for (int y = 0; y < MB; ++y) {
+    const long row = m0 + 32 * (MB * wm + y) + l32;
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int x = 0; x < NB; ++x)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const long off = cbase + row * p.N + n0 + 32 * (2 * wn + x) + 8 * i + 4 * half;
+        const long off = cbase + row * p.N + n0 + 32 * (NB * wn + x) + 8 * i + 4 * half;
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = al * acc[x][y][4 * i + j];
@@ -239,7 +249,182 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
         o[1] = pack2(v[2], v[3]);
         *(u32x2*)((bf16*)p.c + off) = o;
         if (mirror) {
-          const long col = n0 + 32 * (2 * wn + x) + 8 * i + 4 * half;
+          const long col = n0 + 32 * (NB * wn + x) + 8 * i + 4 * half;
+          unsigned short* mc = (unsigned short*)p.c + cbase + col * p.M + row;
+          mc[0] = (unsigned short)(o[0] & 0xffffu);
+          mc[p.M] = (unsigned short)(o[0] >> 16);
+          mc[2L * p.M] = (unsigned short)(o[1] & 0xffffu);
+          mc[3L * p.M] = (unsigned short)(o[1] >> 16);
+        }
+      }
+  }
+}
+
+// The 192 x 192 tile: four waves, each a 96 x 96 quarter (3 x 3 blocks of
+// 32 x 32, nine accumulators), K in steps of 32 through three LDS stages
+// (copies two steps ahead), two workgroups per compute unit. Per byte
+// copied into LDS it does 1.5 times the MFMA work of the 128 x 128 tile,
+// and at m = 768 its tile count matches the workgroup slots (512 per
+// product of the trainer's groups: one full round).
+// LDS: [x][k] operand tiles are 192 rows of 64 bytes (4 chunks), chunk j of
+// row r at j ^ ((r >> 2) & 3), so that the 16 rows a read serves per pass
+// at one logical chunk land on 16 distinct 16-byte bank groups. A [k][n]
+// tile (B given as [K][N]) is three 64-column sub-tiles of 32 rows of 128
+// bytes, swizzled as the 8-chunk rows above and read with transpose reads.
+template <bool BN>
+__global__ void __launch_bounds__(256, 2) gemm192_kernel(GemmParams p) {
+  constexpr int T = 192, TK = 32, NST = 3;
+  constexpr int SE = T * TK;  // elements per operand stage
+  __shared__ __attribute__((aligned(1024))) bf16 As[NST][SE];
+  __shared__ __attribute__((aligned(1024))) bf16 Bs[NST][SE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int wm = w >> 1, wn = w & 1;  // row blocks 3 wm .., column blocks 3 wn ..
+  const int tiles_n = p.N / T;
+  const int per_mat = gemm_tiles(p.M, p.N, p.sym, T, T);
+  const int w_item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+  const int tile = w_item % per_mat;
+  int tm, tn;
+  tile_of(tile, tiles_n, p.sym, tm, tn);
+  const int m0 = tm * T;
+  const int n0 = tn * T;
+  const long bz = w_item / per_mat;
+
+  const bf16* A = (const bf16*)p.a + bz * p.M * p.K;
+  const bf16* B = (const bf16*)p.b + bz * p.N * p.K;
+  const u32x4 ra = rsrc_words(A, (uint32_t)(p.M * p.K * 2));
+  const u32x4 rb = rsrc_words(B, (uint32_t)(p.N * p.K * 2));
+
+  // Copies: instruction j (0..2) of wave w fills the 1 KB block blk = 4j + w
+  // of each operand stage. [x][k]: rows 16 blk + lane/4, the lane's LDS chunk
+  // lane % 4 holding global chunk (lane % 4) ^ ((lane >> 4) & 3) (the row's
+  // swizzle: (row >> 2) & 3 = (lane >> 4) & 3). [k][n]: sub-tile j, k-rows
+  // 8w + lane/8, LDS chunk lane % 8 holding column chunk (lane % 8) ^ swz<8>(row).
+  const uint32_t ox = (uint32_t)((lane / 4) * p.K + 8 * ((lane & 3) ^ ((lane >> 4) & 3))) * 2;
+  uint32_t obn = 0;
+  if constexpr (BN) {
+    const int kr = 8 * w + lane / 8;
+    obn = (uint32_t)((lane / 8) * p.N + 8 * ((lane & 7) ^ swz<8>(kr))) * 2;
+  }
+  auto issue = [&](int ks, int st) {
+    const int k0 = ks * TK;
+    const uint32_t la = lds_addr(&As[st][0]);
+    const uint32_t lb = lds_addr(&Bs[st][0]);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int blk = 4 * j + w;
+      dma16(ra, uniform((int)(la + blk * 1024)), ox + (uint32_t)(((m0 + 16 * blk) * p.K + k0) * 2), 0u);
+      if constexpr (BN)
+        dma16(rb, uniform((int)(lb + blk * 1024)), obn + (uint32_t)(((k0 + 8 * w) * p.N + n0 + 64 * j) * 2), 0u);
+      else
+        dma16(rb, uniform((int)(lb + blk * 1024)), ox + (uint32_t)(((n0 + 16 * blk) * p.K + k0) * 2), 0u);
+    }
+  };
+
+  // Row reads of [x][k] tiles: row 32 blk + l32, chunk 2 kk + half (k = 16 kk
+  // + 8 half + e). Transpose reads of the [k][n] tile: column block cb (32
+  // columns) is half cb % 2 of sub-tile cb / 2; rows 16 kk + 8 half + tq (+4),
+  // columns 16 g1 + 4 qq of the block; lane l receives column l32 of the
+  // block at k = 16 kk + 8 half + e, the same K order as the row reads.
+  auto row_op = [&](uint32_t base, int blk, int kk) {
+    const int r = 32 * blk + l32;
+    return *(SA_LDS const bf16x8*)(uintptr_t)(base + (uint32_t)(r * 64 + (((2 * kk + half) ^ ((r >> 2) & 3)) << 4)));
+  };
+  uint32_t trb[2] = {0u, 0u};
+  if constexpr (BN) {
+    const int tq = (lane >> 2) & 3, g1 = (lane >> 4) & 1, qq = lane & 3;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) trb[hi] = (uint32_t)swz_off<8>(8 * half + tq + 4 * hi, 16 * g1 + 4 * qq) * 2;
+  }
+  auto tr_op = [&](uint32_t base, int cb, int kk) {
+    const uint32_t rbase = base + (uint32_t)((cb >> 1) * 4096 + kk * 16 * 128);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (SA_LDS bf16x4*)(uintptr_t)(rbase + (trb[0] ^ (uint32_t)((cb & 1) << 6))));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (SA_LDS bf16x4*)(uintptr_t)(rbase + (trb[1] ^ (uint32_t)((cb & 1) << 6))));
+    return cat(lo, hi);
+  };
+
+  f32x16 acc[3][3];  // [n block][m block]: register 4i + j of lane l = C[row l32][column 8i + 4half + j]
+#pragma unroll
+  for (int x = 0; x < 3; ++x)
+#pragma unroll
+    for (int y = 0; y < 3; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+
+  const int nk = p.K / TK;
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  int st = 0;
+#pragma clang loop unroll(disable)
+  for (int ks = 0; ks < nk; ++ks) {
+    // this wave's copies of step ks have landed (those of step ks + 1, six
+    // instructions, may still be in flight); after the barrier every wave's
+    // have, and every wave has finished step ks - 1, whose stage the copies
+    // of step ks + 2 overwrite
+    if (ks + 1 < nk)
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ks + 2 < nk) issue(ks + 2, st == 0 ? 2 : st - 1);
+    const uint32_t la = lds_addr(&As[st][0]);
+    const uint32_t lb = lds_addr(&Bs[st][0]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 bo[3], ao[3];
+#pragma unroll
+      for (int y = 0; y < 3; ++y) bo[y] = row_op(la, 3 * wm + y, kk);
+#pragma unroll
+      for (int x = 0; x < 3; ++x) {
+        if constexpr (BN)
+          ao[x] = tr_op(lb, 3 * wn + x, kk);
+        else
+          ao[x] = row_op(lb, 3 * wn + x, kk);
+      }
+#pragma unroll
+      for (int x = 0; x < 3; ++x)
+#pragma unroll
+        for (int y = 0; y < 3; ++y) acc[x][y] = mfma32(ao[x], bo[y], acc[x][y]);
+    }
+    st = st == 2 ? 0 : st + 1;
+  }
+
+  // epilogue: C = alpha acc + beta C0 (bf16), mirrored for an off-diagonal
+  // tile of a symmetric product, as in gemm_kernel
+  const long cbase = bz * p.M * p.N;
+  const bool mirror = p.sym && tm != tn;
+  float al, be;
+  gemm_scales(p, bz, al, be);
+#pragma unroll
+  for (int y = 0; y < 3; ++y) {
+    const long row = m0 + 32 * (3 * wm + y) + l32;
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long col = n0 + 32 * (3 * wn + x) + 8 * i + 4 * half;
+        const long off = cbase + row * p.N + col;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = al * acc[x][y][4 * i + j];
+        if (p.c0 != nullptr) {
+          const u32x2 c0 = *(const u32x2*)((const bf16*)p.c0 + off);
+          v[0] += be * __uint_as_float(c0[0] << 16);
+          v[1] += be * __uint_as_float(c0[0] & 0xffff0000u);
+          v[2] += be * __uint_as_float(c0[1] << 16);
+          v[3] += be * __uint_as_float(c0[1] & 0xffff0000u);
+        }
+        u32x2 o;
+        o[0] = pack2(v[0], v[1]);
+        o[1] = pack2(v[2], v[3]);
+        *(u32x2*)((bf16*)p.c + off) = o;
+        if (mirror) {
           unsigned short* mc = (unsigned short*)p.c + cbase + col * p.M + row;
           mc[0] = (unsigned short)(o[0] & 0xffffu);
           mc[p.M] = (unsigned short)(o[0] >> 16);
@@ -346,14 +531,26 @@ __global__ void __launch_bounds__(256) transpose_kernel(const bf16* in, bf16* ou
   }
 }
 
-hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream) {
+hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream, int tile) {
   const int splits = p.splits > 1 ? p.splits : 1;
-  const int ntile = gemm_tiles(p.M, p.N, p.sym);
+  if (tile == 192) {
+    if (splits > 1 || p.M % 192 != 0 || p.N % 192 != 0 || p.K % 32 != 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(gemm_tiles(p.M, p.N, p.sym, 192, 192) * batch));
+    if (b_kn)
+      hipLaunchKernelGGL((gemm192_kernel<true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm192_kernel<false>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (tile != 128 && (tile != 96 || !b_kn || splits > 1 || p.sym || p.M % 96 != 0)) return hipErrorInvalidValue;
+  const int ntile = gemm_tiles(p.M, p.N, p.sym, tile);
   const dim3 grid((unsigned)(ntile * splits * batch));
-  if (b_kn)
-    hipLaunchKernelGGL((gemm_kernel<true>), grid, dim3(256), 0, stream, p);
+  if (tile == 96)
+    hipLaunchKernelGGL((gemm_kernel<true, 96>), grid, dim3(256), 0, stream, p);
+  else if (b_kn)
+    hipLaunchKernelGGL((gemm_kernel<true, 128>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_kernel<false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_kernel<false, 128>), grid, dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(ntile * 16), (unsigned)batch), dim3(256), 0, stream, p);

@@ -130,9 +130,10 @@ struct GemmParams {
   int npow;
   float neps;
 };
-// Tiles of C that a GEMM computes (all, or those on and above the diagonal).
-__host__ __device__ inline int gemm_tiles(int M, int N, int sym) {
-  const int tm = M / 128, tn = N / 128;
+// Tiles of C that a GEMM computes (all, or those on and above the diagonal; tile_m x tile_n
+// tiles, square when symmetric).
+__host__ __device__ inline int gemm_tiles(int M, int N, int sym, int tile_m = 128, int tile_n = 128) {
+  const int tm = M / tile_m, tn = N / tile_n;
   return sym ? tm * (tm + 1) / 2 : tm * tn;
 }
 constexpr int kFroChunks = 64;  // partial sums per matrix of the Frobenius norm
@@ -157,10 +158,11 @@ hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stre
 // With ve: the same launch also writes the value-embedding mix v' and the gate.
 hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev,
                          const VePrepParams* ve = nullptr);
-// Polar-express pieces: GEMM (b_kn: B given as [K][N]), partial sums of
+// Polar-express pieces: GEMM (b_kn: B given as [K][N]; tile: 128 (128 x 128), 96 (96 x 128, b_kn
+// only, unsplit) or 192 (192 x 192, unsplit; M, N multiples of 192, K of 32)), partial sums of
 // squares for ||X||_F per matrix (part: batch * kFroChunks floats), and
 // per-matrix transpose [R][C] -> [C][R].
-hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream);
+hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream, int tile = 128);
 hipError_t launch_fro_sumsq(const void* x, float* part, int batch, long per_matrix, hipStream_t stream);
 hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, hipStream_t stream);
 // Value-embedding gate backward: dve, dx32 and dw from dL/dv' (v' and g come from the norm pass).

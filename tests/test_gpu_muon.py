@@ -64,15 +64,16 @@ def _check(sa, g, steps=5, idx=None):
 # K is split in ranges of at least 1024: (1, 128, 2048): one tile, the
 # Gram's K split in 2; (1, 256, 2048): split in 2 with a mirrored
 # off-diagonal tile; (2, 512, 3072): Gram split in 3; (1, 2048, 2048): the
-# Gram and A A both split in 2, with mirrored tiles
+# Gram and A A both split in 2, with mirrored tiles; (1, 384, 640) and
+# (2, 1152, 384): B X in 96-row tiles (m = 384)
 @pytest.mark.parametrize("shape", [(3, 256, 384), (2, 384, 256), (2, 256, 256), (1, 128, 2048), (1, 256, 2048),
-                                   (2, 512, 3072), (1, 2048, 2048)])
+                                   (2, 512, 3072), (1, 2048, 2048), (1, 384, 640), (2, 1152, 384)])
 def test_polar_express_small(sa, shape):
     log(f"[polar] {shape}")
     _check(sa, _grad(shape, 300 + shape[1]))
 
 
-@pytest.mark.parametrize("shape", [(1, 2048, 2048), (2, 512, 3072), (1, 256, 2048), (2, 384, 256)])
+@pytest.mark.parametrize("shape", [(1, 2048, 2048), (2, 512, 3072), (1, 256, 2048), (2, 384, 256), (1, 384, 640)])
 def test_polar_express_one_step_tiles(sa, shape):
     """One step, where the per-tile bound is tight (1e-2): the symmetric
     products' mirrored tiles and the split-K reductions (K = 2048: A = X X^T
