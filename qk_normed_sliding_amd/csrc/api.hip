@@ -523,15 +523,15 @@ int polar_splits(long jobs, int K) {
 // 128 x 128 1 (19.3 us per round), 96 x 128 0.81 (B given as [K][N] only; 17.9 us),
 // 192 x 192 0.85 (50.9 us).
 int polar_tile(int batch, int M, int N, bool b_kn, bool sym) {
-  const long slots = 2L * cu_count();
   int best = 128;
   double best_cost = 0.0;
+  const long slots = 2L * cu_count();
   for (int t : {128, 96, 192}) {
-    const int tn = t == 192 ? 192 : 128;
-    if (M % t != 0 || N % tn != 0 || (t == 96 && (!b_kn || sym))) continue;
-    const long tiles = (long)batch * sa::gemm_tiles(M, N, sym, t, tn);
+    const int tm = t, tn = t == 192 ? 192 : 128;
+    if (M % tm != 0 || N % tn != 0 || (t == 96 && (!b_kn || sym))) continue;
+    const long tiles = (long)batch * sa::gemm_tiles(M, N, sym, tm, tn);
     const double rate = t == 128 ? 1.0 : (t == 96 ? 0.81 : 0.85);
-    const double cost = (double)((tiles + slots - 1) / slots) * t * tn / rate;
+    const double cost = (double)((tiles + slots - 1) / slots) * tm * tn / rate;
     if (t == 128 || cost < best_cost) {
       best = t;
       best_cost = cost;

@@ -73,6 +73,55 @@ __device__ __forceinline__ void gemm_scales(const GemmParams& p, long bz, float&
   }
 }
 
+// Epilogue of 32-row block y of a wave's part of C: C = alpha acc + beta C0
+// (bf16) over NB column blocks of 32 (column col0 + 32 x + 8 i .. + 3 from
+// register quad i of acc[x][y]). All of the block's C0 values are loaded
+// before its first store: one memory round trip per block of rows rather
+// than one per value (the stores could alias C0 as far as the compiler
+// knows, so it would not move later loads above them). An off-diagonal tile
+// of a symmetric product also goes to its mirror position, where 32 lanes
+// store 32 consecutive elements of a row per instruction.
+template <int NB, int MB>
+__device__ __forceinline__ void gemm_store_rows(const GemmParams& p, long cbase, long row, long col0,
+                                                const f32x16 (&acc)[NB][MB], int y, float al, float be,
+                                                bool mirror) {
+  u32x2 c0v[NB][4];
+#pragma unroll
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c0v[x][i] = u32x2{0u, 0u};
+  if (p.c0 != nullptr) {
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        c0v[x][i] = *(const u32x2*)((const bf16*)p.c0 + cbase + row * p.N + col0 + 32 * x + 8 * i);
+  }
+#pragma unroll
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long col = col0 + 32 * x + 8 * i;
+      const u32x2 c0 = c0v[x][i];
+      float v[4];
+      v[0] = al * acc[x][y][4 * i + 0] + be * __uint_as_float(c0[0] << 16);
+      v[1] = al * acc[x][y][4 * i + 1] + be * __uint_as_float(c0[0] & 0xffff0000u);
+      v[2] = al * acc[x][y][4 * i + 2] + be * __uint_as_float(c0[1] << 16);
+      v[3] = al * acc[x][y][4 * i + 3] + be * __uint_as_float(c0[1] & 0xffff0000u);
+      u32x2 o;
+      o[0] = pack2(v[0], v[1]);
+      o[1] = pack2(v[2], v[3]);
+      *(u32x2*)((bf16*)p.c + cbase + row * p.N + col) = o;
+      if (mirror) {
+        unsigned short* mc = (unsigned short*)p.c + cbase + col * p.M + row;
+        mc[0] = (unsigned short)(o[0] & 0xffffu);
+        mc[p.M] = (unsigned short)(o[0] >> 16);
+        mc[2L * p.M] = (unsigned short)(o[1] & 0xffffu);
+        mc[3L * p.M] = (unsigned short)(o[1] >> 16);
+      }
+    }
+}
+
 template <bool BN, int TM>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   constexpr int TN = 128, TK = 64;
@@ -219,45 +268,14 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     return;
   }
 
-  // epilogue: C = alpha acc + beta C0 (bf16); an off-diagonal tile of a
-  // symmetric product also goes to its mirror position, where 32 lanes
-  // store 32 consecutive elements of a row per instruction
+  // epilogue: C = alpha acc + beta C0 (bf16), mirrored for an off-diagonal tile of a symmetric product
   const long cbase = bz * p.M * p.N;
-  const bool mirror = p.sym && tm != tn;
   float al, be;
   gemm_scales(p, bz, al, be);
 #pragma unroll
-  for (int y = 0; y < MB; ++y) {
-    const long row = m0 + 32 * (MB * wm + y) + l32;
-#pragma unroll
-    for (int x = 0; x < NB; ++x)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const long off = cbase + row * p.N + n0 + 32 * (NB * wn + x) + 8 * i + 4 * half;
-        float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = al * acc[x][y][4 * i + j];
-        if (p.c0 != nullptr) {
-          const u32x2 c0 = *(const u32x2*)((const bf16*)p.c0 + off);
-          v[0] += be * __uint_as_float(c0[0] << 16);
-          v[1] += be * __uint_as_float(c0[0] & 0xffff0000u);
-          v[2] += be * __uint_as_float(c0[1] << 16);
-          v[3] += be * __uint_as_float(c0[1] & 0xffff0000u);
-        }
-        u32x2 o;
-        o[0] = pack2(v[0], v[1]);
-        o[1] = pack2(v[2], v[3]);
-        *(u32x2*)((bf16*)p.c + off) = o;
-        if (mirror) {
-          const long col = n0 + 32 * (NB * wn + x) + 8 * i + 4 * half;
-          unsigned short* mc = (unsigned short*)p.c + cbase + col * p.M + row;
-          mc[0] = (unsigned short)(o[0] & 0xffffu);
-          mc[p.M] = (unsigned short)(o[0] >> 16);
-          mc[2L * p.M] = (unsigned short)(o[1] & 0xffffu);
-          mc[3L * p.M] = (unsigned short)(o[1] >> 16);
-        }
-      }
-  }
+  for (int y = 0; y < MB; ++y)
+    gemm_store_rows(p, cbase, m0 + 32 * (MB * wm + y) + l32, n0 + 32 * NB * wn + 4 * half, acc, y, al, be,
+                    p.sym && tm != tn);
 }
 
 // The 192 x 192 tile: four waves, each a 96 x 96 quarter (3 x 3 blocks of
@@ -395,44 +413,14 @@ __global__ void __launch_bounds__(256, 2) gemm192_kernel(GemmParams p) {
     st = st == 2 ? 0 : st + 1;
   }
 
-  // epilogue: C = alpha acc + beta C0 (bf16), mirrored for an off-diagonal
-  // tile of a symmetric product, as in gemm_kernel
+  // epilogue: C = alpha acc + beta C0 (bf16), mirrored for an off-diagonal tile of a symmetric product
   const long cbase = bz * p.M * p.N;
-  const bool mirror = p.sym && tm != tn;
   float al, be;
   gemm_scales(p, bz, al, be);
 #pragma unroll
-  for (int y = 0; y < 3; ++y) {
-    const long row = m0 + 32 * (3 * wm + y) + l32;
-#pragma unroll
-    for (int x = 0; x < 3; ++x)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const long col = n0 + 32 * (3 * wn + x) + 8 * i + 4 * half;
-        const long off = cbase + row * p.N + col;
-        float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = al * acc[x][y][4 * i + j];
-        if (p.c0 != nullptr) {
-          const u32x2 c0 = *(const u32x2*)((const bf16*)p.c0 + off);
-          v[0] += be * __uint_as_float(c0[0] << 16);
-          v[1] += be * __uint_as_float(c0[0] & 0xffff0000u);
-          v[2] += be * __uint_as_float(c0[1] << 16);
-          v[3] += be * __uint_as_float(c0[1] & 0xffff0000u);
-        }
-        u32x2 o;
-        o[0] = pack2(v[0], v[1]);
-        o[1] = pack2(v[2], v[3]);
-        *(u32x2*)((bf16*)p.c + off) = o;
-        if (mirror) {
-          unsigned short* mc = (unsigned short*)p.c + cbase + col * p.M + row;
-          mc[0] = (unsigned short)(o[0] & 0xffffu);
-          mc[p.M] = (unsigned short)(o[0] >> 16);
-          mc[2L * p.M] = (unsigned short)(o[1] & 0xffffu);
-          mc[3L * p.M] = (unsigned short)(o[1] >> 16);
-        }
-      }
-  }
+  for (int y = 0; y < 3; ++y)
+    gemm_store_rows(p, cbase, m0 + 32 * (3 * wm + y) + l32, n0 + 32 * 3 * wn + 4 * half, acc, y, al, be,
+                    p.sym && tm != tn);
 }
 
 // Split-K reduction: the 32 x 32 block blockIdx.x % 16 of computed tile
