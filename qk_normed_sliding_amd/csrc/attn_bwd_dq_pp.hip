@@ -292,7 +292,6 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
         tab[m][3] = __builtin_bit_cast(f32x4, bload16(rs, off + 16));
       }
     }
-    bf16* qh = (bf16*)p.qhat + first;
 #pragma unroll
     for (int m = 0; m < QM; ++m) {
       const int r = QRPI * m + crow;  // row within the wave's 32
@@ -323,7 +322,6 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= rr;
       const u32x4 w = pack8(f);
-      if (norm && r0 + r < T) st16(qh + (long)(r0 + r) * qstride + 8 * cch, w);
       const uint32_t at = stage + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4));
       *(SA_LDS u32x4*)(uintptr_t)at = norm ? w : xq[m];
       if (cch == 0) {
@@ -339,6 +337,24 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
       qf[kk] = *(SA_LDS const bf16x8*)(uintptr_t)(rbase + (uint32_t)((((2 * kk + half) ^ (l32 % CPR))) << 4));
     r_q = scal[l32];
     delta = scal[32 + l32];
+    lse2 = row < T ? lse_raw * kLog2e : INFINITY;
+    if (half == 0 && row < T) {
+      p.delta[lrow] = delta;
+      p.lse2[lrow] = lse2;  // for the dK/dV kernel's probabilities
+    }
+    // the q_hat rows for the dK/dV kernel, read back from the staging area, as
+    // the last memory operations of the prologue (rows at or past T are dropped
+    // by the buffer's range): the wait below then covers the row loads and the
+    // first tiles but not these stores
+    if (norm) {
+      const auto rqh = make_rsrc((bf16*)p.qhat + first, bytes);
+#pragma unroll
+      for (int m = 0; m < QM; ++m) {
+        const int r = QRPI * m + crow;
+        const u32x4 w = *(SA_LDS const u32x4*)(uintptr_t)(stage + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4)));
+        bstore16(rqh, (uint32_t)((r0 + r) * qstride + 8 * cch) * 2, w);
+      }
+    }
 #pragma unroll
     for (int m = 0; m < QM; ++m) {
       const int r = QRPI * m + crow;
@@ -347,13 +363,12 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk)
       df[kk] = *(SA_LDS const bf16x8*)(uintptr_t)(rbase + (uint32_t)((((2 * kk + half) ^ (l32 % CPR))) << 4));
-    lse2 = row < T ? lse_raw * kLog2e : INFINITY;
-    if (half == 0 && row < T) {
-      p.delta[lrow] = delta;
-      p.lse2[lrow] = lse2;  // for the dK/dV kernel's probabilities
-    }
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  // vector memory operations complete in issue order: all but the last QM (the stores above)
+  if (norm)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QM) : "memory");
+  else
+    __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // ---- phases: group 0 runs M(tau) in interval 2tau and V(tau) in 2tau+1,
