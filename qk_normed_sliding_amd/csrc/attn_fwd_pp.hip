@@ -382,17 +382,20 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
 
   // Epilogue of a finished item: O / l -> bf16, LSE (natural log); then the
   // accumulators start over for the next item.
+  // The epilogue's stores (kEpiStores per wave, always issued: rows at or past
+  // T fall outside the buffers' ranges and are dropped) are the last memory
+  // operations before the V-phase's wait, which so does not wait for them.
+  constexpr int kEpiStores = 4 * NDB + 1;
   struct Epi {
-    long o_off;    // element offset of (b, row, head, 4 half) in o
-    long lse_off;  // index of (b, head, row) in lse
-    bool ok;       // row < T
+    int b, head, row;  // the lane's row of (batch, query head)
   };
-  Epi epi{0, 0, false};
+  Epi epi{0, 0, 0};
   auto epilogue = [&]() {
     const float l_tot = pair_sum(l_run[0] + l_run[1]);
-    if (epi.ok) {
+    {
       const float inv = 1.f / l_tot;
-      bf16* dst = (bf16*)p.o + epi.o_off;
+      const auto ro = make_rsrc((const bf16*)p.o + (long)epi.b * T * qstride, (uint32_t)T * qstride * 2);
+      const uint32_t off = (uint32_t)(epi.row * qstride + epi.head * D + 4 * half) * 2;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -400,9 +403,10 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
           u32x2 v;
           v[0] = pack2(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
           v[1] = pack2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
-          *(u32x2*)(dst + 32 * db + 8 * i) = v;
+          bstore8(ro, off + (uint32_t)(32 * db + 8 * i) * 2, v);
         }
-      if (half == 0) p.lse[epi.lse_off] = fast_log2(l_tot) * kLn2;
+      const auto rl = make_rsrc(p.lse + ((long)epi.b * p.Hq + epi.head) * T, (uint32_t)T * 4);
+      if (half == 0) bstore4(rl, (uint32_t)epi.row * 4, fast_log2(l_tot) * kLn2);
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -452,19 +456,23 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
     // tiles of the item that hold keys visible to some row of this wave
     const int ta = r0 < T ? (W < 0 ? 0 : max(0, r0 - W) / BN) - it.n_lo : 1;
     const int tb = r0 < T ? min(r0 + 31, row_hi) / BN - it.n_lo : 0;
-    const Epi here{((long)it.b * T + r0 + l32) * qstride + (long)it.head * D + 4 * half,
-                   ((long)it.b * p.Hq + it.head) * T + r0 + l32, r0 + l32 < T};
+    const Epi here{it.b, it.head, r0 + l32};
 #pragma clang loop unroll(disable)
     for (int tau = 0; tau < it.ntile; ++tau, ++st) {
       const bool act = tau >= ta && tau <= tb;
       m_phase(st, pend_pv, act);
       __syncthreads();
-      if (pend_epi) epilogue();
+      const bool stored = pend_epi;
+      if (stored) epilogue();
       if (act) v_phase(it.n_lo + tau, r0);
       pend_pv = act;
       pend_epi = act && tau == tb;
       if (pend_epi) epi = here;
-      __builtin_amdgcn_s_waitcnt(0);
+      // this wave's earlier copies have landed (not the epilogue's stores)
+      if (stored)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kEpiStores) : "memory");
+      else
+        __builtin_amdgcn_s_waitcnt(0);
       if (k + 1 < nk) {
         if (tau == 0) q_prefetch(item(k + 1));
         if (tau == it.ntile - 1) {

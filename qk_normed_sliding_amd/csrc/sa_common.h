@@ -92,6 +92,12 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
 }
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, 0);
+}
 
 // Buffer resource as four dwords (base address, stride 0, size in bytes,
 // flags), uniform across the wave so that it lives in scalar registers.
