@@ -64,6 +64,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   constexpr int RPI = 64 / CPR;        // rows per direct-to-LDS instruction (1 KB)
   constexpr int IPW = BQ / RPI / 4;    // instructions per wave, per tile
   constexpr int LEAD = 4;              // operands in flight ahead of the MFMAs
+  constexpr int kStoreOps = 32 / RPI;  // whole-row stores per wave of a finished block
   static_assert(KST == 2 * NDB, "operand groups of the row and transpose MFMAs have the same size");
 
   __shared__ __attribute__((aligned(1024))) bf16 Qs[NB][TILE];
@@ -467,11 +468,19 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
           }
       }
     }
-    // the rows, 1/rms and first tile of the next block have arrived: the next rows go to the
-    // operand registers, then this block's dv (group A) or dk (group B) rows leave through the
-    // staging area (a wave's LDS accesses stay in order, so the reads see the rows first)
-    __builtin_amdgcn_s_waitcnt(0);
-    if (more) kf_from_stage();
+    // the rows and 1/rms of the next block have arrived (its first tile, issued last, may still
+    // be in flight): the next rows go to the operand registers, then this block's dv (group A)
+    // or dk (group B) rows leave through the staging area (a wave's LDS accesses stay in order,
+    // so the reads see the rows first)
+    if (more) {
+      if (rw == 0)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW + 1) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(IPW) : "memory");
+      kf_from_stage();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     {
       int el = lane;
       asm volatile("" : "+v"(el));
@@ -487,22 +496,28 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
           const int c = 4 * db + i;  // 16-byte chunk of head_dim 32db + 8i
           *(SA_LDS u32x2*)(uintptr_t)(wbase + (uint32_t)((c ^ (e32 % CPR)) << 4)) = w;
         }
-      const int nrows = min(32, T - e_kw0);  // rows of the wave's keys below T
-      bf16* dst = (bf16*)(grp == 0 ? p.dv : p.dk) + ((long)e_b * T + e_kw0) * kvstride + (long)e_g * D;
+      // (kStoreOps buffer stores per wave, always issued: rows at or past T fall outside the
+      // range, which ends with head e_g's part of row T - 1, and are dropped)
+      const auto rd = make_rsrc((bf16*)(grp == 0 ? p.dv : p.dk) + (long)e_b * T * kvstride + (long)e_g * D,
+                                (uint32_t)(T * kvstride - e_g * D) * 2);
       const int crow = el / CPR, cch = el % CPR;
+      u32x4 w[kStoreOps];  // all rows read before the first store: one LDS latency, not one per store
 #pragma unroll
-      for (int m = 0; m < 32 / RPI; ++m) {
+      for (int m = 0; m < kStoreOps; ++m) {
         const int r = RPI * m + crow;
-        const u32x4 w = *(SA_LDS const u32x4*)(uintptr_t)(kst_lds + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4)));
-        if (r < nrows) st16(dst + (long)r * kvstride + 8 * cch, w);
+        w[m] = *(SA_LDS const u32x4*)(uintptr_t)(kst_lds + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4)));
       }
+#pragma unroll
+      for (int m = 0; m < kStoreOps; ++m)
+        bstore16(rd, (uint32_t)((e_kw0 + RPI * m + crow) * kvstride + 8 * cch) * 2, w[m]);
     }
-    // the next block's accumulators start at zero
+    // the next block's accumulators start at zero; its first tile has landed (not the stores)
     if (more) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStoreOps) : "memory");
     }
     __syncthreads();
   }
