@@ -562,9 +562,9 @@ SA_API size_t sa_polar_express_workspace_bytes(int batch, int rows, int cols) {
   const size_t m = (size_t)(rows < cols ? rows : cols), n = (size_t)(rows < cols ? cols : rows);
   const PolarPlan pl = polar_plan(batch, (int)m, (int)n);
   // X (two buffers, wide side [m][n]), A and B ([m][m]), partial sums of the
-  // norm, split-K partial tiles
+  // first Gram product's diagonal (||G||_F^2), split-K partial tiles
   return 2 * round256((size_t)batch * m * n * 2) + 2 * round256((size_t)batch * m * m * 2) +
-         round256((size_t)batch * sa::kFroChunks * 4) + round256(pl.part_floats * 4);
+         round256((size_t)batch * sa::gemm_trace_parts((int)m) * 4) + round256(pl.part_floats * 4);
 }
 
 SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, size_t workspace_bytes, int batch,
@@ -586,32 +586,36 @@ SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, siz
   void* Bm = (char*)A + round256((size_t)batch * m * m * 2);
   float* part = (float*)((char*)Bm + round256((size_t)batch * m * m * 2));
   const PolarPlan pl = polar_plan(batch, m, n);
-  float* kpart = (float*)((char*)part + round256((size_t)batch * sa::kFroChunks * 4));
+  float* kpart = (float*)((char*)part + round256((size_t)batch * sa::gemm_trace_parts(m) * 4));
   // wide view of the input: the transpose of a tall matrix
   const void* src = g;
   if (tall) {
     if (sa::launch_transpose(g, x0, batch, rows, cols, s) != hipSuccess) return SA_ERR_HIP;
     src = x0;
   }
-  // ||G||_F in partial sums; the first step reads G itself and scales its products
-  if (sa::launch_fro_sumsq(src, part, batch, (long)m * n, s) != hipSuccess) return SA_ERR_HIP;
   // step k writes bufs[k % 2]; x0 (the transposed input of a tall matrix) is read by step 0 only
   void* bufs[2] = {x1, x0};
   const void* cur = src;
+  const int parts = sa::gemm_trace_parts(m);
   for (int k = 0; k < steps; ++k) {
     const float a = kPolarCoeffs[k][0], b = kPolarCoeffs[k][1], c = kPolarCoeffs[k][2];
-    const float* nsum = k == 0 ? part : nullptr;
-    // A = X X^T (symmetric: upper tiles only); X = G / (||G|| + eps) on the first step
-    sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f, 1, pl.s_xx, kpart, nsum, 2, eps};
-    if (sa::launch_gemm(pg, false, batch, s, pl.s_xx > 1 ? 128 : polar_tile(batch, m, m, false, true)) != hipSuccess)
-      return SA_ERR_HIP;
+    // On the first step X = s G, s = 1 / (||G||_F + eps): its Gram product is G G^T itself (A0),
+    // written with the partial sums of its diagonal (||G||_F^2) in 128 x 128 tiles, and the next
+    // two products take the powers of s: B = c s^4 A0 A0 + b s^2 A0, X <- s B G + a s G.
+    const bool first = k == 0;
+    const float* nsum = first ? part : nullptr;
+    // A = X X^T (symmetric: upper tiles only)
+    sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f, 1, pl.s_xx, kpart, nullptr, 0, 0, 0, eps,
+                      first ? part : nullptr};
+    const int tg = (pl.s_xx > 1 || first) ? 128 : polar_tile(batch, m, m, false, true);
+    if (sa::launch_gemm(pg, false, batch, s, tg) != hipSuccess) return SA_ERR_HIP;
     // B = c A A + b A  (A is symmetric: A A = A A^T, and so is B)
-    sa::GemmParams pb{A, A, A, Bm, m, m, m, c, b, 1, pl.s_aa, kpart};
+    sa::GemmParams pb{A, A, A, Bm, m, m, m, c, b, 1, pl.s_aa, kpart, nsum, parts, 4, 2, eps, nullptr};
     if (sa::launch_gemm(pb, false, batch, s, pl.s_aa > 1 ? 128 : polar_tile(batch, m, m, false, true)) != hipSuccess)
       return SA_ERR_HIP;
     // X <- B X + a X, straight into the output on the last step of a wide matrix
     void* dst = (k == steps - 1 && !tall) ? out : bufs[k % 2];
-    sa::GemmParams px{Bm, cur, cur, dst, m, n, m, 1.f, a, 0, 0, nullptr, nsum, 1, eps};
+    sa::GemmParams px{Bm, cur, cur, dst, m, n, m, 1.f, a, 0, 0, nullptr, nsum, parts, 1, 1, eps, nullptr};
     if (sa::launch_gemm(px, true, batch, s, polar_tile(batch, m, n, true, false)) != hipSuccess) return SA_ERR_HIP;
     cur = bufs[k % 2];
   }

@@ -1,7 +1,6 @@
 // Muon's polar-express orthogonalisation ("autoresearch Administrator &
 // Developer Guide", section 8.2.3) for stacks of bf16 matrices: the gradient
-// scaled by its Frobenius norm (the scale is folded into the first step's
-// products: X X^T takes s^2 and B X + a X takes s), then five steps
+// scaled by its Frobenius norm, then five steps
 //   A = X X^T,  B = b A + c A A,  X <- a X + B X
 // on the wide side (a tall matrix is turned into a wide one by a transpose
 // on the way in and out: the iteration commutes with transposition).
@@ -25,6 +24,11 @@
 // each workgroup writes its fp32 partial tile and a second kernel adds the
 // partials in a fixed order, applies alpha and beta and stores C (mirrored
 // too when symmetric).
+// The scaling by s = 1 / (||G||_F + eps) is folded into the first step: its
+// Gram product is G G^T itself, whose diagonal sums to ||G||_F^2 (the
+// product writes fixed-order partial sums of its diagonal blocks), and the
+// next two products scale their alpha and beta by the powers of s that the
+// scaled iteration implies (A A: c s^4 and b s^2; B X + a X: s and a s).
 #include "sa_common.h"
 #include "sa_kernels.h"
 
@@ -56,20 +60,22 @@ __device__ __forceinline__ int xcd_item(int L, int n) {
   return start + slot;
 }
 
-// alpha and beta of a product, times s^npow when the operand's scaling
-// s = 1 / (||G||_F + eps) is folded in (the partial sums added in the same
-// fixed order everywhere)
+// alpha and beta of a product, times s^npow_a and s^npow_b when the
+// operand's scaling s = 1 / (||G||_F + eps) is folded in (the partial sums
+// of ||G||_F^2 added in the same fixed order everywhere)
 __device__ __forceinline__ void gemm_scales(const GemmParams& p, long bz, float& al, float& be) {
   al = p.alpha;
   be = p.beta;
   if (p.nsum != nullptr) {
-    const float* pm = p.nsum + bz * kFroChunks;
+    const float* pm = p.nsum + bz * p.nsum_n;
     float ss = 0.f;
-    for (int c = 0; c < kFroChunks; ++c) ss += pm[c];
+    for (int c = 0; c < p.nsum_n; ++c) ss += pm[c];
     const float sc = 1.f / (sqrtf(ss) + p.neps);
-    const float f = p.npow == 2 ? sc * sc : sc;
-    al *= f;
-    be *= f;
+    float fa = 1.f, fb = 1.f;
+    for (int i = 0; i < p.npow_a; ++i) fa *= sc;
+    for (int i = 0; i < p.npow_b; ++i) fb *= sc;
+    al *= fa;
+    be *= fb;
   }
 }
 
@@ -268,6 +274,26 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
     return;
   }
 
+  // the diagonal of a symmetric product's diagonal tile (waves with wm == wn
+  // hold its 32 x 32 diagonal blocks acc[y][y]): lane l has the element of
+  // row l32 when its half matches, in register 4 (l32 >> 3) + (l32 & 3); the
+  // wave adds them by a fixed butterfly
+  if constexpr (TM == 128) {
+    if (p.trace != nullptr && tm == tn && wm == wn) {
+      const int rr = 4 * (l32 >> 3) + (l32 & 3);
+      const bool on = half == ((l32 >> 2) & 1);
+#pragma unroll
+      for (int y = 0; y < MB; ++y) {
+        float v = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = (on && r == rr) ? acc[y][y][r] : v;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+        if (lane == 0) p.trace[bz * gemm_trace_parts(p.M) + 4 * tm + MB * wm + y] = v;
+      }
+    }
+  }
+
   // epilogue: C = alpha acc + beta C0 (bf16), mirrored for an off-diagonal tile of a symmetric product
   const long cbase = bz * p.M * p.N;
   float al, be;
@@ -429,6 +455,7 @@ __global__ void __launch_bounds__(256, 2) gemm192_kernel(GemmParams p) {
 // stores 8 bytes; the mirror goes through an LDS transpose.
 __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   __shared__ unsigned short t[32][34];
+  __shared__ float dg[32];
   const int tile = blockIdx.x / 16, br = (blockIdx.x / 4) & 3, bc = blockIdx.x & 3;
   int tm, tn;
   tile_of(tile, p.N / 128, p.sym, tm, tn);
@@ -441,6 +468,17 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
     const f32x4 x = *(const f32x4*)(p.part + (((long)bz * p.splits + s) * ntile + tile) * (128 * 128) + lr * 128 + lc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] += x[e];
+  }
+  // a diagonal block's diagonal (element (r, 4q + e) with 4q + e = r), added in row order
+  if (p.trace != nullptr && tm == tn && br == bc) {
+    const int e = r - 4 * q;
+    if (e >= 0 && e < 4) dg[r] = e == 0 ? v[0] : e == 1 ? v[1] : e == 2 ? v[2] : v[3];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float s = 0.f;
+      for (int i = 0; i < 32; ++i) s += dg[i];
+      p.trace[bz * gemm_trace_parts(p.M) + 4 * tm + br] = s;
+    }
   }
   const long row = tm * 128 + lr, col = tn * 128 + lc;
   const long off = bz * p.M * p.N + row * p.N + col;
@@ -474,27 +512,6 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   *(u32x2*)((bf16*)p.c + moff) = m;
 }
 
-// Sum of squares of chunk blockIdx.x of matrix blockIdx.y (elements
-// [chunk * per, (chunk + 1) * per)), in a fixed order: part[y * gridDim.x + x].
-__global__ void __launch_bounds__(256) sumsq_kernel(const bf16* x, float* part, long per_matrix, long per) {
-  __shared__ float red[4];
-  const bf16* base = x + (long)blockIdx.y * per_matrix + (long)blockIdx.x * per;
-  float s = 0.f;
-  for (long e = 8L * threadIdx.x; e < per; e += 8L * 256) {
-    float f[8];
-    unpack8(ld16(base + e), f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s += f[k] * f[k];
-  }
-  // wave sum: groups of 16 (DPP), then across the four rows of the wave
-  s = group_sum<16>(s);
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) part[(long)blockIdx.y * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
-}
-
 // out[b][c][r] = in[b][r][c] for 64 x 64 tiles (R, C multiples of 64): 16-byte
 // loads of input rows into an LDS tile, 16-byte stores of output rows read
 // down its columns.
@@ -521,6 +538,7 @@ __global__ void __launch_bounds__(256) transpose_kernel(const bf16* in, bf16* ou
 
 hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream, int tile) {
   const int splits = p.splits > 1 ? p.splits : 1;
+  if (p.trace != nullptr && (tile != 128 || b_kn || !p.sym)) return hipErrorInvalidValue;
   if (tile == 192) {
     if (splits > 1 || p.M % 192 != 0 || p.N % 192 != 0 || p.K % 32 != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(gemm_tiles(p.M, p.N, p.sym, 192, 192) * batch));
@@ -542,13 +560,6 @@ hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t st
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(ntile * 16), (unsigned)batch), dim3(256), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_fro_sumsq(const void* x, float* part, int batch, long per_matrix, hipStream_t stream) {
-  const long per = per_matrix / kFroChunks;
-  const dim3 grid((unsigned)kFroChunks, (unsigned)batch);
-  hipLaunchKernelGGL(sumsq_kernel, grid, dim3(256), 0, stream, (const bf16*)x, part, per_matrix, per);
   return hipGetLastError();
 }
 

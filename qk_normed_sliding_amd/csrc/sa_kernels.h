@@ -125,18 +125,22 @@ struct GemmParams {
   int sym;         // C is symmetric (M == N): only tiles on or above the diagonal are computed, each stored mirrored too
   int splits;      // K in this many equal ranges (0 or 1: none); fp32 partial tiles in part, summed by a second kernel
   float* part;     // batch * splits * (computed tiles) * 128 * 128 floats
-  const float* nsum;  // optional: per matrix kFroChunks partial sums of squares of an operand G; alpha and
-                      // beta are then multiplied by s^npow, s = 1 / (||G||_F + neps) (the operand's scaling)
-  int npow;
+  const float* nsum;  // optional: per matrix nsum_n partial sums whose total is ||G||_F^2 for an operand G;
+                      // alpha is then multiplied by s^npow_a and beta by s^npow_b, s = 1 / (||G||_F + neps)
+  int nsum_n;
+  int npow_a, npow_b;
   float neps;
+  float* trace;       // optional (symmetric, 128 x 128 tiles): per matrix 4 (M / 128) partial sums of the
+                      // diagonal of the unscaled product, one per 32 x 32 diagonal block, in block order
 };
+// Partial sums per matrix of the diagonal that a symmetric GEMM writes to GemmParams::trace.
+__host__ __device__ inline int gemm_trace_parts(int M) { return 4 * (M / 128); }
 // Tiles of C that a GEMM computes (all, or those on and above the diagonal; tile_m x tile_n
 // tiles, square when symmetric).
 __host__ __device__ inline int gemm_tiles(int M, int N, int sym, int tile_m = 128, int tile_n = 128) {
   const int tm = M / tile_m, tn = N / tile_n;
   return sym ? tm * (tm + 1) / 2 : tm * tn;
 }
-constexpr int kFroChunks = 64;  // partial sums per matrix of the Frobenius norm
 
 // Optional events of a kernel launch (benchmarking hook), attached to the kernel's own
 // dispatch (hipExtLaunchKernelGGL), so their elapsed time is the kernel's duration.
@@ -159,11 +163,9 @@ hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stre
 hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev,
                          const VePrepParams* ve = nullptr);
 // Polar-express pieces: GEMM (b_kn: B given as [K][N]; tile: 128 (128 x 128), 96 (96 x 128, b_kn
-// only, unsplit) or 192 (192 x 192, unsplit; M, N multiples of 192, K of 32)), partial sums of
-// squares for ||X||_F per matrix (part: batch * kFroChunks floats), and
-// per-matrix transpose [R][C] -> [C][R].
+// only, unsplit) or 192 (192 x 192, unsplit; M, N multiples of 192, K of 32); trace only with 128),
+// and per-matrix transpose [R][C] -> [C][R].
 hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream, int tile = 128);
-hipError_t launch_fro_sumsq(const void* x, float* part, int batch, long per_matrix, hipStream_t stream);
 hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, hipStream_t stream);
 // Value-embedding gate backward: dve, dx32 and dw from dL/dv' (v' and g come from the norm pass).
 hipError_t launch_ve_bwd(const VeBwdParams& p, int head_dim, hipStream_t stream);

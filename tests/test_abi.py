@@ -206,16 +206,17 @@ def test_polar_express_validation_paths(sa):
     lib = sa.library()
     P = ctypes.c_void_p
     r256 = lambda x: (x + 255) // 256 * 256
-    # two X buffers on the wide side, A and B, 64 partial sums per matrix, and
+    # two X buffers on the wide side, A and B, the partial sums of the first
+    # Gram product's diagonal (4 per 128 rows: 24 per matrix at m = 768), and
     # split-K partial tiles: the Gram X X^T (K = 3072) of 8 matrices has 21
     # upper tiles each, 168 workgroups; ranges are at least 1024 long, so its K
     # is split in 3 (504 workgroups, the most ranges allowed); A A (K = 768) is
     # not split: 3 x 168 fp32 tiles of 128 x 128
     assert lib.sa_polar_express_workspace_bytes(8, 768, 3072) == 2 * r256(8 * 768 * 3072 * 2) + 2 * r256(
-        8 * 768 * 768 * 2) + r256(8 * 64 * 4) + r256(3 * 168 * 128 * 128 * 4)
+        8 * 768 * 768 * 2) + r256(8 * 24 * 4) + r256(3 * 168 * 128 * 128 * 4)
     # 32 matrices of 768 x 768: 672 workgroups per Gram, no split, no partials
     assert lib.sa_polar_express_workspace_bytes(32, 768, 768) == 2 * r256(32 * 768 * 768 * 2) + 2 * r256(
-        32 * 768 * 768 * 2) + r256(32 * 64 * 4)
+        32 * 768 * 768 * 2) + r256(32 * 24 * 4)
     assert lib.sa_polar_express_workspace_bytes(8, 3072, 768) == lib.sa_polar_express_workspace_bytes(8, 768, 3072)
     assert lib.sa_polar_express_workspace_bytes(1, 100, 128) == 0
     # the GEMM grids are one-dimensional: batch x 128-tiles stays below 2^20
