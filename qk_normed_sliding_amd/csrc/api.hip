@@ -519,18 +519,20 @@ int polar_splits(long jobs, int K) {
 
 // Tile of an unsplit polar-express product C [M][N] (K a multiple of 128): the shape whose
 // rounds of workgroups (two per compute unit) take the least time, a round's time taken as
-// the tile's area over its relative rate per element, measured on B X at m = 768 (K = 768):
-// 128 x 128 1 (19.3 us per round), 96 x 128 0.81 (B given as [K][N] only; 17.9 us),
-// 192 x 192 0.85 (50.9 us).
+// the tile's area over its relative rate per element, measured at m = 768 (K = 768): on B X,
+// 128 x 128 1 (19.3 us per round), 96 x 128 0.81 (B given as [K][N] only; 17.9 us), 192 x 192
+// 0.85 (50.9 us); on A A of 8 matrices, 64 x 64 0.26 (one round of 624 tiles, 14.1 us, against
+// 14.8 for one of 168 tiles of 128 x 128).
 int polar_tile(int batch, int M, int N, bool b_kn, bool sym) {
   int best = 128;
   double best_cost = 0.0;
-  const long slots = 2L * cu_count();
-  for (int t : {128, 96, 192}) {
-    const int tm = t, tn = t == 192 ? 192 : 128;
-    if (M % tm != 0 || N % tn != 0 || (t == 96 && (!b_kn || sym))) continue;
+  for (int t : {128, 96, 192, 64}) {
+    const int tm = t, tn = (t == 192 || t == 64) ? t : 128;
+    if (M % tm != 0 || N % tn != 0 || (t == 96 && (!b_kn || sym)) || (t == 64 && b_kn)) continue;
+    // workgroups per compute unit: two, or four of the 64 x 64 tile
+    const long slots = (t == 64 ? 4L : 2L) * cu_count();
     const long tiles = (long)batch * sa::gemm_tiles(M, N, sym, tm, tn);
-    const double rate = t == 128 ? 1.0 : (t == 96 ? 0.81 : 0.85);
+    const double rate = t == 128 ? 1.0 : (t == 96 ? 0.81 : (t == 192 ? 0.85 : 0.26));
     const double cost = (double)((tiles + slots - 1) / slots) * tm * tn / rate;
     if (t == 128 || cost < best_cost) {
       best = t;

@@ -9,7 +9,9 @@
 // accumulation, C = alpha A op(B) + beta C0, op(B) = B^T ("bt": B given as
 // [N][K], both operands read along K) or B ("bn": B given as [K][N], read
 // with LDS transpose reads). A 256-thread workgroup owns a 128 x 128 tile of
-// C (a 64 x 64 quarter per wave, 2 x 2 blocks of 32 x 32), or (bn only) a
+// C (a 64 x 64 quarter per wave, 2 x 2 blocks of 32 x 32), a 64 x 64 tile
+// (bt only; a 32 x 32 block per wave, up to four workgroups per compute
+// unit, for products with few tiles), or (bn only) a
 // 96 x 128 tile (a 96 x 32 column strip per wave, 3 blocks), which the host
 // picks when its tile count fills the compute units' workgroup slots in
 // fewer rounds of work (at m = 768: 1536 tiles, three full rounds of 512,
@@ -130,10 +132,11 @@ __device__ __forceinline__ void gemm_store_rows(const GemmParams& p, long cbase,
 
 template <bool BN, int TM>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
-  constexpr int TN = 128, TK = 64;
-  static_assert(TM == 128 || (TM == 96 && BN), "128 x 128 tiles, or 96 x 128 with B given as [K][N]");
-  constexpr int MB = TM == 128 ? 2 : 3;  // 32-row blocks per wave
-  constexpr int NB = TM == 128 ? 2 : 1;  // 32-column blocks per wave
+  constexpr int TN = TM == 64 ? 64 : 128, TK = 64;
+  static_assert(TM == 128 || (TM == 96 && BN) || (TM == 64 && !BN),
+                "128 x 128 tiles, 96 x 128 with B given as [K][N], or 64 x 64 with B given as [N][K]");
+  constexpr int MB = TM == 96 ? 3 : TM / 64;  // 32-row blocks per wave
+  constexpr int NB = TM == 96 ? 1 : TM / 64;  // 32-column blocks per wave
   __shared__ __attribute__((aligned(1024))) bf16 As[2][TM * TK];  // [m][k], 8 chunks per row
   __shared__ __attribute__((aligned(1024))) bf16 Bs[2][TN * TK];  // bt: [n][k] (8 chunks); bn: [k][n] (16 chunks)
 
@@ -143,14 +146,14 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
   // this wave's part of the tile: row blocks MB wm .., column blocks NB wn ..
-  const int wm = TM == 128 ? w >> 1 : 0, wn = TM == 128 ? w & 1 : w;
+  const int wm = TM == 96 ? 0 : w >> 1, wn = TM == 96 ? w : w & 1;
   const int tiles_n = p.N / TN;
   const int splits = p.splits > 1 ? p.splits : 1;
   // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
   // work item w = (matrix, tile, split) in that order goes to the XCD that
   // runs a contiguous range of items, so the tiles of a matrix, which share
   // its row and column panels, meet in one L2.
-  const int per_mat = gemm_tiles(p.M, p.N, p.sym, TM) * splits;
+  const int per_mat = gemm_tiles(p.M, p.N, p.sym, TM, TN) * splits;
   const int w_item = xcd_item((int)blockIdx.x, (int)gridDim.x);
   const int tile = (w_item % per_mat) / splits, sp = w_item % splits;
   int tm, tn;
@@ -166,7 +169,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   const u32x4 rb = rsrc_words(B, (uint32_t)(p.N * p.K * 2));
 
   // Copies: instruction j of wave w fills the 1 KB block blk = 4j + w of a
-  // tile (A: TM / 8 blocks). [x][k] tiles (8 chunks per row): rows 8 blk + lane/8; the row's
+  // tile (A: TM / 8 blocks, B: TN / 8). [x][k] tiles (8 chunks per row): rows 8 blk + lane/8; the row's
   // swizzle depends on blk only through its parity, which is w's. [k][n]
   // tiles (16 chunks per row): rows 4 blk + lane/16; swizzle from blk mod 4 = w.
   uint32_t oa, ob;
@@ -190,7 +193,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
       if (j < TM / 32) dma16(ra, uniform((int)(la + blk * 1024)), oa + (uint32_t)(((m0 + 8 * blk) * p.K + k0) * 2), 0u);
       if constexpr (BN)
         dma16(rb, uniform((int)(lb + blk * 1024)), ob + (uint32_t)(((k0 + 4 * blk) * p.N + n0) * 2), 0u);
-      else
+      else if (j < TN / 32)
         dma16(rb, uniform((int)(lb + blk * 1024)), ob + (uint32_t)(((n0 + 8 * blk) * p.K + k0) * 2), 0u);
     }
   };
@@ -260,7 +263,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   }
 
   if (splits > 1) {  // fp32 partial tile, row-major 128 x 128
-    float* dst = p.part + (((long)bz * splits + sp) * gemm_tiles(p.M, p.N, p.sym) + tile) * (TM * TN);
+    float* dst = p.part + (((long)bz * splits + sp) * gemm_tiles(p.M, p.N, p.sym, TM, TN) + tile) * (TM * TN);
 #pragma unroll
     for (int y = 0; y < MB; ++y)
 #pragma unroll
@@ -546,6 +549,12 @@ hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t st
       hipLaunchKernelGGL((gemm192_kernel<true>), grid, dim3(256), 0, stream, p);
     else
       hipLaunchKernelGGL((gemm192_kernel<false>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (tile == 64) {
+    if (b_kn || splits > 1 || p.M % 64 != 0 || p.N % 64 != 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(gemm_tiles(p.M, p.N, p.sym, 64, 64) * batch));
+    hipLaunchKernelGGL((gemm_kernel<false, 64>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
   }
   if (tile != 128 && (tile != 96 || !b_kn || splits > 1 || p.sym || p.M % 96 != 0)) return hipErrorInvalidValue;
