@@ -589,15 +589,12 @@ SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, siz
   float* part = (float*)((char*)Bm + round256((size_t)batch * m * m * 2));
   const PolarPlan pl = polar_plan(batch, m, n);
   float* kpart = (float*)((char*)part + round256((size_t)batch * sa::gemm_trace_parts(m) * 4));
-  // wide view of the input: the transpose of a tall matrix
-  const void* src = g;
-  if (tall) {
-    if (sa::launch_transpose(g, x0, batch, rows, cols, s) != hipSuccess) return SA_ERR_HIP;
-    src = x0;
-  }
-  // step k writes bufs[k % 2]; x0 (the transposed input of a tall matrix) is read by step 0 only
+  // A tall matrix G ([n][m], n > m) is iterated as it is: with Y = G (the transpose of the wide
+  // iterate X), A = X X^T = Y^T Y (both operands given as [K][*]) and X <- B X + a X becomes
+  // Y <- Y B + a Y (B symmetric, so given as [N][K] it is B itself).
+  // step k writes bufs[k % 2]
   void* bufs[2] = {x1, x0};
-  const void* cur = src;
+  const void* cur = g;
   const int parts = sa::gemm_trace_parts(m);
   for (int k = 0; k < steps; ++k) {
     const float a = kPolarCoeffs[k][0], b = kPolarCoeffs[k][1], c = kPolarCoeffs[k][2];
@@ -609,19 +606,24 @@ SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, siz
     // A = X X^T (symmetric: upper tiles only)
     sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f, 1, pl.s_xx, kpart, nullptr, 0, 0, 0, eps,
                       first ? part : nullptr};
-    const int tg = (pl.s_xx > 1 || first) ? 128 : polar_tile(batch, m, m, false, true);
-    if (sa::launch_gemm(pg, false, batch, s, tg) != hipSuccess) return SA_ERR_HIP;
+    const int tg = (pl.s_xx > 1 || first || tall) ? 128 : polar_tile(batch, m, m, false, true);
+    if (sa::launch_gemm(pg, tall, batch, s, tg, tall) != hipSuccess) return SA_ERR_HIP;
     // B = c A A + b A  (A is symmetric: A A = A A^T, and so is B)
     sa::GemmParams pb{A, A, A, Bm, m, m, m, c, b, 1, pl.s_aa, kpart, nsum, parts, 4, 2, eps, nullptr};
     if (sa::launch_gemm(pb, false, batch, s, pl.s_aa > 1 ? 128 : polar_tile(batch, m, m, false, true)) != hipSuccess)
       return SA_ERR_HIP;
-    // X <- B X + a X, straight into the output on the last step of a wide matrix
-    void* dst = (k == steps - 1 && !tall) ? out : bufs[k % 2];
-    sa::GemmParams px{Bm, cur, cur, dst, m, n, m, 1.f, a, 0, 0, nullptr, nsum, parts, 1, 1, eps, nullptr};
-    if (sa::launch_gemm(px, true, batch, s, polar_tile(batch, m, n, true, false)) != hipSuccess) return SA_ERR_HIP;
+    // X <- B X + a X (tall: Y <- Y B + a Y), straight into the output on the last step
+    void* dst = k == steps - 1 ? out : bufs[k % 2];
+    if (tall) {
+      sa::GemmParams py{cur, Bm, cur, dst, n, m, m, 1.f, a, 0, 0, nullptr, nsum, parts, 1, 1, eps, nullptr};
+      if (sa::launch_gemm(py, false, batch, s, polar_tile(batch, n, m, false, false)) != hipSuccess)
+        return SA_ERR_HIP;
+    } else {
+      sa::GemmParams px{Bm, cur, cur, dst, m, n, m, 1.f, a, 0, 0, nullptr, nsum, parts, 1, 1, eps, nullptr};
+      if (sa::launch_gemm(px, true, batch, s, polar_tile(batch, m, n, true, false)) != hipSuccess) return SA_ERR_HIP;
+    }
     cur = bufs[k % 2];
   }
-  if (tall && sa::launch_transpose(cur, out, batch, m, n, s) != hipSuccess) return SA_ERR_HIP;
   return SA_OK;
 }
 

@@ -2,8 +2,8 @@
 // Developer Guide", section 8.2.3) for stacks of bf16 matrices: the gradient
 // scaled by its Frobenius norm, then five steps
 //   A = X X^T,  B = b A + c A A,  X <- a X + B X
-// on the wide side (a tall matrix is turned into a wide one by a transpose
-// on the way in and out: the iteration commutes with transposition).
+// on the wide side; a tall matrix Y is iterated as it is, as the transpose
+// of the wide iterate (A = Y^T Y, Y <- Y B + a Y with B symmetric).
 //
 // The contractions are batched bf16 GEMMs on the matrix cores with fp32
 // accumulation, C = alpha A op(B) + beta C0, op(B) = B^T ("bt": B given as
@@ -130,14 +130,17 @@ __device__ __forceinline__ void gemm_store_rows(const GemmParams& p, long cbase,
     }
 }
 
-template <bool BN, int TM>
+// AN: A given as [K][M] too (copied and read like B given as [K][N]), for
+// the Gram product of a tall matrix Y, Y^T Y.
+template <bool BN, int TM, bool AN = false>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   constexpr int TN = TM == 64 ? 64 : 128, TK = 64;
   static_assert(TM == 128 || (TM == 96 && BN) || (TM == 64 && !BN),
                 "128 x 128 tiles, 96 x 128 with B given as [K][N], or 64 x 64 with B given as [N][K]");
+  static_assert(!AN || (BN && TM == 128), "A given as [K][M] with B given as [K][N] and 128 x 128 tiles");
   constexpr int MB = TM == 96 ? 3 : TM / 64;  // 32-row blocks per wave
   constexpr int NB = TM == 96 ? 1 : TM / 64;  // 32-column blocks per wave
-  __shared__ __attribute__((aligned(1024))) bf16 As[2][TM * TK];  // [m][k], 8 chunks per row
+  __shared__ __attribute__((aligned(1024))) bf16 As[2][TM * TK];  // [m][k], 8 chunks per row (an: [k][m], 16 chunks)
   __shared__ __attribute__((aligned(1024))) bf16 Bs[2][TN * TK];  // bt: [n][k] (8 chunks); bn: [k][n] (16 chunks)
 
   const int tid = threadIdx.x;
@@ -176,6 +179,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
   {
     const int r8 = (w & 1) * 8 + lane / 8;
     oa = (uint32_t)((lane / 8) * p.K + 8 * ((lane % 8) ^ swz<8>(r8))) * 2;
+    if constexpr (AN) {
+      const int r16 = (w & 3) * 4 + lane / 16;
+      oa = (uint32_t)((lane / 16) * p.M + 8 * ((lane % 16) ^ swz<16>(r16))) * 2;
+    }
     if constexpr (BN) {
       const int r16 = (w & 3) * 4 + lane / 16;
       ob = (uint32_t)((lane / 16) * p.N + 8 * ((lane % 16) ^ swz<16>(r16))) * 2;
@@ -190,7 +197,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int blk = 4 * j + w;
-      if (j < TM / 32) dma16(ra, uniform((int)(la + blk * 1024)), oa + (uint32_t)(((m0 + 8 * blk) * p.K + k0) * 2), 0u);
+      if constexpr (AN)
+        dma16(ra, uniform((int)(la + blk * 1024)), oa + (uint32_t)(((k0 + 4 * blk) * p.M + m0) * 2), 0u);
+      else if (j < TM / 32)
+        dma16(ra, uniform((int)(la + blk * 1024)), oa + (uint32_t)(((m0 + 8 * blk) * p.K + k0) * 2), 0u);
       if constexpr (BN)
         dma16(rb, uniform((int)(lb + blk * 1024)), ob + (uint32_t)(((k0 + 4 * blk) * p.N + n0) * 2), 0u);
       else if (j < TN / 32)
@@ -243,7 +253,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int y = 0; y < MB; ++y) bo[kk][y] = row_op(la, MB * wm + y, kk);
+      for (int y = 0; y < MB; ++y) {
+        if constexpr (AN)
+          bo[kk][y] = tr_op(la, MB * wm + y, kk);
+        else
+          bo[kk][y] = row_op(la, MB * wm + y, kk);
+      }
 #pragma unroll
       for (int x = 0; x < NB; ++x) {
         if constexpr (BN)
@@ -515,32 +530,18 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmParams p) {
   *(u32x2*)((bf16*)p.c + moff) = m;
 }
 
-// out[b][c][r] = in[b][r][c] for 64 x 64 tiles (R, C multiples of 64): 16-byte
-// loads of input rows into an LDS tile, 16-byte stores of output rows read
-// down its columns.
-__global__ void __launch_bounds__(256) transpose_kernel(const bf16* in, bf16* out, int R, int C) {
-  __shared__ unsigned short t[64][72];  // rows padded to 144 bytes (16-byte aligned)
-  const int tr = blockIdx.x / (C / 64), tc = blockIdx.x % (C / 64);
-  const long mb = (long)blockIdx.y * R * C;
-  const int r = threadIdx.x >> 3, c8 = 8 * (threadIdx.x & 7);  // rows r and r + 32, columns c8 .. c8 + 7
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const u32x4 w = ld16(in + mb + (long)(64 * tr + r + 32 * h) * C + 64 * tc + c8);
-    *(u32x4*)&t[r + 32 * h][c8] = w;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int oc = r + 32 * h;  // output row: input column 64 tc + oc; output columns c8 .. c8 + 7 = input rows
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)t[c8 + 2 * e][oc] | ((uint32_t)t[c8 + 2 * e + 1][oc] << 16);
-    st16(out + mb + (long)(64 * tc + oc) * R + 64 * tr + c8, w);
-  }
-}
-
-hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream, int tile) {
+hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream, int tile, bool a_kn) {
   const int splits = p.splits > 1 ? p.splits : 1;
+  if (a_kn) {
+    if (!b_kn || tile != 128) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(gemm_tiles(p.M, p.N, p.sym) * splits * batch));
+    hipLaunchKernelGGL((gemm_kernel<true, 128, true>), grid, dim3(256), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(gemm_tiles(p.M, p.N, p.sym) * 16), (unsigned)batch),
+                       dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.trace != nullptr && (tile != 128 || b_kn || !p.sym)) return hipErrorInvalidValue;
   if (tile == 192) {
     if (splits > 1 || p.M % 192 != 0 || p.N % 192 != 0 || p.K % 32 != 0) return hipErrorInvalidValue;
@@ -569,12 +570,6 @@ hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t st
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(ntile * 16), (unsigned)batch), dim3(256), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, hipStream_t stream) {
-  const dim3 grid((unsigned)((R / 64) * (C / 64)), (unsigned)batch);
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, stream, (const bf16*)in, (bf16*)out, R, C);
   return hipGetLastError();
 }
 

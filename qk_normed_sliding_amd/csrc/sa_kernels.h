@@ -164,10 +164,9 @@ hipError_t launch_qknorm(const NormParams& p, int head_dim, hipStream_t stream, 
                          const VePrepParams* ve = nullptr);
 // Polar-express pieces: GEMM (b_kn: B given as [K][N]; tile: 128 (128 x 128), 96 (96 x 128, b_kn
 // only, unsplit), 64 (64 x 64, not b_kn, unsplit) or 192 (192 x 192, unsplit; M, N multiples of 192,
-// K of 32); trace only with 128),
-// and per-matrix transpose [R][C] -> [C][R].
-hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream, int tile = 128);
-hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, hipStream_t stream);
+// K of 32); trace only with 128; a_kn: A given as [K][M] too, with b_kn and tile 128).
+hipError_t launch_gemm(const GemmParams& p, bool b_kn, int batch, hipStream_t stream, int tile = 128,
+                       bool a_kn = false);
 // Value-embedding gate backward: dve, dx32 and dw from dL/dv' (v' and g come from the norm pass).
 hipError_t launch_ve_bwd(const VeBwdParams& p, int head_dim, hipStream_t stream);
 

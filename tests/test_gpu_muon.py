@@ -101,12 +101,21 @@ def test_polar_express_model_shape_groups(sa, shape):
 
 
 def test_polar_express_transpose_symmetry(sa):
-    """A tall stack and its transpose go through different paths (transposed
-    copies around the wide iteration): the results must be transposes."""
+    """The iteration commutes with transposition, and a tall stack and its
+    transpose go through different products (Y^T Y and Y B + a Y on the tall
+    matrix, X X^T and B X + a X on the wide one), so the results agree up to
+    bf16 rounding: each against the oracle, and the two against each other
+    within the same relative-Frobenius bound."""
     g = _grad((2, 512, 256), 77)
-    a = sa.sa_polar_express(g.cuda())
-    b = sa.sa_polar_express(g.transpose(-2, -1).contiguous().cuda())
-    assert torch.equal(a, b.transpose(-2, -1))
+    gt = g.transpose(-2, -1).contiguous()
+    _check(sa, g)
+    _check(sa, gt)
+    a = sa.sa_polar_express(g.cuda()).cpu().double()
+    b = sa.sa_polar_express(gt.cuda()).cpu().double().transpose(-2, -1)
+    for i in range(g.shape[0]):
+        rel = float((a[i] - b[i]).norm() / b[i].norm())
+        log(f"  tall vs wide, matrix {i}: rel-Frobenius {rel:.3e}")
+        assert rel <= POLAR_REL_FRO
 
 
 def test_polar_express_matrices_are_independent(sa):
