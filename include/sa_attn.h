@@ -281,9 +281,10 @@ sa_status sa_attn_bwd_ex(const void* q, const void* k, const void* v, const void
  *               (cols / 128) < 2^20 (SA_ERR_SHAPE otherwise).
  *   steps     : 1..5 (5 in the trainer); eps >= 0 (the trainer's guard is tiny).
  *   workspace : at least sa_polar_express_workspace_bytes(batch, rows, cols)
- *               bytes, 256-byte aligned (two copies of X on its wide side,
- *               A and B, the norm's partial sums, fp32 partial tiles of the
- *               products whose K is split); contents unspecified.
+ *               bytes, 256-byte aligned (two copies of X, A and B, partial
+ *               sums of the first Gram product's diagonal (||G||_F^2), fp32
+ *               partial tiles of the products whose K is split); contents
+ *               unspecified.
  *   Arithmetic: bf16 MFMA operands with fp32 accumulation; X, A and B are
  *   stored as bf16 between the products, as a bf16 optimizer step keeps them.
  *   The result depends only on its own matrix: matrices of a stack are
