@@ -50,7 +50,7 @@ KERNELS = {
     "fwd": ("attn_fwd_pp_kernel", ("attn_fwd_pp.hip", "sa_common.h")),
     "bwd_dq": ("attn_bwd_dq_pp_kernel", ("attn_bwd_dq_pp.hip", "sa_common.h")),
     "bwd_dkdv": ("attn_bwd_dkdv_pp_kernel", ("attn_bwd_dkdv_pp.hip", "sa_common.h")),
-    "knorm": ("qknorm_kernel", ("qknorm.hip", "sa_common.h")),
+    "knorm": ("qknorm_kernel", ("qknorm.hip", "sa_common.h", "ve_common.h")),
 }
 # the MFMA-bound attention kernels and the HBM-bound pass that norms the key rows (the
 # forward's; the backward reads its output back from the forward's workspace)
@@ -315,6 +315,15 @@ def summarize_trace(trace_dir, trace_json, plain_json, command):
         shapes.append(f"- {name}: grid {r0['Grid_Size_X']}x{r0['Grid_Size_Y']}, wg {r0['Workgroup_Size_X']}, "
                       f"LDS {r0['LDS_Block_Size']}, VGPR {r0['VGPR_Count']}, AGPR {r0['Accum_VGPR_Count']}, "
                       f"scratch {r0['Scratch_Size']}")
+    known = [k for k in by if any(k.startswith(n + "<") or k == n for n, _ in KERNELS.values())]
+    others = sorted((k for k in by if k not in known and not k.startswith("__amd")),
+                    key=lambda k: -sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in by[k]))
+    if others:
+        out += ["", "Other kernels in the run (all dispatches, warm-up included):", "",
+                "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for k in others:
+            d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in by[k]]
+            out.append(f"| {k} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} |")
     out += ["", "Launch shape (grid threads, workgroup threads, LDS bytes, VGPR/AGPR as reported, scratch):", ""]
     out += shapes
     rf = plain.get("roofline")
