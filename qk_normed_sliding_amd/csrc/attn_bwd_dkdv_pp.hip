@@ -496,8 +496,8 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
           const int c = 4 * db + i;  // 16-byte chunk of head_dim 32db + 8i
           *(SA_LDS u32x2*)(uintptr_t)(wbase + (uint32_t)((c ^ (e32 % CPR)) << 4)) = w;
         }
-      // (kStoreOps buffer stores per wave, always issued: rows at or past T fall outside the
-      // range, which ends with head e_g's part of row T - 1, and are dropped)
+      // (kStoreOps buffer stores per wave: rows at or past T fall outside the range, which ends
+      // with head e_g's part of row T - 1, and are dropped)
       const auto rd = make_rsrc((bf16*)(grp == 0 ? p.dv : p.dk) + (long)e_b * T * kvstride + (long)e_g * D,
                                 (uint32_t)(T * kvstride - e_g * D) * 2);
       const int crow = el / CPR, cch = el % CPR;
@@ -507,17 +507,21 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
         const int r = RPI * m + crow;
         w[m] = *(SA_LDS const u32x4*)(uintptr_t)(kst_lds + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4)));
       }
+      // the next block's first tile has landed before the stores are issued, which then stay in
+      // flight across the barrier (the first vector phase's wait covers them). (A partial vmcnt
+      // after the stores would not do: loads and stores are not retired in order with respect
+      // to each other.)
+      __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
       for (int m = 0; m < kStoreOps; ++m)
         bstore16(rd, (uint32_t)((e_kw0 + RPI * m + crow) * kvstride + 8 * cch) * 2, w[m]);
     }
-    // the next block's accumulators start at zero; its first tile has landed (not the stores)
+    // the next block's accumulators start at zero
     if (more) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStoreOps) : "memory");
     }
     __syncthreads();
   }

@@ -338,14 +338,18 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
     r_q = scal[l32];
     delta = scal[32 + l32];
     lse2 = row < T ? lse_raw * kLog2e : INFINITY;
+    // every load and tile copy of the prologue has landed before the first
+    // store is issued: the stores below are then left in flight across the
+    // barrier (the first vector phase's wait covers them). (A partial vmcnt
+    // after the stores would not do: loads and stores are not retired in
+    // order with respect to each other.)
+    __builtin_amdgcn_s_waitcnt(0);
     if (half == 0 && row < T) {
       p.delta[lrow] = delta;
       p.lse2[lrow] = lse2;  // for the dK/dV kernel's probabilities
     }
-    // the q_hat rows for the dK/dV kernel, read back from the staging area, as
-    // the last memory operations of the prologue (rows at or past T are dropped
-    // by the buffer's range): the wait below then covers the row loads and the
-    // first tiles but not these stores
+    // the q_hat rows for the dK/dV kernel, read back from the staging area
+    // (rows at or past T are dropped by the buffer's range)
     if (norm) {
       const auto rqh = make_rsrc((bf16*)p.qhat + first, bytes);
 #pragma unroll
@@ -364,11 +368,6 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
     for (int kk = 0; kk < KST; ++kk)
       df[kk] = *(SA_LDS const bf16x8*)(uintptr_t)(rbase + (uint32_t)((((2 * kk + half) ^ (l32 % CPR))) << 4));
   }
-  // vector memory operations complete in issue order: all but the last QM (the stores above)
-  if (norm)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QM) : "memory");
-  else
-    __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // ---- phases: group 0 runs M(tau) in interval 2tau and V(tau) in 2tau+1,

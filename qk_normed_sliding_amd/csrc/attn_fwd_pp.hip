@@ -382,20 +382,28 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
 
   // Epilogue of a finished item: O / l -> bf16, LSE (natural log); then the
   // accumulators start over for the next item.
-  // The epilogue's stores (kEpiStores per wave, always issued: rows at or past
-  // T fall outside the buffers' ranges and are dropped) are the last memory
-  // operations before the V-phase's wait, which so does not wait for them.
-  constexpr int kEpiStores = 4 * NDB + 1;
+  // The epilogue runs in two parts: the row sum is taken (and reset) before
+  // the vector phase of the next item's first tile, and the stores (rows at
+  // or past T fall outside the buffers' ranges and are dropped) are issued
+  // after that phase's wait for its earlier copies, so the wait does not
+  // include them; the next vector phase's wait does. (A partial vmcnt after
+  // the stores would not do: loads and stores are not retired in order with
+  // respect to each other.)
   struct Epi {
     int b, head, row;  // the lane's row of (batch, query head)
   };
   Epi epi{0, 0, 0};
-  auto epilogue = [&]() {
-    const float l_tot = pair_sum(l_run[0] + l_run[1]);
+  float epi_l = 0.f;
+  auto epi_sum = [&]() {
+    epi_l = pair_sum(l_run[0] + l_run[1]);
+    l_run[0] = l_run[1] = 0.f;
+  };
+  auto epi_store = [&](const Epi& e) {
+    const float l_tot = epi_l;
     {
       const float inv = 1.f / l_tot;
-      const auto ro = make_rsrc((const bf16*)p.o + (long)epi.b * T * qstride, (uint32_t)T * qstride * 2);
-      const uint32_t off = (uint32_t)(epi.row * qstride + epi.head * D + 4 * half) * 2;
+      const auto ro = make_rsrc((const bf16*)p.o + (long)e.b * T * qstride, (uint32_t)T * qstride * 2);
+      const uint32_t off = (uint32_t)(e.row * qstride + e.head * D + 4 * half) * 2;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -405,14 +413,13 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
           v[1] = pack2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
           bstore8(ro, off + (uint32_t)(32 * db + 8 * i) * 2, v);
         }
-      const auto rl = make_rsrc(p.lse + ((long)epi.b * p.Hq + epi.head) * T, (uint32_t)T * 4);
-      if (half == 0) bstore4(rl, (uint32_t)epi.row * 4, fast_log2(l_tot) * kLn2);
+      const auto rl = make_rsrc(p.lse + ((long)e.b * p.Hq + e.head) * T, (uint32_t)T * 4);
+      if (half == 0) bstore4(rl, (uint32_t)e.row * 4, fast_log2(l_tot) * kLn2);
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    l_run[0] = l_run[1] = 0.f;
   };
 
   // ---- prologue: the first tiles of the stream (K tiles 0..NB-1 by group
@@ -463,16 +470,14 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
       m_phase(st, pend_pv, act);
       __syncthreads();
       const bool stored = pend_epi;
-      if (stored) epilogue();
+      const Epi epi_done = epi;
+      if (stored) epi_sum();
       if (act) v_phase(it.n_lo + tau, r0);
       pend_pv = act;
       pend_epi = act && tau == tb;
       if (pend_epi) epi = here;
-      // this wave's earlier copies have landed (not the epilogue's stores)
-      if (stored)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kEpiStores) : "memory");
-      else
-        __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (stored) epi_store(epi_done);
       if (k + 1 < nk) {
         if (tau == 0) q_prefetch(item(k + 1));
         if (tau == it.ntile - 1) {
@@ -489,7 +494,10 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   // final step: P.V of the last tile; group 1 ends on its M-phase barrier
   m_phase(st, pend_pv, false);
   __syncthreads();
-  if (pend_epi) epilogue();
+  if (pend_epi) {
+    epi_sum();
+    epi_store(epi);
+  }
   if (grp == 1) return;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
