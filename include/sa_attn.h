@@ -291,6 +291,12 @@ sa_status sa_attn_bwd_ex(const void* q, const void* k, const void* v, const void
  *   independent.
  */
 size_t sa_polar_express_workspace_bytes(int batch, int rows, int cols);
+/* MFMA FLOP that sa_polar_express executes for these arguments (the symmetric
+ * products compute only their tiles on and above the diagonal, so this is
+ * below the full-product count 5 (4 m^2 n + 2 m^3) per matrix); 0 for
+ * arguments it would reject. Launches nothing; the tiles it counts depend on
+ * the current device's compute units (128 x 128 tiles without a device). */
+double sa_polar_express_executed_flops(int batch, int rows, int cols, int steps);
 sa_status sa_polar_express(const void* g, void* out, void* workspace, size_t workspace_bytes,
                            int batch, int rows, int cols, int steps, float eps, void* stream);
 

@@ -92,6 +92,8 @@ def _load():
                                    vp, i64t, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.sa_polar_express_workspace_bytes.restype = sz
     lib.sa_polar_express_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.sa_polar_express_executed_flops.restype = ctypes.c_double
+    lib.sa_polar_express_executed_flops.argtypes = [i32, i32, i32, i32]
     lib.sa_polar_express.restype = i32
     lib.sa_polar_express.argtypes = [vp, vp, vp, sz, i32, i32, i32, i32, f32, vp]
     lib.sa_set_timing_events.restype = i32
@@ -413,6 +415,11 @@ def sa_attn_bwd_rope(q, k, v, o, lse, dout, rope_cos, rope_sin, window=-1, softm
 
 def sa_polar_express_workspace_bytes(batch, rows, cols):
     return int(_lib.sa_polar_express_workspace_bytes(batch, rows, cols))
+
+
+def sa_polar_express_executed_flops(batch, rows, cols, steps=5):
+    """MFMA FLOP the library executes for sa_polar_express (symmetric products: upper tiles only)."""
+    return float(_lib.sa_polar_express_executed_flops(batch, rows, cols, steps))
 
 
 def sa_polar_express(g, out=None, steps=5, eps=1e-7, workspace=None, stream=None):

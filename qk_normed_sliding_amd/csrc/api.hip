@@ -524,6 +524,7 @@ int polar_splits(long jobs, int K) {
 // 0.85 (50.9 us); on A A of 8 matrices, 64 x 64 0.26 (one round of 624 tiles, 14.1 us, against
 // 14.8 for one of 168 tiles of 128 x 128).
 int polar_tile(int batch, int M, int N, bool b_kn, bool sym) {
+  if (cu_count() <= 0) return 128;  // no device to size the rounds for
   int best = 128;
   double best_cost = 0.0;
   for (int t : {128, 96, 192, 64}) {
@@ -557,7 +558,37 @@ PolarPlan polar_plan(int batch, int m, int n) {
   return pl;
 }
 
+// Tiles of one step's three products on [m][n] matrices (tall: the iterate is [n][m]): the Gram
+// (128 on the first step, whose epilogue sums the diagonal, when split, and for a tall matrix,
+// whose Gram reads both operands as [K][*]), A A, and the X update.
+struct PolarTiles {
+  int gram, aa, upd;
+};
+PolarTiles polar_tiles(int batch, int m, int n, bool tall, bool first, const PolarPlan& pl) {
+  PolarTiles t;
+  t.gram = (pl.s_xx > 1 || first || tall) ? 128 : polar_tile(batch, m, m, false, true);
+  t.aa = pl.s_aa > 1 ? 128 : polar_tile(batch, m, m, false, true);
+  t.upd = tall ? polar_tile(batch, n, m, false, false) : polar_tile(batch, m, n, true, false);
+  return t;
+}
+
 }  // namespace
+
+SA_API double sa_polar_express_executed_flops(int batch, int rows, int cols, int steps) {
+  if (check_polar(batch, rows, cols, steps, 0.f) != SA_OK) return 0.0;
+  const bool tall = rows > cols;
+  const int m = tall ? cols : rows, n = tall ? rows : cols;
+  const PolarPlan pl = polar_plan(batch, m, n);
+  double f = 0.0;
+  for (int k = 0; k < steps; ++k) {
+    const PolarTiles t = polar_tiles(batch, m, n, tall, k == 0, pl);
+    // the symmetric products compute their tiles on and above the diagonal only
+    f += (double)sa::gemm_tiles(m, m, 1, t.gram, t.gram) * t.gram * t.gram * 2.0 * n;
+    f += (double)sa::gemm_tiles(m, m, 1, t.aa, t.aa) * t.aa * t.aa * 2.0 * m;
+    f += 2.0 * m * (double)m * n;
+  }
+  return f * batch;
+}
 
 SA_API size_t sa_polar_express_workspace_bytes(int batch, int rows, int cols) {
   if (check_polar(batch, rows, cols, 5, 0.f) != SA_OK) return 0;
@@ -606,21 +637,22 @@ SA_API sa_status sa_polar_express(const void* g, void* out, void* workspace, siz
     // A = X X^T (symmetric: upper tiles only)
     sa::GemmParams pg{cur, cur, nullptr, A, m, m, n, 1.f, 0.f, 1, pl.s_xx, kpart, nullptr, 0, 0, 0, eps,
                       first ? part : nullptr};
-    const int tg = (pl.s_xx > 1 || first || tall) ? 128 : polar_tile(batch, m, m, false, true);
+    const PolarTiles tl = polar_tiles(batch, m, n, tall, first, pl);
+    const int tg = tl.gram;
     if (sa::launch_gemm(pg, tall, batch, s, tg, tall) != hipSuccess) return SA_ERR_HIP;
     // B = c A A + b A  (A is symmetric: A A = A A^T, and so is B)
     sa::GemmParams pb{A, A, A, Bm, m, m, m, c, b, 1, pl.s_aa, kpart, nsum, parts, 4, 2, eps, nullptr};
-    if (sa::launch_gemm(pb, false, batch, s, pl.s_aa > 1 ? 128 : polar_tile(batch, m, m, false, true)) != hipSuccess)
+    if (sa::launch_gemm(pb, false, batch, s, tl.aa) != hipSuccess)
       return SA_ERR_HIP;
     // X <- B X + a X (tall: Y <- Y B + a Y), straight into the output on the last step
     void* dst = k == steps - 1 ? out : bufs[k % 2];
     if (tall) {
       sa::GemmParams py{cur, Bm, cur, dst, n, m, m, 1.f, a, 0, 0, nullptr, nsum, parts, 1, 1, eps, nullptr};
-      if (sa::launch_gemm(py, false, batch, s, polar_tile(batch, n, m, false, false)) != hipSuccess)
+      if (sa::launch_gemm(py, false, batch, s, tl.upd) != hipSuccess)
         return SA_ERR_HIP;
     } else {
       sa::GemmParams px{Bm, cur, cur, dst, m, n, m, 1.f, a, 0, 0, nullptr, nsum, parts, 1, 1, eps, nullptr};
-      if (sa::launch_gemm(px, true, batch, s, polar_tile(batch, m, n, true, false)) != hipSuccess) return SA_ERR_HIP;
+      if (sa::launch_gemm(px, true, batch, s, tl.upd) != hipSuccess) return SA_ERR_HIP;
     }
     cur = bufs[k % 2];
   }

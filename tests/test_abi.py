@@ -202,6 +202,20 @@ def test_binding_rejects_cpu_tensors(sa):
         sa.sa_attn_fwd(q, k, k)
 
 
+def test_polar_express_executed_flops_count_upper_tiles(sa):
+    """The executed MFMA count: the symmetric products X X^T and A A compute
+    their tiles on and above the diagonal only (21 of 36 at m = 768 in
+    128 x 128 tiles, the tiles used without a device), the update the full
+    product. (8, 768, 3072): m = 768, n = 3072, five steps."""
+    m, n, b = 768, 3072, 8
+    per_step = 21 * 128 * 128 * 2 * n + 21 * 128 * 128 * 2 * m + 2 * m * m * n
+    got = sa.sa_polar_express_executed_flops(b, m, n, 5)
+    assert got == b * 5 * per_step
+    assert got < b * 5 * (4 * m * m * n + 2 * m ** 3)
+    assert sa.sa_polar_express_executed_flops(b, n, m, 5) == got  # tall: the same products
+    assert sa.sa_polar_express_executed_flops(1, 100, 128, 5) == 0.0
+
+
 def test_polar_express_validation_paths(sa):
     lib = sa.library()
     P = ctypes.c_void_p
