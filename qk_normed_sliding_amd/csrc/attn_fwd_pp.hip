@@ -311,18 +311,6 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
     const uint32_t Vb = vs_lds + (uint32_t)(((st + NB - 1) % NB) * TILE * 2);
     const uint32_t Kb = ks_lds + (uint32_t)((st % NB) * TILE * 2);
     __builtin_amdgcn_s_setprio(0);
-    if (do_pv) {
-      bf16x8 ring[LEAD];
-#pragma unroll
-      for (int i = 0; i < LEAD; ++i) ring[i] = pv_read(Vb, i);
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        const bf16x8 a = ring[i % LEAD];
-        pv_op(i, a);
-        if (i + LEAD < NPV) ring[i % LEAD] = pv_read(Vb, i + LEAD);
-      }
-      sched_ring<NPV, LEAD, 2>();
-    }
     if (do_s) {
       constexpr int N = 2 * KST;
       bf16x8 ring[LEAD];
@@ -335,6 +323,18 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
         if (i + LEAD < N) ring[i % LEAD] = s_read(Kb, i + LEAD);
       }
       sched_ring<N, LEAD, 1>();
+    }
+    if (do_pv) {
+      bf16x8 ring[LEAD];
+#pragma unroll
+      for (int i = 0; i < LEAD; ++i) ring[i] = pv_read(Vb, i);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const bf16x8 a = ring[i % LEAD];
+        pv_op(i, a);
+        if (i + LEAD < NPV) ring[i % LEAD] = pv_read(Vb, i + LEAD);
+      }
+      sched_ring<NPV, LEAD, 2>();
     }
     __builtin_amdgcn_s_setprio(1);
   };
