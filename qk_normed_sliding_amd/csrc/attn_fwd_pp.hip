@@ -27,9 +27,10 @@
 //     registers a whole item ahead, and an item's epilogue (O / l, LSE) runs
 //     inside the next item's first vector phase, so the pipeline never
 //     drains between items.
-//   - Work per wave is split into an M-phase (the P.V MFMAs of the previous
-//     tile plus the S MFMAs of the current one, with the LDS reads of the
-//     next MFMA group in flight behind the current group) and a V-phase (the
+//   - Work per wave is split into an M-phase (the S MFMAs of the current
+//     tile, which the V-phase that follows needs first, then the P.V MFMAs of
+//     the previous tile, with the LDS reads of the next MFMA group in flight
+//     behind the current group) and a V-phase (the
 //     exponentials and row sums of the current tile, then the next loads).
 //     Group 1 runs one phase behind group 0 and the phases are separated by
 //     workgroup barriers, so on every SIMD one wave is in its M-phase while
@@ -298,8 +299,11 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
     s[c] = mfma32(a, qf[kk], kk == 0 ? f32x16{} : s[c]);
   };
 
-  // M-phase of stream step st: P.V of tile st-1 (if it was one of this
-  // wave's), then S of tile st (if it is). Each part is straight-line with
+  // M-phase of stream step st: S of tile st (if it is one of this wave's),
+  // then P.V of tile st-1 (if it was): the vector phase that follows needs S,
+  // whose last results so arrive while the P.V MFMAs issue (S last, its
+  // latency sat at the end of the phase: the forward was 1.7% slower). Each
+  // part is straight-line with
   // its operand reads LEAD MFMAs ahead of their use, and updates its
   // accumulators in place. The wave drops to the low issue priority for its
   // M-phase and takes the high one for the vector phase that follows: the
