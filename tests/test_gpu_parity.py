@@ -232,6 +232,7 @@ PERSIST_CASES = [
     (2, 260, 4, 2, 64, 0, 3),
     (2, 700, 6, 6, 128, 256, 3),    # MHA: 256-row items of one head
     (3, 390, 3, 1, 64, -1, 2),      # G = 3
+    (3, 129, 2, 2, 128, -1, 2),     # MHA: one-tile key blocks between longer ones
 ]
 
 
