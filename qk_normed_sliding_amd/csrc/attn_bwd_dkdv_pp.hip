@@ -52,7 +52,7 @@ __device__ __forceinline__ void sched_mphase() {
   __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool ROT>
 __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   constexpr int NB = 3;
   constexpr int BQ = 64;               // query rows per tile (two 32-row chunks)
@@ -93,17 +93,35 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   const int n_items = p.nkb * p.B * p.Hkv;
   const int NG = gridDim.x;
   auto item_index = [&](int k) { return k * NG + ((k & 1) ? NG - 1 - (int)blockIdx.x : (int)blockIdx.x); };
+  // ROT (a problem of many rounds, at least two per key block: dkdv_rotated_order) takes them in a
+  // rotated order instead: round k holds every key block of RC = NG / nkb (batch, KV head) pairs, and
+  // workgroup w takes pair k RC + w mod RC, key block (w / RC + k) mod nkb. A pair's key blocks then
+  // run together and share its q_hat / dO tiles in the caches (the heavy-first order visits them
+  // rounds apart, which matters once a layer's rows outgrow the last-level cache), and every
+  // workgroup cycles through all key blocks, so the rounds stay balanced.
+  const int npair = p.B * p.Hkv;
+  const int RC = ROT ? NG / p.nkb : 1;
   int n_blk = 0;
-  while (item_index(n_blk) < n_items) ++n_blk;
+  if constexpr (ROT)
+    n_blk = npair / RC;
+  else
+    while (item_index(n_blk) < n_items) ++n_blk;
   if (n_blk == 0) return;  // whole workgroup: no barrier has been passed
 
   // coordinates of the current block (set per block; the lambdas below read them)
   int kb = 0, g = 0, b = 0, kb0 = 0, kw0 = 0, key = 0, q_hi = 0, qb_lo = 0, nqb = 0, nit = 0;
   auto set_block = [&](int k) {
-    const int i = item_index(k);
-    kb = i / (p.B * p.Hkv);
-    g = (i / p.B) % p.Hkv;
-    b = i % p.B;
+    int pair;
+    if constexpr (ROT) {
+      kb = ((int)blockIdx.x / RC + k) % p.nkb;
+      pair = k * RC + (int)blockIdx.x % RC;
+    } else {
+      const int i = item_index(k);
+      kb = i / npair;
+      pair = i % npair;
+    }
+    g = pair / p.B;
+    b = pair % p.B;
     kb0 = kb * BK;
     kw0 = kb0 + 32 * rw;  // first key of this wave
     key = kw0 + l32;
@@ -527,19 +545,35 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
   }
 }
 
+// The rotated key-block order (see the kernel) for NG workgroups: RC = NG / nkb pairs per round, at
+// least two rounds per key block.
+bool dkdv_rotated_order(int NG, int nkb, int npair) {
+  const int rc = NG % nkb == 0 ? NG / nkb : 0;
+  return rc > 0 && npair % rc == 0 && npair / rc >= 2 * nkb;
+}
+
+template <int D, bool ROPE>
+void launch_bwd_dkdv_pp_d(const BwdParams& p, dim3 grid, bool rot, hipStream_t stream, const TimingEvents& ev) {
+  if (rot)
+    hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<D, ROPE, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+  else
+    hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<D, ROPE, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+}
+
 hipError_t launch_bwd_dkdv_pp(const BwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
   const dim3 grid((unsigned)min(p.nkb * p.B * p.Hkv, p.nwg));
+  const bool rot = dkdv_rotated_order((int)grid.x, p.nkb, p.B * p.Hkv);
   const bool rope = p.rope.cos != nullptr;
   if (head_dim == 128) {
     if (rope)
-      hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+      launch_bwd_dkdv_pp_d<128, true>(p, grid, rot, stream, ev);
     else
-      hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<128, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+      launch_bwd_dkdv_pp_d<128, false>(p, grid, rot, stream, ev);
   } else {
     if (rope)
-      hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+      launch_bwd_dkdv_pp_d<64, true>(p, grid, rot, stream, ev);
     else
-      hipExtLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<64, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+      launch_bwd_dkdv_pp_d<64, false>(p, grid, rot, stream, ev);
   }
   return hipGetLastError();
 }

@@ -52,8 +52,15 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
 
   const int per_qb = p.B * p.Hkv * p.nsub;
   const int bid = blockIdx.x;
-  const int qb = p.nqb - 1 - bid / per_qb;  // heavy query blocks first
-  int rem = bid % per_qb;
+  // heavy query blocks first; a problem of many rounds of nwg workgroups (at least two per query
+  // block) runs in chunks of RC = nwg / nqb (batch, KV head, sub) units instead, heavy-first inside
+  // a chunk, so that a unit's query blocks run together and share its K/V band in the caches (the
+  // workgroups are dispatched as compute units free up, which keeps the rounds balanced)
+  const int RC = p.nwg % p.nqb == 0 ? p.nwg / p.nqb : 0;
+  const bool chunked = RC > 0 && per_qb % RC == 0 && per_qb / RC >= 2 * p.nqb;
+  const int CW = chunked ? RC : per_qb;
+  const int qb = p.nqb - 1 - (bid % (CW * p.nqb)) / CW;
+  int rem = (bid / (CW * p.nqb)) * CW + bid % CW;
   const int sub = rem % p.nsub;
   rem /= p.nsub;
   const int g = rem % p.Hkv;

@@ -56,7 +56,7 @@ __device__ __forceinline__ void sched_ring() {
   __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
 }
 
-template <int D, int NB, bool ROPE>
+template <int D, int NB, bool ROPE, bool ROT>
 __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   constexpr int BN = 64;              // keys per tile
   constexpr int BM = 128;             // query rows per item (per head)
@@ -98,18 +98,34 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   const int G = gridDim.x;
   const int w = blockIdx.x;
   auto item_index = [&](int k) { return k * G + ((k & 1) ? G - 1 - w : w); };
+  // ROT (a problem of many rounds, at least two per query block: fwd_rotated_order) takes them in a
+  // rotated order instead: round k holds every query block of RC = G / nqb (batch, KV head, sub)
+  // units, and workgroup w takes unit k RC + w mod RC, query block nqb - 1 - ((w / RC + k) mod nqb).
+  // A unit's query blocks then run together and share its K/V band in the caches (the heavy-first
+  // order visits them rounds apart, which matters once a layer's K and V outgrow the last-level
+  // cache), and every workgroup cycles through all query blocks, so the rounds stay balanced.
+  const int RC = ROT ? G / p.nqb : 1;
   int nk = 0;
-  while (item_index(nk) < n_items) ++nk;
+  if constexpr (ROT)
+    nk = per_qb / RC;
+  else
+    while (item_index(nk) < n_items) ++nk;
   if (nk == 0) return;  // whole workgroup: no barrier has been passed
 
   struct Item {
     int b, g, head, qb, n_lo, ntile;
   };
   auto item = [&](int k) {
-    const int i = item_index(k);
     Item it;
-    it.qb = p.nqb - 1 - i / per_qb;
-    int rem = i % per_qb;
+    int rem;
+    if constexpr (ROT) {
+      it.qb = p.nqb - 1 - (w / RC + k) % p.nqb;
+      rem = k * RC + w % RC;
+    } else {
+      const int i = item_index(k);
+      it.qb = p.nqb - 1 - i / per_qb;
+      rem = i % per_qb;
+    }
     const int sub = rem % p.nsub;
     rem /= p.nsub;
     it.g = rem % p.Hkv;
@@ -507,21 +523,38 @@ __global__ void __launch_bounds__(512) attn_fwd_pp_kernel(FwdParams p) {
   __syncthreads();
 }
 
-hipError_t launch_fwd_pp(const FwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
+// The rotated item order (see the kernel) for G workgroups: RC = G / nqb units per round, at least
+// two rounds per query block.
+bool fwd_rotated_order(int G, int nqb, int per_qb) {
+  const int rc = G % nqb == 0 ? G / nqb : 0;
+  return rc > 0 && per_qb % rc == 0 && per_qb / rc >= 2 * nqb;
+}
+
+template <int D, bool ROPE>
+void launch_fwd_pp_d(const FwdParams& p, dim3 grid, bool rot, hipStream_t stream, const TimingEvents& ev) {
   constexpr int NB = 3;
-  const int n_items = p.nqb * p.B * p.Hkv * p.nsub;
+  if (rot)
+    hipExtLaunchKernelGGL((attn_fwd_pp_kernel<D, NB, ROPE, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+  else
+    hipExtLaunchKernelGGL((attn_fwd_pp_kernel<D, NB, ROPE, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+}
+
+hipError_t launch_fwd_pp(const FwdParams& p, int head_dim, hipStream_t stream, const TimingEvents& ev) {
+  const int per_qb = p.B * p.Hkv * p.nsub;
+  const int n_items = p.nqb * per_qb;
   const dim3 grid((unsigned)min(n_items, p.nwg));
+  const bool rot = fwd_rotated_order((int)grid.x, p.nqb, per_qb);
   const bool rope = p.rope.cos != nullptr;
   if (head_dim == 128) {
     if (rope)
-      hipExtLaunchKernelGGL((attn_fwd_pp_kernel<128, NB, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+      launch_fwd_pp_d<128, true>(p, grid, rot, stream, ev);
     else
-      hipExtLaunchKernelGGL((attn_fwd_pp_kernel<128, NB, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+      launch_fwd_pp_d<128, false>(p, grid, rot, stream, ev);
   } else {
     if (rope)
-      hipExtLaunchKernelGGL((attn_fwd_pp_kernel<64, NB, true>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+      launch_fwd_pp_d<64, true>(p, grid, rot, stream, ev);
     else
-      hipExtLaunchKernelGGL((attn_fwd_pp_kernel<64, NB, false>), grid, dim3(512), 0, stream, ev.start, ev.stop, 0, p);
+      launch_fwd_pp_d<64, false>(p, grid, rot, stream, ev);
   }
   return hipGetLastError();
 }

@@ -233,6 +233,12 @@ PERSIST_CASES = [
     (2, 700, 6, 6, 128, 256, 3),    # MHA: 256-row items of one head
     (3, 390, 3, 1, 64, -1, 2),      # G = 3
     (3, 129, 2, 2, 128, -1, 2),     # MHA: one-tile key blocks between longer ones
+    # many rounds per query / key block: the rotated orders of the forward and dK/dV kernels and the
+    # chunked order of the dQ kernel
+    (4, 256, 4, 2, 128, -1, 4),     # G = 2
+    (4, 256, 4, 2, 128, 100, 4),
+    (8, 512, 2, 2, 64, -1, 8),      # MHA: 256-row items
+    (8, 512, 2, 2, 64, 200, 8),
 ]
 
 
