@@ -19,7 +19,8 @@
 //
 // The kernel is persistent: one workgroup per compute unit takes key blocks
 // in a fixed heavy-first snake order (key blocks near the start of the
-// sequence see the most query rows). At a block's end each wave issues the
+// sequence see the most query rows), or, in a launch of many rounds, a
+// rotated order that runs a (batch, KV head)'s key blocks in the same round. At a block's end each wave issues the
 // loads of its rows for the next block (k_hat or v) and that block's first
 // tile before running the finished block's epilogue, so the epilogue, the
 // next block's first loads and the workgroup's start overlap. The epilogue's

@@ -13,7 +13,9 @@
 //     workgroup runs per compute unit and takes the items of a fixed
 //     heavy-first "snake" order (round k: item k*G + w, or k*G + G-1-w on
 //     odd rounds), which balances the causal triangle as well as a dynamic
-//     queue would, without a counter.
+//     queue would, without a counter; a launch of many rounds takes a rotated
+//     order that runs a (batch, KV head)'s query blocks in the same round
+//     (see the item list below).
 //   - The norm pass has written k_hat (normed key rows); the value rows are
 //     read as stored (v, or v' with value embeddings). Both tiles of 64 keys
 //     are plain copies, issued as buffer loads straight into LDS (no
