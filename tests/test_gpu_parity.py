@@ -270,6 +270,8 @@ ROPE_CASES = [
     (1, 260, 6, 2, 64, 100, 40, 0),      # G = 3, D = 64
     (2, 129, 2, 1, 64, 0, None, 0),      # window 0
     (3, 390, 4, 2, 128, 100, None, 3),   # persistent items back to back (next item's rows turned)
+    (4, 256, 4, 2, 128, 100, None, 4),   # many rounds per block: the rotated work orders
+    (8, 512, 2, 2, 64, -1, None, 8),     # the same, MHA
 ]
 
 
