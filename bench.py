@@ -157,11 +157,11 @@ def summarize_pmc(fetch_dir, write_dir, workload, extra=""):
                        "fetch_scale": f_scale, "write_scale": w_scale},
         "kernels": kernels,
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o pmc -- python -u bench.py --steps 2 "
+            f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o pmc -- python -u bench.py --steps 2 "
             f"--warmup 1 --cpu-seconds 0 --no-kernel-events --no-graph --copy-probe{extra}",
-            "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o pmc -- python -u bench.py --steps 2 "
+            f"rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o pmc -- python -u bench.py --steps 2 "
             f"--warmup 1 --cpu-seconds 0 --no-kernel-events --no-graph --copy-probe{extra}",
-            f"python bench.py --summarize-pmc gpurun_out/pmc_fetch gpurun_out/pmc_write{extra}",
+            f"python bench.py --summarize-pmc {fetch_dir} {write_dir}{extra}",
         ],
     }
     os.makedirs(PROFILES, exist_ok=True)
@@ -396,9 +396,9 @@ def summarize_sq(dir_a, dir_b, workload, extra=""):
                 f"wait-inst {f('SQ_WAIT_INST_ANY') / wave:6.1%}  MFMA/VALU insts "
                 f"{f('SQ_INSTS_MFMA') / max(1.0, f('SQ_INSTS_VALU')):.3f}")
     base = f"python -u bench.py --steps 2 --warmup 1 --cpu-seconds 0 --no-kernel-events --no-graph{extra}"
-    cmds = [f"timeout -s KILL 120 rocprofv3 --pmc {SQ_PASSES[i]} -f csv -d gpurun_out/pmc_sq{i} -o pmc -- {base}"
-            for i in range(2)]
-    cmds.append(f"python bench.py --summarize-sq gpurun_out/pmc_sq0 gpurun_out/pmc_sq1{extra}")
+    cmds = [f"timeout -s KILL 120 rocprofv3 --pmc {SQ_PASSES[i]} -f csv -d {d} -o pmc -- {base}"
+            for i, d in enumerate((dir_a, dir_b))]
+    cmds.append(f"python bench.py --summarize-sq {dir_a} {dir_b}{extra}")
     out = [f"# SQ counters: {workload}", "",
            "Commands (two counter passes, each its own run, then the summary; from the repository root):", "",
            "```", *cmds, "```", "",
