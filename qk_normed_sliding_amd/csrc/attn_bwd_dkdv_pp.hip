@@ -529,11 +529,12 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
       // the next block's first tile has landed before the stores are issued, which then stay in
       // flight across the barrier (the first vector phase's wait covers them). (A partial vmcnt
       // after the stores would not do: loads and stores are not retired in order with respect
-      // to each other.)
+      // to each other.) The rows are streamed past the L2 cache (non-temporal): nothing in this
+      // pass reads them again, and the cache keeps serving the q_hat and dO tiles instead.
       __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
       for (int m = 0; m < kStoreOps; ++m)
-        bstore16(rd, (uint32_t)((e_kw0 + RPI * m + crow) * kvstride + 8 * cch) * 2, w[m]);
+        bstore16_nt(rd, (uint32_t)((e_kw0 + RPI * m + crow) * kvstride + 8 * cch) * 2, w[m]);
     }
     // the next block's accumulators start at zero
     if (more) {

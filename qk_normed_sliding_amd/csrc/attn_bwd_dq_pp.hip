@@ -494,7 +494,8 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   // The wave's 32 rows go through its staging area (free again: every M-phase
   // ended before the last barrier), row r's 16-byte chunk j at chunk
   // j ^ (r mod CPR) as in the prologue, and leave as whole rows: each store
-  // instruction writes QRPI rows of D contiguous values. (The lane index is
+  // instruction writes QRPI rows of D contiguous values, streamed past the L2
+  // cache (non-temporal), which keeps serving the K and V tiles instead. (The lane index is
   // made opaque so that these addresses are computed here, not kept in
   // registers from the prologue's equal ones.)
   int el = lane;
@@ -517,7 +518,7 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
   for (int m = 0; m < QM; ++m) {
     const int r = QRPI * m + crow;  // row within the wave's 32
     const u32x4 w = *(SA_LDS const u32x4*)(uintptr_t)(stage + (uint32_t)(r * D * 2 + ((cch ^ (r % CPR)) << 4)));
-    if (r0 + r < T) st16((bf16*)p.dq + first + (long)(r0 + r) * qstride + 8 * cch, w);
+    if (r0 + r < T) st16_nt((bf16*)p.dq + first + (long)(r0 + r) * qstride + 8 * cch, w);
   }
 }
 

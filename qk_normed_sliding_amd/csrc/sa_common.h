@@ -92,6 +92,12 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
 }
+// As bstore16 with the non-temporal (streaming) cache policy: for whole-row results
+// that nothing in the same pass reads again, so they do not displace the tiles
+// that the L2 cache still serves.
+__device__ __forceinline__ void bstore16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 2);
+}
 __device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
 }
@@ -139,6 +145,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4*)p); }
 
 __device__ __forceinline__ void unpack8(u32x4 w, float* f) {
 #pragma unroll
