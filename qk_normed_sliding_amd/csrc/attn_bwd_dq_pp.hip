@@ -274,9 +274,9 @@ __global__ void __launch_bounds__(512) attn_bwd_dq_pp_kernel(BwdParams p) {
 #pragma unroll
     for (int m = 0; m < QM; ++m) {
       const uint32_t off = (uint32_t)((r0 + QRPI * m + crow) * qstride + 8 * cch) * 2;
-      xq[m] = bload16(rq, off);
-      xd[m] = bload16(rd, off);
-      xo[m] = bload16(ro, off);
+      xq[m] = bload16_nt(rq, off);  // q and o rows are read once in the backward;
+      xd[m] = bload16(rd, off);     // dO rows again as the dK/dV kernel's tiles
+      xo[m] = bload16_nt(ro, off);
     }
     if (grp == 1) {
       for (int tau = 0; tau < 3 && tau < ntile; ++tau) issue_k(tau);

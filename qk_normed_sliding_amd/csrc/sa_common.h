@@ -87,6 +87,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+// As bload16 with the non-temporal (streaming) cache policy: for rows read once,
+// so that they do not displace data the L2 cache serves again.
+__device__ __forceinline__ u32x4 bload16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
+}
 // Raw buffer store: writes at or past the resource's byte range are dropped,
 // so a store of a ragged tail needs no branch (and is always issued).
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
