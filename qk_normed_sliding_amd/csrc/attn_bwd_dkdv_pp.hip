@@ -434,17 +434,6 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
       // of the key sits in group A's operand kk = 2db + i/2 of lane
       // 32(i%2) + l%32, elements 4half + j.
       constexpr bool rope = ROPE;
-      const long tr = (long)e_key * p.rope.stride + 4 * half;
-      f32x4 tc[NDB / 2][4], ts[NDB / 2][4];
-      if (rope) {
-#pragma unroll
-        for (int db = 0; db < NDB / 2; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            tc[db][i] = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
-            ts[db][i] = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
-          }
-      }
       float dot = 0.f;
       u32x2 kh[NDB][4] = {};
       if (norm) {
@@ -473,6 +462,17 @@ __global__ void __launch_bounds__(512) attn_bwd_dkdv_pp_kernel(BwdParams p) {
             acc[db][4 * i + j] = norm ? e_rk * (gh - kx * dot) : gh;
           }
       if (rope) {
+        // the tables are read only now, when the k_hat words are dead: held across the
+        // correction above they pushed the epilogue past the register file
+        const long tr = (long)e_key * p.rope.stride + 4 * half;
+        f32x4 tc[NDB / 2][4], ts[NDB / 2][4];
+#pragma unroll
+        for (int db = 0; db < NDB / 2; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            tc[db][i] = *(const f32x4*)(p.rope.cos + tr + 32 * db + 8 * i);
+            ts[db][i] = *(const f32x4*)(p.rope.sin + tr + 32 * db + 8 * i);
+          }
 #pragma unroll
         for (int db = 0; db < NDB / 2; ++db)
 #pragma unroll
